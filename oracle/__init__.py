@@ -1,0 +1,2 @@
+"""CPU oracle (test infrastructure only; never imported by the product path)."""
+from .attention import attend, decode, gather_context, reshape_and_cache, verify, widen  # noqa: F401
