@@ -1,0 +1,267 @@
+"""Benchmark: batch-64 paged GQA decode step over 28 layer caches on one MI355X.
+
+One step = for each of 28 layers: pa_reshape_and_cache of one new K/V token
+per sequence, then pa_decode of one query token per sequence (64 sequences,
+16 query / 8 KV heads, head_dim 128, bf16, block size 16, context = 256-token
+prompt + U{1..256} generated tokens, a shuffled pool of 16384 blocks per
+layer, one shared block table).  The step is captured once in a HIP graph and
+replayed (the pages' change 4: graphs per batch bucket); ``--eager`` launches
+every kernel from Python instead.
+
+Printed: one JSON line with tokens/s for the whole step (``value``), the decode
+kernel's achieved HBM bandwidth on algorithmic bytes against the 8 TB/s peak
+(``roofline``), and the CPU oracle timed on a bounded sample
+(``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+WORKLOAD = "batch64_28layer_bf16"
+METRIC = "paged GQA decode attention: achieved HBM GB/s (% of peak) + tokens/s at batch 64"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library default)")
+    p.add_argument("--eager", action="store_true", help="launch from Python instead of a graph")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--decode-reps", type=int, default=20,
+                   help="graph replays of the 28 decode launches for the per-kernel timing")
+    p.add_argument("--traffic-file", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "profiles", "pa_decode_batch64_traffic.json"))
+    return p.parse_args()
+
+
+def algorithmic_bytes(lens, q_heads, kv_heads, head_dim, elem=2):
+    """Bytes pa_decode must move for one layer: K and V of exactly L_b positions per
+    (sequence, KV head), q in, out, the used block-table entries and the lengths."""
+    lens = np.asarray(lens, np.int64)
+    kv = int(lens.sum()) * kv_heads * head_dim * elem * 2
+    qo = len(lens) * q_heads * head_dim * elem * 2
+    tables = int(((lens + 15) // 16).sum()) * 4 + len(lens) * 4
+    return kv + qo + tables
+
+
+def cache_write_bytes(num_tokens, kv_heads, head_dim, elem=2):
+    return num_tokens * kv_heads * head_dim * elem * 2 * 2 + num_tokens * 8
+
+
+def cpu_baseline(target_s: float):
+    """The fp64 oracle on a bounded sample of the same workload (single thread)."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+    from paged_kv_gqa_pa_amd import workloads as wl
+    case = wl.build_case(WORKLOAD, layer=0)
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    try:
+        n_layers = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables,
+                          case.context_lens, case.scale, "bf16", "bf16")
+            n_layers += 1
+            el = time.perf_counter() - t0
+            if el >= target_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    per_layer = el / n_layers
+    spec = case.spec
+    tok_s = spec.num_seqs / (per_layer * spec.layers)
+    gbps = algorithmic_bytes(case.context_lens, spec.q_heads, spec.kv_heads, spec.head_dim) / per_layer / 1e9
+    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_layers} decode passes of layer 0 (64 seqs, 16q/8kv heads, D=128) in "
+                      f"{el:.1f} s; tokens/s = 64 / (28 x time per layer); cache write not timed; "
+                      f"{gbps:.3f} GB/s on the same algorithmic bytes",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the decode path is measured on a single MI355X "
+              "(multi-GPU sharding is a design note, not a measured path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_gqa_pa_amd import _lib as pa
+    from paged_kv_gqa_pa_amd import workloads as wl
+
+    pa.lib()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    spec = wl.CONFIGS[WORKLOAD]
+    N, Hq, Hkv, D, NB, Lyr = spec.num_seqs, spec.q_heads, spec.kv_heads, spec.head_dim, spec.num_blocks, spec.layers
+    lens, table = wl.structure(spec)
+    slots = wl.slots_for_positions(table, np.arange(N), lens.astype(np.int64) - 1)
+    print(f"[bench] {WORKLOAD}: N={N} Hq={Hq} Hkv={Hkv} D={D} layers={Lyr} "
+          f"L in [{lens.min()},{lens.max()}] mean {lens.mean():.1f}", flush=True)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.seed)
+    bt = torch.from_numpy(table).to(dev)
+    cl = torch.from_numpy(lens).to(dev)
+    sm = torch.from_numpy(slots).to(dev)
+    kc, vc, qs, nks, nvs, outs = [], [], [], [], [], []
+    for _ in range(Lyr):
+        kc.append(torch.randn((Hkv, NB, 16, D), generator=gen, device=dev, dtype=torch.bfloat16))
+        vc.append(torch.randn((Hkv, NB, 16, D), generator=gen, device=dev, dtype=torch.bfloat16))
+        qs.append(torch.randn((N, Hq, D), generator=gen, device=dev, dtype=torch.bfloat16))
+        nks.append(torch.randn((N, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16))
+        nvs.append(torch.randn((N, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16))
+        outs.append(torch.empty((N, Hq, D), device=dev, dtype=torch.bfloat16))
+    max_len = spec.max_len
+    ws_bytes = pa.workspace_size(N, 1, Hq, Hkv, D, max_len, torch.bfloat16, args.split)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scale = 1.0 / float(np.sqrt(D))
+    torch.cuda.synchronize()
+    print(f"[bench] caches ready: {2 * Lyr * kc[0].numel() * 2 / 2**30:.1f} GiB, "
+          f"workspace {ws_bytes} B", flush=True)
+
+    def step():
+        for l in range(Lyr):
+            pa.reshape_and_cache(nks[l], nvs[l], kc[l], vc[l], sm)
+            pa.decode(outs[l], qs[l], kc[l], vc[l], bt, cl, scale, max_len,
+                      split_tokens=args.split, workspace=ws)
+
+    def decode_only():
+        for l in range(Lyr):
+            pa.decode(outs[l], qs[l], kc[l], vc[l], bt, cl, scale, max_len,
+                      split_tokens=args.split, workspace=ws)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            step()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+
+    if args.eager:
+        run_step = step
+        run_decode = decode_only
+    else:
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            step()
+        g_dec = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_dec):
+            decode_only()
+        run_step = g_step.replay
+        run_decode = g_dec.replay
+        for _ in range(max(1, args.warmup)):
+            run_step()
+        torch.cuda.synchronize()
+    print("[bench] warm", flush=True)
+
+    # Whole step: K steps between two events, synchronised on both sides.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        run_step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tok_s = N / (ms_step / 1e3)
+    print(f"[bench] step {ms_step * 1e3:.1f} us", flush=True)
+
+    # Decode kernel alone: back-to-back launches over the 28 layers (distinct caches,
+    # 2.8 GB per pass, far beyond the 256 MB last-level cache), events on the launch stream.
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(args.decode_reps):
+        run_decode()
+    d1.record()
+    torch.cuda.synchronize()
+    us_decode = d0.elapsed_time(d1) * 1e3 / (args.decode_reps * Lyr)
+    bytes_launch = algorithmic_bytes(lens, Hq, Hkv, D)
+    gbps = bytes_launch / (us_decode * 1e-6) / 1e9
+    print(f"[bench] decode {us_decode:.2f} us/launch, {gbps:.0f} GB/s", flush=True)
+
+    traffic = None
+    if os.path.exists(args.traffic_file):
+        try:
+            with open(args.traffic_file) as f:
+                tr = json.load(f)
+            if tr.get("kernel_source_hash") == _kernel_hash():
+                traffic = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "num_seqs": N, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "block_size": 16, "layers": Lyr, "num_blocks_per_layer": NB,
+                   "context": "256 + U{1..256} (new token included)",
+                   "step": "28 x (reshape_and_cache + decode)",
+                   "launch": "eager" if args.eager else "hipgraph",
+                   "split_tokens": args.split or pa.default_split_tokens(Hq, Hkv, D, torch.bfloat16)},
+        "hbm_gbps": round(gbps, 1),
+        "pct_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "decode_pass1",
+                     "us_per_launch": round(us_decode, 3), "algorithmic_bytes_per_launch": bytes_launch},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline ...", flush=True)
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def _kernel_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_gqa_pa_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        if n.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, n), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

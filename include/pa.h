@@ -1,0 +1,198 @@
+/*
+ * pa.h -- C ABI of libpa: paged grouped-query attention for LLM decoding on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the attention step of a decoding engine with a paged KV
+ * cache, as the page "From 183 ms to 19 ms per decode step" (mini-engine)
+ * describes it in section "Four changes, one profile at a time":
+ *   - change 2: the cache is head-major, [kv_heads, num_blocks, block_size,
+ *     head_dim], so one index over the slots of a head returns a sequence's
+ *     context in order;
+ *   - change 3: the kernel walks each sequence's block table and reads K and V
+ *     in place, one program per (sequence, KV head) serving every query head
+ *     of its group, with an fp32 online softmax (running max and sum,
+ *     rescaled per tile);
+ *   - change 4: each step hands the kernels fixed buffers of cache slots,
+ *     block tables and lengths;
+ * and in section "Then speculative decoding got slower": a kernel for a few
+ * query tokens per sequence (k+1 speculative tokens) with a causal mask
+ * among the new tokens.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory: every pointer argument is DEVICE memory owned by the caller,
+ *   contiguous and row-major in the shape given.  The library never
+ *   allocates, frees or synchronises, and never reads device memory on the
+ *   host.  Pointers to 16-bit or wider data must be 16-byte aligned.
+ * Streams: `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *   enqueues kernels on it and returns; results are valid once the stream has
+ *   reached that point.  No call records or waits on events, so calls can be
+ *   captured into a hipGraph.
+ * Dtypes: q / cache / out combinations supported:
+ *   PA_F32 / PA_F32 / fp32, PA_BF16 / PA_BF16 / bf16, PA_BF16 / PA_INT8 / bf16.
+ *   bf16 values are raw bfloat16 bit patterns; outputs are rounded to nearest
+ *   even.  Accumulation is fp32.
+ * int8 caches: signed codes in [-127, 127]; the value of a cached element is
+ *   code * scale[kv_head, physical_block] (one fp32 scale per block and KV
+ *   head, separately for K and V).
+ * Lengths: context_lens[b] is the number of cached positions sequence b
+ *   attends to, INCLUDING the token(s) being decoded -- write the new token's
+ *   K/V with pa_reshape_and_cache first, then attend (the decode loop of
+ *   "Anatomy of a Decode-Step Stall", section "Full Source", engine.py, writes
+ *   at the token's position and then attends over everything up to it).
+ *   A context length of 0 yields a zero output row.
+ * Block tables: block_tables[b, i] is the physical block of logical block i
+ *   of sequence b (positions 16*i .. 16*i+15).  Only the first
+ *   ceil(context_lens[b] / block_size) entries are read; the rest may hold
+ *   anything (e.g. -1).  Positions >= context_lens[b] are never read, so stale
+ *   or poisoned slots in a sequence's last block do not matter.
+ * Head mapping: query head h reads KV head h / (q_heads / kv_heads).
+ * Errors: each call returns a pa_status.  Argument errors are detected on the
+ *   host before anything is enqueued; a failed launch returns PA_ERR_HIP.
+ *   pa_last_error() returns a message for the calling thread's last failure.
+ *   Device-side preconditions are NOT checked (the host cannot read device
+ *   memory): block-table entries that are read must lie in [0, num_blocks),
+ *   context_lens[b] <= min(max_context_len, max_blocks_per_seq * block_size),
+ *   and slots must be < num_blocks * block_size.  Violating them reads or
+ *   writes out of bounds.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* null pointer, inconsistent sizes, bad enum   */
+  PA_ERR_UNSUPPORTED = -2,  /* valid but not built: dtype triple, head_dim, */
+                            /* group size or block size                     */
+  PA_ERR_WORKSPACE = -3,    /* workspace missing or too small               */
+  PA_ERR_HIP = -4           /* the HIP runtime reported a launch failure    */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2 } pa_dtype;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+/* Message describing the calling thread's most recent non-OK status. */
+const char* pa_last_error(void);
+
+/*
+ * pa_reshape_and_cache -- write new tokens' K and V into their cache slots.
+ *
+ * For each token i with slot_mapping[i] >= 0 and every KV head g:
+ *   k_cache[g, slot / block_size, slot % block_size, :] = key[i, g, :]
+ *   v_cache[g, slot / block_size, slot % block_size, :] = value[i, g, :]
+ * Tokens with a negative slot are skipped (padding rows).  Bits are copied
+ * unchanged; no other byte of either cache is touched.  Slots follow "From
+ * 183 ms to 19 ms per decode step", "Four changes", changes 2 and 4: a flat
+ * index over the (block, offset) slots of one head.
+ *
+ * key, value    [num_tokens, kv_heads, head_dim], dtype kv_dtype
+ * k_cache, v_cache [kv_heads, num_blocks, block_size, head_dim], kv_dtype
+ * slot_mapping  [num_tokens] int64
+ * kv_dtype      PA_F32 or PA_BF16 (PA_INT8 returns PA_ERR_UNSUPPORTED)
+ * head_dim      64 or 128; block_size 16.  num_tokens == 0 is a no-op.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int num_tokens, int kv_heads,
+                         int head_dim, int num_blocks, int block_size, int kv_dtype,
+                         void* stream);
+
+/*
+ * Split-K over context.  A sequence's context is cut into consecutive pieces
+ * of `split_tokens` positions (a multiple of block_size); each piece is
+ * reduced to a partial (normalised output, log-sum-exp) pair in fp32, and a
+ * second pass merges the pieces: with M = max_s lse_s and w_s = exp(lse_s-M),
+ * out = sum_s w_s o_s / sum_s w_s.  This is the online-softmax rescaling
+ * applied across pieces instead of across tiles.  The piece length depends
+ * only on the arguments given here, never on the lengths in the batch, so a
+ * sequence's result does not depend on what it is batched with.
+ *
+ * pa_default_split_tokens returns the piece length used when a call passes
+ * split_tokens = 0.
+ */
+int pa_default_split_tokens(int q_heads, int kv_heads, int head_dim, int kv_dtype);
+
+/*
+ * Workspace bytes pa_decode / pa_verify need for these sizes (0 when one
+ * piece covers max_context_len).  num_query_tokens is 1 for pa_decode.
+ * Returns 0 and sets pa_last_error on invalid sizes.
+ */
+size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv_heads,
+                         int head_dim, int max_context_len, int kv_dtype, int split_tokens);
+
+/*
+ * pa_decode -- one query token per sequence over the paged cache.
+ *
+ * out[b, h, :] = softmax_j(scale * <q[b, h, :], K_b[j, :]>) @ V_b[j, :]
+ * over positions j < context_lens[b], with K_b / V_b read in place through
+ * block_tables from KV head h / G.  ("From 183 ms to 19 ms per decode step",
+ * "Four changes", change 3; the per-row formula of "Anatomy of a Decode-Step
+ * Stall", "Full Source", engine.py.)
+ *
+ * out           [num_seqs, q_heads, head_dim], dtype q_dtype
+ * q             [num_seqs, q_heads, head_dim], dtype q_dtype
+ * k_cache, v_cache [kv_heads, num_blocks, block_size, head_dim], kv_dtype
+ * k_scale, v_scale [kv_heads, num_blocks] fp32; required for PA_INT8, else
+ *               ignored (may be NULL)
+ * block_tables  [num_seqs, max_blocks_per_seq] int32
+ * context_lens  [num_seqs] int32
+ * max_context_len  host-side upper bound of context_lens (sizes the grid and
+ *               the workspace; does not change the arithmetic)
+ * scale         softmax scale (typically 1/sqrt(head_dim))
+ * split_tokens  piece length, a positive multiple of block_size, or 0 for
+ *               pa_default_split_tokens()
+ * workspace     device scratch of at least pa_workspace_size(...) bytes
+ *               (may be NULL when that size is 0); contents on entry are
+ *               ignored.  Calls sharing one workspace must be ordered on one
+ *               stream.
+ * Supported: head_dim 64 or 128; block_size 16; q_heads / kv_heads in 1..8
+ * or 16; the dtype triples listed at the top.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const float* k_scale, const float* v_scale, const int32_t* block_tables,
+              const int32_t* context_lens, int num_seqs, int q_heads, int kv_heads,
+              int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+              int max_context_len, float scale, int q_dtype, int kv_dtype, int split_tokens,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_verify -- T = num_query_tokens new tokens per sequence (a speculative
+ * verify step of k+1 tokens), causal among themselves.
+ *
+ * context_lens[b] counts the cached positions INCLUDING the T new tokens,
+ * whose K/V must already be in the cache.  Query token t (0-based) sits at
+ * position context_lens[b] - T + t and attends to positions
+ * 0 .. context_lens[b] - T + t.  ("From 183 ms to 19 ms per decode step",
+ * section "Then speculative decoding got slower"; causal slicing as in the
+ * prefill code of "Anatomy of a Decode-Step Stall", "Full Source".)
+ * A sequence with context_lens[b] < T has no position for its earliest
+ * tokens; those rows see positions 0 .. context_lens[b] - T + t only, and a
+ * row that sees none returns zeros.
+ *
+ * out, q        [num_seqs, num_query_tokens, q_heads, head_dim], q_dtype
+ * other arguments as pa_decode.  num_query_tokens * (q_heads / kv_heads)
+ * must be <= 16 (the row count of one matrix-core tile).
+ * Supported dtypes: PA_BF16 / PA_BF16 and PA_F32 / PA_F32 (fp32 is rounded
+ * to bf16... no: fp32 inputs take the vector path and are not rounded).
+ */
+int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const float* k_scale, const float* v_scale, const int32_t* block_tables,
+              const int32_t* context_lens, int num_seqs, int num_query_tokens, int q_heads,
+              int kv_heads, int head_dim, int block_size, int num_blocks,
+              int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
+              int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

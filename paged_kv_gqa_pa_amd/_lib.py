@@ -1,0 +1,205 @@
+"""ctypes binding of libpa (argument marshalling only).
+
+Every function takes torch tensors on the GPU, checks their dtype, shape and
+contiguity, passes raw device pointers and the current HIP stream to the C
+ABI (``include/pa.h``), and raises ``PAError`` on a non-OK status.  All
+arithmetic runs in the HIP kernels; there is no fallback.
+
+torch is imported before the library is loaded so that libpa binds to the HIP
+runtime torch already loaded (both carry the soname libamdhip64.so.7), which
+makes torch's streams and device pointers valid inside libpa.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
+PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
+
+EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_default_split_tokens",
+            "pa_workspace_size", "pa_decode", "pa_verify"]
+
+_DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_INT8}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libpa status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m paged_kv_gqa_pa_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.pa_version.restype = i
+    lib.pa_version.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_reshape_and_cache.restype = i
+    lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.pa_default_split_tokens.restype = i
+    lib.pa_default_split_tokens.argtypes = [i, i, i, i]
+    lib.pa_workspace_size.restype = sz
+    lib.pa_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    lib.pa_decode.restype = i
+    lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,           # pointers
+                              i, i, i, i, i, i, i, i,                   # sizes
+                              f, i, i, i, vp, sz, vp]
+    lib.pa_verify.restype = i
+    lib.pa_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                              i, i, i, i, i, i, i, i, i,
+                              f, i, i, i, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _load()
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PAError(status, _load().pa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def version() -> int:
+    return _load().pa_version()
+
+
+def default_split_tokens(q_heads: int, kv_heads: int, head_dim: int, kv_dtype: torch.dtype) -> int:
+    return _load().pa_default_split_tokens(q_heads, kv_heads, head_dim, _DTYPE[kv_dtype])
+
+
+def workspace_size(num_seqs: int, num_query_tokens: int, q_heads: int, kv_heads: int,
+                   head_dim: int, max_context_len: int, kv_dtype: torch.dtype,
+                   split_tokens: int = 0) -> int:
+    return _load().pa_workspace_size(num_seqs, num_query_tokens, q_heads, kv_heads, head_dim,
+                                     max_context_len, _DTYPE[kv_dtype], split_tokens)
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
+    """Write key/value [num_tokens, kv_heads, head_dim] into the caches at slot_mapping."""
+    _need(key, "key", ndim=3)
+    _need(value, "value", dtype=key.dtype, ndim=3)
+    _need(k_cache, "k_cache", dtype=key.dtype, ndim=4)
+    _need(v_cache, "v_cache", dtype=key.dtype, ndim=4)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    H, NB, BS, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or key.shape != value.shape:
+        raise ValueError("cache or key/value shapes differ")
+    T = key.shape[0]
+    if key.shape[1:] != (H, D) or slot_mapping.shape[0] != T:
+        raise ValueError("key [num_tokens, kv_heads, head_dim] does not match the cache")
+    _check(_load().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(slot_mapping), T, H, D, NB, BS, _DTYPE[key.dtype],
+                                        _stream(stream)))
+
+
+def _attention(fn_verify: bool, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+               max_context_len, k_scale, v_scale, split_tokens, workspace, stream):
+    _need(q, "q")
+    _need(out, "out", dtype=q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    Hkv, NB, BS, D = k_cache.shape
+    if fn_verify:
+        if q.dim() != 4:
+            raise ValueError("verify q must be [num_seqs, num_query_tokens, q_heads, head_dim]")
+        N, T, Hq, Dq = q.shape
+    else:
+        if q.dim() != 3:
+            raise ValueError("decode q must be [num_seqs, q_heads, head_dim]")
+        N, Hq, Dq = q.shape
+        T = 1
+    if Dq != D or block_tables.shape[0] != N or context_lens.shape[0] != N:
+        raise ValueError("q, block_tables and context_lens disagree with the cache")
+    kvd = _DTYPE[k_cache.dtype]
+    if kvd == PA_INT8:
+        for nm, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{nm} is required for an int8 cache")
+            _need(s, nm, dtype=torch.float32, ndim=2)
+            if tuple(s.shape) != (Hkv, NB):
+                raise ValueError(f"{nm} must be [kv_heads, num_blocks]")
+    else:
+        k_scale = v_scale = None
+    need = _load().pa_workspace_size(N, T, Hq, Hkv, D, int(max_context_len), kvd, int(split_tokens))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib_ = _load()
+    if fn_verify:
+        st = lib_.pa_verify(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                            _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), N, T, Hq, Hkv,
+                            D, BS, NB, block_tables.shape[1], int(max_context_len), float(scale),
+                            _DTYPE[q.dtype], kvd, int(split_tokens), _ptr(workspace), ws_bytes,
+                            _stream(stream))
+    else:
+        st = lib_.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                            _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), N, Hq, Hkv, D,
+                            BS, NB, block_tables.shape[1], int(max_context_len), float(scale),
+                            _DTYPE[q.dtype], kvd, int(split_tokens), _ptr(workspace), ws_bytes,
+                            _stream(stream))
+    _check(st)
+    return out
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+           k_scale=None, v_scale=None, split_tokens=0, workspace=None, stream=None):
+    """Paged GQA decode: q/out [num_seqs, q_heads, head_dim]."""
+    return _attention(False, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, k_scale, v_scale, split_tokens, workspace, stream)
+
+
+def verify(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+           k_scale=None, v_scale=None, split_tokens=0, workspace=None, stream=None):
+    """Multi-token causal verify: q/out [num_seqs, num_query_tokens, q_heads, head_dim]."""
+    return _attention(True, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, k_scale, v_scale, split_tokens, workspace, stream)

@@ -1,0 +1,260 @@
+// C ABI of libpa: argument validation on the host, then kernel launches on the
+// caller's stream.  Nothing here allocates, synchronises or reads device
+// memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/pa.h"
+#include "pa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int elem_size(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : dt == PA_INT8 ? 1 : 0; }
+
+constexpr int kMaxGridYZ = 65535;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int split_tokens = 0;
+  int max_pieces = 1;
+  size_t o_bytes = 0;
+  size_t lse_bytes = 0;
+  size_t total() const { return max_pieces > 1 ? o_bytes + lse_bytes : 0; }
+};
+
+int default_split(int q_heads, int kv_heads, int head_dim, int kv_dtype) {
+  (void)q_heads;
+  (void)kv_heads;
+  (void)head_dim;
+  (void)kv_dtype;
+  return 512;
+}
+
+// Validates sizes shared by decode and verify and fills the split plan.
+int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
+                int max_context_len, int kv_dtype, int split_tokens, Plan* plan) {
+  if (num_seqs < 0 || T < 1 || q_heads <= 0 || kv_heads <= 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "invalid sizes: num_seqs=%d num_query_tokens=%d q_heads=%d kv_heads=%d "
+                "max_context_len=%d",
+                num_seqs, T, q_heads, kv_heads, max_context_len);
+  if (q_heads % kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "q_heads (%d) is not a multiple of kv_heads (%d)", q_heads,
+                kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_INT8)
+    return fail(PA_ERR_INVALID_ARG, "unknown kv dtype %d", kv_dtype);
+  int st = split_tokens == 0 ? default_split(q_heads, kv_heads, head_dim, kv_dtype) : split_tokens;
+  if (st <= 0 || st % pa::kBlockSizeHost != 0)
+    return fail(PA_ERR_INVALID_ARG, "split_tokens %d must be a positive multiple of %d",
+                split_tokens, pa::kBlockSizeHost);
+  plan->split_tokens = st;
+  plan->max_pieces = max_context_len > 0 ? (max_context_len + st - 1) / st : 1;
+  const size_t rows = size_t(num_seqs) * T * q_heads;
+  plan->o_bytes = round_up(rows * plan->max_pieces * head_dim * sizeof(float));
+  plan->lse_bytes = round_up(rows * plan->max_pieces * sizeof(float));
+  return PA_OK;
+}
+
+int check_attention_args(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         int num_seqs, int kv_heads, int block_size, int num_blocks,
+                         int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
+                         int kv_dtype) {
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", block_size);
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks (%d) and max_blocks_per_seq (%d) must be > 0",
+                num_blocks, max_blocks_per_seq);
+  if (long(max_context_len) > long(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds max_blocks_per_seq * block_size",
+                max_context_len);
+  const bool triple_ok = (q_dtype == PA_F32 && kv_dtype == PA_F32) ||
+                         (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
+                         (q_dtype == PA_BF16 && kv_dtype == PA_INT8);
+  if (!triple_ok) {
+    if (elem_size(q_dtype) == 0 || q_dtype == PA_INT8)
+      return fail(PA_ERR_INVALID_ARG, "invalid q dtype %d", q_dtype);
+    return fail(PA_ERR_UNSUPPORTED, "dtype pair q=%d kv=%d not built", q_dtype, kv_dtype);
+  }
+  if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (num_seqs > kMaxGridYZ || kv_heads > kMaxGridYZ)
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs and kv_heads must be <= %d", kMaxGridYZ);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (kv_dtype == PA_INT8 && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARG, "int8 cache needs k_scale and v_scale");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PA_ERR_INVALID_ARG, "out, q and the caches must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      (k_scale && !aligned(k_scale, 4)) || (v_scale && !aligned(v_scale, 4)))
+    return fail(PA_ERR_INVALID_ARG, "misaligned table, length or scale pointer");
+  return PA_OK;
+}
+
+int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
+                  const void* v_cache, const float* k_scale, const float* v_scale,
+                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int T,
+                  int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
+                  int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
+                  int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  Plan plan;
+  int st = plan_pieces(num_seqs, T, q_heads, kv_heads, head_dim, max_context_len, kv_dtype,
+                       split_tokens, &plan);
+  if (st != PA_OK) return st;
+  st = check_attention_args(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                            context_lens, num_seqs, kv_heads, block_size, num_blocks,
+                            max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype);
+  if (st != PA_OK) return st;
+  const int G = q_heads / kv_heads;
+  if (is_verify) {
+    if (!pa::verify_supported(q_dtype, kv_dtype, head_dim, G, T))
+      return fail(PA_ERR_UNSUPPORTED,
+                  "verify not built for q=%d kv=%d head_dim=%d group=%d tokens=%d", q_dtype,
+                  kv_dtype, head_dim, G, T);
+  } else if (!pa::decode_group_supported(G)) {
+    return fail(PA_ERR_UNSUPPORTED, "group size %d not built (1..8 or 16)", G);
+  }
+  if (num_seqs == 0) return PA_OK;
+  const size_t need = plan.total();
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu",
+                need, workspace ? workspace_bytes : size_t(0));
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.part_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.part_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes)
+                    : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_query_tokens = T;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.split_tokens = plan.split_tokens;
+  a.max_pieces = plan.max_pieces;
+  a.scale = scale;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = is_verify ? pa::launch_verify_pass1(a, s) : pa::launch_decode_pass1(a, s);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "pass-1 launch failed: %s", hipGetErrorString(e));
+  if (plan.max_pieces > 1) {
+    pa::MergeArgs m{};
+    m.out = out;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.context_lens = context_lens;
+    m.rows_per_seq = T * q_heads;
+    m.num_rows = num_seqs * m.rows_per_seq;
+    m.max_pieces = plan.max_pieces;
+    m.split_tokens = plan.split_tokens;
+    m.head_dim = head_dim;
+    m.out_dtype = q_dtype;
+    e = pa::launch_merge(m, s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return 100; }
+
+const char* pa_last_error(void) { return g_err; }
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int num_tokens, int kv_heads,
+                         int head_dim, int num_blocks, int block_size, int kv_dtype,
+                         void* stream) {
+  if (num_tokens < 0 || kv_heads <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "invalid sizes: num_tokens=%d kv_heads=%d num_blocks=%d",
+                num_tokens, kv_heads, num_blocks);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", block_size);
+  if (kv_dtype == PA_INT8)
+    return fail(PA_ERR_UNSUPPORTED, "int8 cache write is not built");
+  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "unknown kv dtype %d", kv_dtype);
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer argument");
+  pa::CacheArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, kv_heads, num_blocks,
+                  head_dim * elem_size(kv_dtype)};
+  hipError_t e = pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_default_split_tokens(int q_heads, int kv_heads, int head_dim, int kv_dtype) {
+  return default_split(q_heads, kv_heads, head_dim, kv_dtype);
+}
+
+size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv_heads,
+                         int head_dim, int max_context_len, int kv_dtype, int split_tokens) {
+  Plan plan;
+  if (plan_pieces(num_seqs, num_query_tokens, q_heads, kv_heads, head_dim, max_context_len,
+                  kv_dtype, split_tokens, &plan) != PA_OK)
+    return 0;
+  return plan.total();
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const float* k_scale, const float* v_scale, const int32_t* block_tables,
+              const int32_t* context_lens, int num_seqs, int q_heads, int kv_heads,
+              int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+              int max_context_len, float scale, int q_dtype, int kv_dtype, int split_tokens,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(false, out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
+                       split_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const float* k_scale, const float* v_scale, const int32_t* block_tables,
+              const int32_t* context_lens, int num_seqs, int num_query_tokens, int q_heads,
+              int kv_heads, int head_dim, int block_size, int num_blocks,
+              int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
+              int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  return run_attention(true, out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, num_seqs, num_query_tokens, q_heads, kv_heads, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       q_dtype, kv_dtype, split_tokens, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Device-side helpers shared by the libpa kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kBlockSize = 16;   // tokens per cache block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct bf16_t { uint16_t bits; };   // storage tag for bfloat16 data
+struct i8_t { int8_t v; };          // storage tag for int8 codes
+
+template <typename T> struct Bytes { static constexpr int value = sizeof(T); };
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Sum over groups of N consecutive lanes (N a power of two, N <= 64); every
+// lane of a group receives the group's sum.  Inside a 16-lane DPP row the
+// butterflies are quad_perm (lane ^ 1, lane ^ 2), then row_half_mirror and
+// row_mirror, which after the quad steps pair each quad with the other
+// quads of its half row and row.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, true);   // [1,0,3,2]
+  if constexpr (N >= 4) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, true);   // [2,3,0,1]
+  if constexpr (N >= 8) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  if constexpr (N >= 16) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, true); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// 16-byte streaming load (data read once: marked non-temporal).
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace pa

@@ -1,0 +1,70 @@
+// Internal launch interface between the C ABI (pa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum DType : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+
+constexpr int kBlockSizeHost = 16;  // tokens per cache block
+
+struct CacheArgs {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slot_mapping;
+  int num_tokens;
+  int kv_heads;
+  int num_blocks;
+  int row_bytes;  // head_dim * element size
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_o;    // [rows, max_pieces, head_dim]  (rows = num_seqs * T * q_heads)
+  float* part_lse;  // [rows, max_pieces], log2 domain
+  int num_seqs;
+  int num_query_tokens;  // T (1 for decode)
+  int q_heads;
+  int kv_heads;
+  int head_dim;
+  int num_blocks;
+  int max_blocks_per_seq;
+  int split_tokens;
+  int max_pieces;
+  float scale;
+  int q_dtype;
+  int kv_dtype;
+};
+
+struct MergeArgs {
+  void* out;
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* context_lens;
+  int num_rows;
+  int rows_per_seq;
+  int max_pieces;
+  int split_tokens;
+  int head_dim;
+  int out_dtype;
+};
+
+hipError_t launch_reshape_and_cache(const CacheArgs& a, hipStream_t stream);
+hipError_t launch_decode_pass1(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_verify_pass1(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+bool decode_group_supported(int G);
+bool verify_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T);
+
+}  // namespace pa

@@ -1,0 +1,50 @@
+"""Moving seeded workloads onto the GPU and results back (no attention arithmetic)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "int8": 2e-2}
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    """numpy stored form -> GPU tensor (uint16 bit patterns become bfloat16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bytes of a GPU tensor as a numpy array (bf16 -> uint16 bit patterns)."""
+    if t.dtype == torch.bfloat16:
+        return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+class DevCase:
+    """GPU copies of a PagedCase's arrays."""
+
+    def __init__(self, case):
+        self.case = case
+        self.q = dev(case.q)
+        self.k_cache = dev(case.k_cache)
+        self.v_cache = dev(case.v_cache)
+        self.block_tables = dev(case.block_tables)
+        self.context_lens = dev(case.context_lens)
+        self.k_scale = None if case.k_scale is None else dev(case.k_scale)
+        self.v_scale = None if case.v_scale is None else dev(case.v_scale)
+        self.new_k = dev(case.new_k)
+        self.new_v = dev(case.new_v)
+        self.slot_mapping = dev(case.slot_mapping)
+
+
+def max_abs_err(gpu: torch.Tensor, want: np.ndarray) -> float:
+    got = host_f64(gpu)
+    assert got.shape == want.shape
+    assert np.isfinite(got).all(), "non-finite output"
+    return float(np.abs(got - want).max()) if got.size else 0.0

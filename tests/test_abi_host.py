@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load, export every function include/pa.h declares, and
+reject invalid arguments on the host before anything would be launched (these
+calls pass NULL or dummy pointers that are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_gqa_pa_amd import _lib as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "pa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(pa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pa.lib()
+    names = declared_functions()
+    assert set(names) >= {"pa_decode", "pa_verify", "pa_reshape_and_cache"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(pa.EXPORTED) == names
+
+
+def test_version_and_default_split():
+    assert pa.lib().pa_version() >= 100
+    st = pa.lib().pa_default_split_tokens(16, 8, 128, pa.PA_BF16)
+    assert st > 0 and st % 16 == 0
+
+
+def test_workspace_size():
+    lib = pa.lib()
+    st = lib.pa_default_split_tokens(12, 2, 128, pa.PA_INT8)
+    # one piece covers the context: no workspace
+    assert lib.pa_workspace_size(64, 1, 16, 8, 128, st, pa.PA_BF16, 0) == 0
+    n = lib.pa_workspace_size(8, 1, 12, 2, 128, 32768, pa.PA_INT8, 512)
+    pieces = 32768 // 512
+    rows = 8 * 12
+    o = rows * pieces * 128 * 4
+    lse = rows * pieces * 4
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert n == rnd(o) + rnd(lse)
+    # invalid sizes give 0
+    assert lib.pa_workspace_size(8, 1, 12, 5, 128, 100, pa.PA_BF16, 0) == 0
+    assert lib.pa_workspace_size(8, 1, 12, 2, 128, 100, pa.PA_BF16, 24) == 0
+
+
+def _decode_status(**kw):
+    lib = pa.lib()
+    a = dict(out=None, q=None, k=None, v=None, ks=None, vs=None, bt=None, cl=None, N=4, Hq=2,
+             Hkv=1, D=64, bs=16, NB=16, MB=4, ML=64, scale=0.125, qd=pa.PA_F32, kd=pa.PA_F32,
+             split=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    st = lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["cl"],
+                       a["N"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["ML"],
+                       ctypes.c_float(a["scale"]), a["qd"], a["kd"], a["split"], a["ws"],
+                       a["wsb"], a["stream"])
+    return st, lib.pa_last_error().decode()
+
+
+FAKE = 0x1000  # aligned non-null dummy address; never dereferenced on these paths
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=3, Hkv=2), pa.PA_ERR_INVALID_ARG),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(split=24), pa.PA_ERR_INVALID_ARG),
+    (dict(ML=65), pa.PA_ERR_INVALID_ARG),
+    (dict(qd=pa.PA_F32, kd=pa.PA_BF16), pa.PA_ERR_UNSUPPORTED),
+    (dict(qd=7), pa.PA_ERR_INVALID_ARG),
+    (dict(N=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(Hq=40, Hkv=1), pa.PA_ERR_INVALID_ARG),   # nulls reported before group size
+    (dict(scale=float("nan")), pa.PA_ERR_INVALID_ARG),
+    (dict(), pa.PA_ERR_INVALID_ARG),                # null pointers
+])
+def test_decode_rejects_invalid_arguments(kw, status):
+    st, msg = _decode_status(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_decode_group_size_and_workspace_checked_before_launch():
+    ptrs = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE)
+    st, msg = _decode_status(Hq=40, Hkv=1, **ptrs)
+    assert st == pa.PA_ERR_UNSUPPORTED, msg
+    # a long context needs a workspace: missing -> PA_ERR_WORKSPACE
+    st, msg = _decode_status(ML=64, MB=4, split=16, **ptrs)
+    assert st == pa.PA_ERR_WORKSPACE, msg
+    # int8 needs scales
+    st, msg = _decode_status(qd=pa.PA_BF16, kd=pa.PA_INT8, **ptrs)
+    assert st == pa.PA_ERR_INVALID_ARG and "scale" in msg
+    # zero sequences is a no-op
+    st, msg = _decode_status(N=0)
+    assert st == pa.PA_OK, msg
+
+
+def test_cache_write_rejects_invalid_arguments():
+    lib = pa.lib()
+
+    def call(**kw):
+        a = dict(key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, T=4, H=2, D=128, NB=8,
+                 bs=16, dt=pa.PA_BF16)
+        a.update(kw)
+        return lib.pa_reshape_and_cache(a["key"], a["value"], a["kc"], a["vc"], a["slots"],
+                                        a["T"], a["H"], a["D"], a["NB"], a["bs"], a["dt"], None)
+
+    assert call(D=80) == pa.PA_ERR_UNSUPPORTED
+    assert call(bs=8) == pa.PA_ERR_UNSUPPORTED
+    assert call(dt=pa.PA_INT8) == pa.PA_ERR_UNSUPPORTED
+    assert call(dt=9) == pa.PA_ERR_INVALID_ARG
+    assert call(key=None) == pa.PA_ERR_INVALID_ARG
+    assert call(key=FAKE + 4) == pa.PA_ERR_INVALID_ARG
+    assert call(T=-1) == pa.PA_ERR_INVALID_ARG
+    assert call(T=0, key=None) == pa.PA_OK

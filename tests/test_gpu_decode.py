@@ -1,0 +1,253 @@
+"""GPU parity of pa_reshape_and_cache and pa_decode against the fp64 oracle.
+
+Every case prints what it runs before touching the GPU.  Tolerances: max-abs
+1e-4 for fp32, 2e-2 for bf16 output (bf16 and int8 caches); cache writes and
+placement / batch invariance are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_gqa_pa_amd import _lib as pa
+from paged_kv_gqa_pa_amd import workloads as wl
+from tests.gpu_util import TOL, DevCase, dev, host_bits, max_abs_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _decode(dc, split_tokens=0, max_len=None, q=None, block_tables=None, k_cache=None,
+            v_cache=None, context_lens=None):
+    case = dc.case
+    q = dc.q if q is None else q
+    out = torch.empty_like(q)
+    pa.decode(out, q, dc.k_cache if k_cache is None else k_cache,
+              dc.v_cache if v_cache is None else v_cache,
+              dc.block_tables if block_tables is None else block_tables,
+              dc.context_lens if context_lens is None else context_lens, case.scale,
+              case.max_context_len if max_len is None else max_len, dc.k_scale, dc.v_scale,
+              split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_decode(case, q=None):
+    return oracle.decode(case.q if q is None else q, case.k_cache, case.v_cache,
+                         case.block_tables, case.context_lens, case.scale, case.spec.q_dtype,
+                         case.spec.kv_dtype, case.k_scale, case.v_scale)
+
+
+@pytest.mark.parametrize("split", [0, 16, 32, 48])
+def test_tiny_fp32_parity(split):
+    _say("tiny_fp32 poison split", split)
+    case = wl.build_case("tiny_fp32", poison=True)
+    dc = DevCase(case)
+    out = _decode(dc, split)
+    err = max_abs_err(out, _oracle_decode(case))
+    assert err < TOL["f32"], err
+
+
+@pytest.mark.parametrize("split", [0, 64, 128])
+def test_qwen2_layer_bf16_parity(split):
+    _say("qwen2_1p5b_bf16 split", split)
+    case = wl.build_case("qwen2_1p5b_bf16", poison=True)
+    dc = DevCase(case)
+    out = _decode(dc, split)
+    err = max_abs_err(out, _oracle_decode(case))
+    assert err < TOL["bf16"], err
+
+
+@pytest.mark.parametrize("layer", [0, 27])
+def test_batch64_cache_write_then_decode(layer):
+    """Full-size batch-64 layer: write the new token, compare whole caches, decode."""
+    _say("batch64_28layer_bf16 layer", layer)
+    case = wl.build_case("batch64_28layer_bf16", layer=layer)
+    dc = DevCase(case)
+    pa.reshape_and_cache(dc.new_k, dc.new_v, dc.k_cache, dc.v_cache, dc.slot_mapping)
+    torch.cuda.synchronize()
+    want_k, want_v = oracle.reshape_and_cache(case.new_k, case.new_v, case.k_cache,
+                                              case.v_cache, case.slot_mapping)
+    assert host_bits(dc.k_cache).tobytes() == want_k.tobytes()
+    assert host_bits(dc.v_cache).tobytes() == want_v.tobytes()
+    case.k_cache, case.v_cache = want_k, want_v
+    out = _decode(dc)
+    err = max_abs_err(out, _oracle_decode(case))
+    assert err < TOL["bf16"], err
+
+
+def test_long_ctx_int8_parity():
+    _say("long_ctx_int8 default split")
+    case = wl.build_case("long_ctx_int8")
+    dc = DevCase(case)
+    out = _decode(dc)
+    err = max_abs_err(out, _oracle_decode(case))
+    assert err < TOL["int8"], err
+
+
+def test_long_ctx_int8_poison_and_small_split():
+    _say("long_ctx_int8 poison, first 2 seqs, split 256")
+    case = wl.build_case("long_ctx_int8", poison=True)
+    dc = DevCase(case)
+    sel = slice(0, 2)
+    out = torch.empty_like(dc.q[sel])
+    pa.decode(out, dc.q[sel].contiguous(), dc.k_cache, dc.v_cache,
+              dc.block_tables[sel].contiguous(), dc.context_lens[sel].contiguous(), case.scale,
+              case.max_context_len, dc.k_scale, dc.v_scale, split_tokens=256)
+    torch.cuda.synchronize()
+    want = oracle.decode(case.q[sel], case.k_cache, case.v_cache, case.block_tables[sel],
+                         case.context_lens[sel], case.scale, "bf16", "int8", case.k_scale,
+                         case.v_scale)
+    assert max_abs_err(out, want) < TOL["int8"]
+
+
+def test_placement_invariance_bitwise():
+    _say("placement invariance qwen2_1p5b_bf16")
+    case = wl.build_case("qwen2_1p5b_bf16")
+    dc = DevCase(case)
+    base = _decode(dc, 64)
+    relabel = np.random.default_rng(11).permutation(case.spec.num_blocks).astype(np.int32)
+    kc2 = np.empty_like(case.k_cache)
+    vc2 = np.empty_like(case.v_cache)
+    kc2[:, relabel] = case.k_cache
+    vc2[:, relabel] = case.v_cache
+    t = case.block_tables
+    t2 = np.where(t >= 0, relabel[np.maximum(t, 0)], -1).astype(np.int32)
+    moved = _decode(dc, 64, block_tables=dev(t2), k_cache=dev(kc2), v_cache=dev(vc2))
+    assert torch.equal(base.view(torch.int16), moved.view(torch.int16))
+
+
+def test_batch_invariance_bitwise():
+    """A sequence alone gives the same bits as inside the batch (fixed piece length)."""
+    _say("batch invariance qwen2_1p5b_bf16")
+    case = wl.build_case("qwen2_1p5b_bf16")
+    dc = DevCase(case)
+    full = _decode(dc, 128)
+    for b in (0, 5, 31):
+        one = torch.empty_like(dc.q[b:b + 1])
+        pa.decode(one, dc.q[b:b + 1].contiguous(), dc.k_cache, dc.v_cache,
+                  dc.block_tables[b:b + 1].contiguous(), dc.context_lens[b:b + 1].contiguous(),
+                  case.scale, int(case.context_lens[b]), split_tokens=128)
+        torch.cuda.synchronize()
+        assert torch.equal(one.view(torch.int16), full[b:b + 1].view(torch.int16)), b
+
+
+def test_split_invariance_fp32():
+    _say("split invariance fp32")
+    rng = np.random.default_rng(5)
+    lens = np.array([1, 15, 16, 17, 100, 257, 600], np.int32)
+    case = _random_case(rng, lens, Hkv=2, G=3, D=128, tag="f32")
+    dc = DevCase(case)
+    want = _oracle_decode(case)
+    outs = []
+    for split in (16, 64, 256, 512, 1024):
+        o = _decode(dc, split)
+        assert max_abs_err(o, want) < TOL["f32"], split
+        outs.append(o.double().cpu().numpy())
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() < 1e-6
+
+
+def _random_case(rng, lens, Hkv, G, D, tag, qtag=None, nb=None):
+    """A PagedCase-like object with random contents for the given lengths."""
+    qtag = qtag or ("f32" if tag == "f32" else "bf16")
+    lens = np.asarray(lens, np.int32)
+    maxb = max(1, -(-int(lens.max()) // 16))
+    need = int(sum(-(-int(L) // 16) for L in lens))
+    nb = nb or need + 3
+    table = wl.assign_blocks(lens, rng.permutation(nb).astype(np.int32), maxb)
+    N = len(lens)
+    k32 = rng.standard_normal((Hkv, nb, 16, D), dtype=np.float32)
+    v32 = rng.standard_normal((Hkv, nb, 16, D), dtype=np.float32)
+    ks = vs = None
+    if tag == "int8":
+        kc, ks = wl.quantize_int8_blocks(k32)
+        vc, vs = wl.quantize_int8_blocks(v32)
+    else:
+        kc, vc = wl.encode(k32, tag), wl.encode(v32, tag)
+    q = wl.encode(rng.standard_normal((N, Hkv * G, D), dtype=np.float32), qtag)
+    spec = wl.Spec("random", 0, N, Hkv * G, Hkv, D, nb, qtag, tag, max(16, int(lens.max())))
+    return wl.PagedCase(spec=spec, layer=0, context_lens=lens, block_tables=table, q=q,
+                        k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs,
+                        new_k=np.zeros((0, Hkv, D), kc.dtype), new_v=np.zeros((0, Hkv, D), kc.dtype),
+                        slot_mapping=np.zeros(0, np.int64), scale=1.0 / np.sqrt(D))
+
+
+EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 200, 511, 512, 513, 1000]
+
+
+@pytest.mark.parametrize("tag", ["f32", "bf16", "int8"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 16])
+def test_edge_lengths_all_shapes(tag, D, G):
+    _say("edge lengths", tag, "D", D, "G", G)
+    rng = np.random.default_rng(100 + G + D)
+    case = _random_case(rng, EDGE_LENS, Hkv=2, G=G, D=D, tag=tag)
+    dc = DevCase(case)
+    want = _oracle_decode(case)
+    for split in (0, 32):
+        out = _decode(dc, split)
+        assert max_abs_err(out, want) < TOL[tag], (split, max_abs_err(out, want))
+        got = out.float().cpu().numpy()
+        assert (got[0] == 0).all(), "empty context must give zeros"
+    if tag != "int8":
+        # one position: the output is that position's V row exactly
+        vrow = oracle.widen(case.v_cache[:, case.block_tables[1, 0], 0, :], tag)   # [Hkv, D]
+        got = out.double().cpu().numpy()[1]
+        assert np.array_equal(got, np.repeat(vrow, G, axis=0))
+
+
+def test_equal_keys_give_mean_of_v():
+    _say("equal keys")
+    rng = np.random.default_rng(9)
+    case = _random_case(rng, [37, 300], Hkv=1, G=4, D=128, tag="f32")
+    case.k_cache[...] = case.k_cache[0, 0, 0]
+    dc = DevCase(case)
+    out = _decode(dc, 64)
+    for b, L in enumerate(case.context_lens):
+        rows = oracle.gather_context(case.v_cache, case.block_tables[b], int(L), 0, "f32")
+        assert np.abs(out[b].double().cpu().numpy() - rows.mean(0)).max() < 1e-5
+
+
+def test_poisoned_tail_and_spare_blocks_bitwise():
+    _say("poison vs clean bf16")
+    clean = wl.build_case("qwen2_1p5b_bf16")
+    dirty = wl.build_case("qwen2_1p5b_bf16", poison=True)
+    a = _decode(DevCase(clean), 0)
+    b = _decode(DevCase(dirty), 0)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+def test_cache_write_skips_negative_slots_and_touches_nothing_else(tag):
+    _say("cache write", tag)
+    rng = np.random.default_rng(17)
+    Hkv, nb, D = 3, 9, 128 if tag == "bf16" else 64
+    kc = wl.encode(rng.standard_normal((Hkv, nb, 16, D), dtype=np.float32), tag)
+    vc = wl.encode(rng.standard_normal((Hkv, nb, 16, D), dtype=np.float32), tag)
+    key = wl.encode(rng.standard_normal((7, Hkv, D), dtype=np.float32), tag)
+    val = wl.encode(rng.standard_normal((7, Hkv, D), dtype=np.float32), tag)
+    slots = np.array([3, -1, 16 * nb - 1, 40, -7, 0, 77], np.int64)
+    dk, dv = dev(kc), dev(vc)
+    pa.reshape_and_cache(dev(key), dev(val), dk, dv, dev(slots))
+    torch.cuda.synchronize()
+    wk, wv = oracle.reshape_and_cache(key, val, kc, vc, slots)
+    assert host_bits(dk).tobytes() == wk.tobytes()
+    assert host_bits(dv).tobytes() == wv.tobytes()
+
+
+def test_invalid_arguments_raise_before_launch():
+    case = wl.build_case("tiny_fp32")
+    dc = DevCase(case)
+    out = torch.empty_like(dc.q)
+    with pytest.raises(pa.PAError) as ei:
+        pa.decode(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                  case.scale, 64, split_tokens=24)
+    assert ei.value.status == pa.PA_ERR_INVALID_ARG
+    with pytest.raises(pa.PAError) as ei:
+        pa.decode(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                  case.scale, 64 * 16 + 1)
+    assert ei.value.status == pa.PA_ERR_INVALID_ARG
