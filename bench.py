@@ -40,6 +40,9 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--decode-reps", type=int, default=20,
                    help="graph replays of the 28 decode launches for the per-kernel timing")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one 256 MiB device-to-device copy (known bytes) so hardware "
+                        "byte counters can be scaled")
     p.add_argument("--traffic-file", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "profiles", "pa_decode_batch64_traffic.json"))
     return p.parse_args()
@@ -142,7 +145,7 @@ def main():
         outs.append(torch.empty((N, Hq, D), device=dev, dtype=torch.bfloat16))
     max_len = spec.max_len
     ws_bytes = pa.workspace_size(N, 1, Hq, Hkv, D, max_len, torch.bfloat16, args.split)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     scale = 1.0 / float(np.sqrt(D))
     torch.cuda.synchronize()
     print(f"[bench] caches ready: {2 * Lyr * kc[0].numel() * 2 / 2**30:.1f} GiB, "
@@ -183,6 +186,13 @@ def main():
             run_step()
         torch.cuda.synchronize()
     print("[bench] warm", flush=True)
+    if args.calibrate_copy:
+        src = torch.ones(256 << 18, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 256 MiB read + 256 MiB written", flush=True)
+        del src, dst
 
     # Whole step: K steps between two events, synchronised on both sides.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -108,8 +108,9 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
 /*
  * Split-K over context.  A sequence's context is cut into consecutive pieces
  * of `split_tokens` positions (a multiple of block_size); each piece is
- * reduced to a partial (normalised output, log-sum-exp) pair in fp32, and a
- * second pass merges the pieces: with M = max_s lse_s and w_s = exp(lse_s-M),
+ * reduced to a partial (normalised output, log-sum-exp) pair in fp32, and the
+ * last piece of a (sequence, KV head) to finish merges them in piece order:
+ * with M = max_s lse_s and w_s = exp(lse_s - M),
  * out = sum_s w_s o_s / sum_s w_s.  This is the online-softmax rescaling
  * applied across pieces instead of across tiles.  The piece length depends
  * only on the arguments given here, never on the lengths in the batch, so a
@@ -147,12 +148,17 @@ size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv
  * max_context_len  host-side upper bound of context_lens (sizes the grid and
  *               the workspace; does not change the arithmetic)
  * scale         softmax scale (typically 1/sqrt(head_dim))
- * split_tokens  piece length, a positive multiple of block_size, or 0 for
- *               pa_default_split_tokens()
- * workspace     device scratch of at least pa_workspace_size(...) bytes
- *               (may be NULL when that size is 0); contents on entry are
- *               ignored.  Calls sharing one workspace must be ordered on one
- *               stream.
+ * split_tokens  piece length, a multiple of block_size in [16, 1024], or 0
+ *               for pa_default_split_tokens()
+ * workspace     device scratch of at least pa_workspace_size(...) bytes,
+ *               256-byte aligned (may be NULL when that size is 0).  Its
+ *               first 256 KiB hold one arrival counter per (sequence, KV
+ *               head); the rest holds the pieces' partial outputs.  Zero-fill
+ *               it once before its first use: every completed call leaves the
+ *               counters at zero again, so the same workspace then serves any
+ *               later call it is large enough for.  Calls sharing one
+ *               workspace must be ordered on one stream.  With more than one
+ *               piece, num_seqs * kv_heads must be <= 65536.
  * Supported: head_dim 64 or 128; block_size 16; q_heads / kv_heads in 1..8
  * or 16; the dtype triples listed at the top.
  */

@@ -24,7 +24,7 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 
 int elem_size(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : dt == PA_INT8 ? 1 : 0; }
 
-constexpr int kMaxGridYZ = 65535;
+constexpr long kMaxGrid = 2147483647L;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -34,7 +34,8 @@ struct Plan {
   int max_pieces = 1;
   size_t o_bytes = 0;
   size_t lse_bytes = 0;
-  size_t total() const { return max_pieces > 1 ? o_bytes + lse_bytes : 0; }
+  size_t ticket_bytes = 0;
+  size_t total() const { return max_pieces > 1 ? o_bytes + lse_bytes + ticket_bytes : 0; }
 };
 
 int default_split(int q_heads, int kv_heads, int head_dim, int kv_dtype) {
@@ -42,7 +43,11 @@ int default_split(int q_heads, int kv_heads, int head_dim, int kv_dtype) {
   (void)kv_heads;
   (void)head_dim;
   (void)kv_dtype;
+#ifdef PA_DEFAULT_SPLIT
+  return PA_DEFAULT_SPLIT;
+#else
   return 512;
+#endif
 }
 
 // Validates sizes shared by decode and verify and fills the split plan.
@@ -61,14 +66,24 @@ int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
   if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_INT8)
     return fail(PA_ERR_INVALID_ARG, "unknown kv dtype %d", kv_dtype);
   int st = split_tokens == 0 ? default_split(q_heads, kv_heads, head_dim, kv_dtype) : split_tokens;
-  if (st <= 0 || st % pa::kBlockSizeHost != 0)
-    return fail(PA_ERR_INVALID_ARG, "split_tokens %d must be a positive multiple of %d",
-                split_tokens, pa::kBlockSizeHost);
+  if (st <= 0 || st % pa::kBlockSizeHost != 0 || st > pa::kMaxSplitTokens)
+    return fail(PA_ERR_INVALID_ARG, "split_tokens %d must be a multiple of %d in [%d, %d]",
+                split_tokens, pa::kBlockSizeHost, pa::kBlockSizeHost, pa::kMaxSplitTokens);
   plan->split_tokens = st;
   plan->max_pieces = max_context_len > 0 ? (max_context_len + st - 1) / st : 1;
   const size_t rows = size_t(num_seqs) * T * q_heads;
   plan->o_bytes = round_up(rows * plan->max_pieces * head_dim * sizeof(float));
   plan->lse_bytes = round_up(rows * plan->max_pieces * sizeof(float));
+  // Arrival counters sit in a fixed region at the start of every workspace, so
+  // partial outputs of one call never overlap the counters of another call,
+  // whatever their shapes: a workspace zeroed once stays valid.
+  plan->ticket_bytes = size_t(pa::kMaxTicketPairs) * sizeof(int);
+  if (plan->max_pieces > 1 && long(num_seqs) * kv_heads > pa::kMaxTicketPairs)
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs * kv_heads > %d with several pieces per sequence",
+                pa::kMaxTicketPairs);
+  if (long(plan->max_pieces) * num_seqs * kv_heads > kMaxGrid)
+    return fail(PA_ERR_UNSUPPORTED, "too many workgroups: pieces * num_seqs * kv_heads > %ld",
+                kMaxGrid);
   return PA_OK;
 }
 
@@ -94,8 +109,6 @@ int check_attention_args(void* out, const void* q, const void* k_cache, const vo
     return fail(PA_ERR_UNSUPPORTED, "dtype pair q=%d kv=%d not built", q_dtype, kv_dtype);
   }
   if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (num_seqs > kMaxGridYZ || kv_heads > kMaxGridYZ)
-    return fail(PA_ERR_UNSUPPORTED, "num_seqs and kv_heads must be <= %d", kMaxGridYZ);
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
@@ -148,9 +161,10 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.v_scale = v_scale;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.part_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
-  a.part_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes)
-                    : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.tickets = need ? reinterpret_cast<int*>(ws) : nullptr;
+  a.part_lse = need ? reinterpret_cast<float*>(ws + plan.ticket_bytes) : nullptr;
+  a.part_o = need ? reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.lse_bytes) : nullptr;
   a.num_seqs = num_seqs;
   a.num_query_tokens = T;
   a.q_heads = q_heads;
@@ -166,21 +180,6 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = is_verify ? pa::launch_verify_pass1(a, s) : pa::launch_decode_pass1(a, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pass-1 launch failed: %s", hipGetErrorString(e));
-  if (plan.max_pieces > 1) {
-    pa::MergeArgs m{};
-    m.out = out;
-    m.part_o = a.part_o;
-    m.part_lse = a.part_lse;
-    m.context_lens = context_lens;
-    m.rows_per_seq = T * q_heads;
-    m.num_rows = num_seqs * m.rows_per_seq;
-    m.max_pieces = plan.max_pieces;
-    m.split_tokens = plan.split_tokens;
-    m.head_dim = head_dim;
-    m.out_dtype = q_dtype;
-    e = pa::launch_merge(m, s);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
-  }
   return PA_OK;
 }
 

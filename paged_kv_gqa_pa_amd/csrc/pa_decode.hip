@@ -17,14 +17,21 @@
 // once at the end.
 //
 // With a single piece the workgroup writes the output row directly.  With
-// several pieces it writes a normalised partial output and its log2-sum-exp
-// to the workspace, and pass 2 merges the pieces of each (sequence, head).
+// several pieces each workgroup writes a normalised partial output and its
+// log2-sum-exp to the workspace, and the last workgroup of a (sequence, KV
+// head) to finish merges them (no second launch).
 // Piece length is fixed per call (never derived from the lengths in the
 // batch), so each sequence's arithmetic depends on its own length only.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
 namespace pa {
+#ifdef PA_TIMING
+__device__ unsigned long long g_times[8192 * 6];
+#define PA_STAMP(k) do { if (threadIdx.x == 0 && blockIdx.x < 8192) { g_times[blockIdx.x * 6 + (k)] = __builtin_amdgcn_s_memrealtime(); if ((k) == 0) g_times[blockIdx.x * 6 + 5] = (unsigned long long)__builtin_amdgcn_s_getreg(4 | (31 << 11)) | ((unsigned long long)__builtin_amdgcn_s_getreg(20 | (31 << 11)) << 32); } } while (0)
+#else
+#define PA_STAMP(k) do { } while (0)
+#endif
 namespace {
 
 // Byte k of x as a float; the backend selects v_cvt_f32_ubyte{k}.
@@ -177,37 +184,94 @@ template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v
 }
 
 // ---------------------------------------------------------------------------
+// Merge of pieces inside the attention kernel.  Every workgroup of a
+// multi-piece (sequence, KV head) stores its partials, then takes a ticket;
+// the one that draws the last ticket merges all pieces in piece order (so the
+// result does not depend on arrival order) and resets the ticket to zero for
+// the next call.  The agent-scope fences order the partial stores before the
+// ticket and the ticket before the merging workgroup's reads, across XCDs.
+// ---------------------------------------------------------------------------
+template <typename O, int D, int R>
+__device__ __forceinline__ void merge_if_last(void* out, const float* part_o,
+                                              const float* part_lse, int* ticket, int n_pieces,
+                                              int max_pieces, size_t row0, int nthreads) {
+  __shared__ int s_last;
+  // The barrier orders every thread's partial stores before thread 0's
+  // agent-scope release; one fence per workgroup (an L2 write-back) instead of
+  // one per wave.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    s_last = atomicAdd(ticket, 1) == n_pieces - 1;
+    if (s_last) __threadfence();  // acquire: the other pieces' partials
+  }
+  __syncthreads();
+  if (!s_last) return;
+  for (int t = threadIdx.x; t < R * D; t += nthreads) {
+    const int r = t / D, d = t % D;
+    const size_t prow = (row0 + r) * max_pieces;
+    const float* lse = part_lse + prow;
+    float M = kNegInf;
+    for (int s = 0; s < n_pieces; ++s) M = fmaxf(M, __builtin_nontemporal_load(lse + s));
+    float wsum = 0.0f, o = 0.0f;
+    for (int s = 0; s < n_pieces; ++s) {
+      const float ls = __builtin_nontemporal_load(lse + s);
+      const float w = ls == kNegInf ? 0.0f : fast_exp2(ls - M);
+      wsum += w;
+      o = __builtin_fmaf(w, __builtin_nontemporal_load(part_o + (prow + s) * D + d), o);
+    }
+    store_out(reinterpret_cast<O*>(out) + (row0 + r) * D + d, wsum > 0.0f ? o / wsum : 0.0f);
+  }
+  if (threadIdx.x == 0) *ticket = 0;
+}
+
+// ---------------------------------------------------------------------------
 // Pass 1
 // ---------------------------------------------------------------------------
-template <typename Q, typename KV, int D, int G, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_pass1(DecodeArgs a) {
+// With 8 waves per workgroup, keep two workgroups per CU (4 waves per SIMD,
+// at most 128 VGPRs); with 4 the register budget is left to the compiler.
+template <typename Q, typename KV, int D, int G, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode_pass1(DecodeArgs a) {
   using GE = Geo<KV, D>;
   constexpr int EPL = GE::EPL, LPK = GE::LPK, KPL = GE::KPL, LPB = GE::LPB;
   constexpr bool kInt8 = __is_same(KV, i8_t);
 
-  const int piece = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  // Lengths beyond the table or the host bound are clamped so that no access
-  // leaves the buffers (the result of such a call is unspecified).
-  const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
-  const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
-  if (piece >= n_pieces) return;
-
+  // 1-D grid, piece-major: ids 0 .. N*Hkv-1 are piece 0 of every (sequence,
+  // KV head), then piece 1, ...  Consecutive ids go to different XCDs, so the
+  // always-present first pieces spread evenly over the chip, and all pieces of
+  // one (sequence, head) land on the same XCD whenever N*Hkv is a multiple of 8.
+  PA_STAMP(0);
+  const int pairs = a.num_seqs * a.kv_heads;
+  const int piece = blockIdx.x / pairs;
+  const int pair = blockIdx.x - piece * pairs;
+  const int b = pair / a.kv_heads;
+  const int g = pair - b * a.kv_heads;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPK;   // key row inside a load
   const int c = lane % LPK;   // 16-byte column of the key row
+  const int split_blocks = a.split_tokens / kBlockSize;
+  const int blk_begin = piece * split_blocks;
 
+  // Issue the loads that do not depend on the context length first, so the
+  // length, the block-table row and q arrive in one round trip: the piece's
+  // table entries (at most 64, one per lane; a tile's physical block is then
+  // read with readlane) and this group's query rows.
+  const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
+  const int tab = blk_begin + lane < a.max_blocks_per_seq ? bt[blk_begin + lane] : 0;
   const int q_stride = a.head_dim;  // elements between consecutive heads
   const Q* qrow = reinterpret_cast<const Q*>(a.q) + (size_t(b) * a.q_heads + size_t(g) * G) * D;
   QRegs<Q, KV, D, G> qr;
   qr.load(qrow, c, q_stride);
 
-  const int split_blocks = a.split_tokens / kBlockSize;
-  const int blk_begin = piece * split_blocks;
+  // Lengths beyond the table are clamped so that no access leaves the
+  // buffers (the result of such a call is unspecified).
+  const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
+  const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
+  if (piece >= n_pieces) return;
+  PA_STAMP(1);
+
   const int blk_end = min(cdiv(L, kBlockSize), blk_begin + split_blocks);
-  const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
   const size_t head_blocks = size_t(g) * a.num_blocks;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
@@ -224,11 +288,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1(DecodeArgs a) {
     if constexpr (kInt8) corr[h] = 0.0f;
   }
 
+  // Out-of-range table entries are clamped into the pool (unspecified
+  // result, but no access outside the cache).
   const int lane_off = lane * 16;
   auto fetch = [&](int blk, u32x4 (&kt)[LPB], u32x4 (&vt)[LPB], float& ks, float& vs) {
-    // Out-of-range table entries are clamped into the pool (unspecified
-    // result, but no access outside the cache).
-    const int phys = min(max(readfirstlane(bt[blk]), 0), a.num_blocks - 1);
+    const int phys = min(max(__builtin_amdgcn_readlane(tab, blk - blk_begin), 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * GE::TILE_BYTES;
 #pragma unroll
     for (int i = 0; i < LPB; ++i) kt[i] = load16_stream(kbase + tile + i * 1024 + lane_off);
@@ -314,29 +378,37 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1(DecodeArgs a) {
     }
   };
 
-  // Each wave takes every NW-th tile of the piece; the next tile's loads are
-  // in flight while the current one is reduced.
-  int blk = blk_begin + wave;
-  if (blk < blk_end) {
-    u32x4 kc[LPB], vc[LPB];
-    float ksc, vsc;
-    fetch(blk, kc, vc, ksc, vsc);
-    while (true) {
-      const int nxt = blk + NW;
-      u32x4 kn[LPB], vn[LPB];
-      float ksn = 1.0f, vsn = 1.0f;
-      if (nxt < blk_end) fetch(nxt, kn, vn, ksn, vsn);
-      process(blk, kc, vc, ksc, vsc);
-      if (nxt >= blk_end) break;
+  // Each wave takes every NW-th tile of the piece.  Tiles go through a ring
+  // of DEPTH + 1 register buffers: while tile j is reduced, tiles j+1 ..
+  // j+DEPTH are in flight.  The loop is unrolled over the ring so every
+  // buffer index is a compile-time constant (the buffers stay in VGPRs).
+  // Fetches are issued unconditionally -- past the wave's last tile they
+  // re-read that tile (in bounds, served by the cache) -- so every path
+  // through the loop has the same number of loads outstanding and each wait
+  // covers exactly the tile about to be reduced.
+  const int first = blk_begin + wave;
+  const int n_my = first < blk_end ? cdiv(blk_end - first, NW) : 0;
+  if (n_my > 0) {
+    const int last = n_my - 1;
+    u32x4 kb[DEPTH + 1][LPB], vb[DEPTH + 1][LPB];
+    float ksb[DEPTH + 1], vsb[DEPTH + 1];
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        kc[i] = kn[i];
-        vc[i] = vn[i];
+    for (int u = 0; u < DEPTH; ++u) fetch(first + min(u, last) * NW, kb[u], vb[u], ksb[u], vsb[u]);
+    int j = 0;
+    // Full turns of the ring: tiles j .. j+DEPTH all exist.  The only exit is
+    // the loop test, so the loop head always sees DEPTH tiles in flight.
+    for (; j + DEPTH <= last; j += DEPTH + 1) {
+#pragma unroll
+      for (int u = 0; u <= DEPTH; ++u) {
+        const int nb = (u + DEPTH) % (DEPTH + 1);  // constant once unrolled
+        fetch(first + min(j + u + DEPTH, last) * NW, kb[nb], vb[nb], ksb[nb], vsb[nb]);
+        process(first + (j + u) * NW, kb[u], vb[u], ksb[u], vsb[u]);
       }
-      ksc = ksn;
-      vsc = vsn;
-      blk = nxt;
     }
+    // At most DEPTH tiles remain; they are already in flight in kb[0 ..].
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+      if (j + u <= last) process(first + (j + u) * NW, kb[u], vb[u], ksb[u], vsb[u]);
   }
 
   if constexpr (kInt8) {
@@ -346,25 +418,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1(DecodeArgs a) {
       for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(-128.0f, corr[h], acc[h][e]);
   }
 
+  PA_STAMP(2);
   // Merge the key rows of this wave (lanes c, c + LPK, c + 2 LPK, ...).
+  if constexpr (LPK < kWave) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mw = m[h];
+    for (int h = 0; h < G; ++h) {
+      const float mw = stride_max<LPK>(m[h]);
+      const float f = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mw);
+      l[h] = stride_sum<LPK>(l[h] * f);
 #pragma unroll
-    for (int off = LPK; off < kWave; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
-    const float f = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mw);
-    float lw = l[h] * f;
-#pragma unroll
-    for (int off = LPK; off < kWave; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float x = acc[h][e] * f;
-#pragma unroll
-      for (int off = LPK; off < kWave; off <<= 1) x += __shfl_xor(x, off);
-      acc[h][e] = x;
+      for (int e = 0; e < EPL; ++e) acc[h][e] = stride_sum<LPK>(acc[h][e] * f);
+      m[h] = mw;
     }
-    m[h] = mw;
-    l[h] = lw;
   }
 
   // Merge the waves through LDS.
@@ -382,6 +447,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1(DecodeArgs a) {
     }
   }
   __syncthreads();
+  PA_STAMP(3);
 
   const int Hq = a.q_heads;
   for (int t = threadIdx.x; t < G * D; t += NW * kWave) {
@@ -406,46 +472,25 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1(DecodeArgs a) {
       if (d == 0) a.part_lse[prow] = lsum > 0.0f ? M + __log2f(lsum) : kNegInf;
     }
   }
+  PA_STAMP(4);
+  if (n_pieces > 1)
+    merge_if_last<Q, D, G>(a.out, a.part_o, a.part_lse, a.tickets + pair, n_pieces, a.max_pieces,
+                           size_t(b) * Hq + size_t(g) * G, NW * kWave);
 }
 
-// ---------------------------------------------------------------------------
-// Pass 2: merge the pieces of each (sequence, query row).  rows_per_seq is
-// q_heads for decode and T * q_heads for verify; the piece count of a row
-// comes from its sequence's context length.
-// ---------------------------------------------------------------------------
-template <typename O, int D>
-__global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.num_rows) return;
-  const int b = row / a.rows_per_seq;
-  const int L = a.context_lens[b];
-  const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
-  if (n_pieces <= 1) return;  // pass 1 wrote this row directly
-  const int lane = threadIdx.x & 63;
-  const float* lse = a.part_lse + size_t(row) * a.max_pieces;
-  const float* po = a.part_o + size_t(row) * a.max_pieces * D;
-  float M = kNegInf;
-  for (int s = 0; s < n_pieces; ++s) M = fmaxf(M, lse[s]);
-  constexpr int PER = D / 64;
-  float o[PER] = {};
-  float wsum = 0.0f;
-  for (int s = 0; s < n_pieces; ++s) {
-    const float w = lse[s] == kNegInf ? 0.0f : fast_exp2(lse[s] - M);
-    wsum += w;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) o[j] = __builtin_fmaf(w, po[size_t(s) * D + j * 64 + lane], o[j]);
-  }
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    store_out(reinterpret_cast<O*>(a.out) + size_t(row) * D + j * 64 + lane, o[j] * inv);
-}
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 1
+#endif
 
 template <typename Q, typename KV, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
-  dim3 grid(a.max_pieces, a.kv_heads, a.num_seqs);
-  decode_pass1<Q, KV, D, G, NW><<<grid, NW * kWave, 0, stream>>>(a);
+  constexpr int NW = PA_DECODE_WAVES;      // waves per workgroup
+  constexpr int DEPTH = PA_DECODE_DEPTH;   // tiles in flight per wave beyond the one reduced
+  const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
+  decode_pass1<Q, KV, D, G, NW, DEPTH><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -476,6 +521,12 @@ hipError_t dispatch_dim(const DecodeArgs& a, int G, hipStream_t stream) {
 
 }  // namespace
 
+#ifdef PA_TIMING
+extern "C" int pa_debug_times(unsigned long long* host, int n) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_times), sizeof(unsigned long long) * n) == hipSuccess ? 0 : -1;
+}
+#endif
+
 bool decode_group_supported(int G) { return (G >= 1 && G <= 8) || G == 16; }
 
 hipError_t launch_decode_pass1(const DecodeArgs& a, hipStream_t stream) {
@@ -484,18 +535,6 @@ hipError_t launch_decode_pass1(const DecodeArgs& a, hipStream_t stream) {
   if (a.q_dtype == kBF16 && a.kv_dtype == kBF16) return dispatch_dim<bf16_t, bf16_t>(a, G, stream);
   if (a.q_dtype == kBF16 && a.kv_dtype == kI8) return dispatch_dim<bf16_t, i8_t>(a, G, stream);
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  dim3 grid(cdiv(a.num_rows, 4));
-  if (a.out_dtype == kF32) {
-    if (a.head_dim == 64) merge_pieces<float, 64><<<grid, 256, 0, stream>>>(a);
-    else merge_pieces<float, 128><<<grid, 256, 0, stream>>>(a);
-  } else {
-    if (a.head_dim == 64) merge_pieces<bf16_t, 64><<<grid, 256, 0, stream>>>(a);
-    else merge_pieces<bf16_t, 128><<<grid, 256, 0, stream>>>(a);
-  }
-  return hipGetLastError();
 }
 
 }  // namespace pa

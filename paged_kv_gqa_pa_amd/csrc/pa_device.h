@@ -33,6 +33,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
+// Exchange across 16-lane rows without LDS: permlane16_swap of a value with
+// itself leaves row r's partner row (r ^ 1) in one of the two results, so
+// combining both results reduces over lane ^ 16; permlane32_swap likewise
+// over lane ^ 32.
+__device__ __forceinline__ float add_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Sum over groups of N consecutive lanes (N a power of two, N <= 64); every
 // lane of a group receives the group's sum.  Inside a 16-lane DPP row the
 // butterflies are quad_perm (lane ^ 1, lane ^ 2), then row_half_mirror and
@@ -44,8 +65,33 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, true);   // [2,3,0,1]
   if constexpr (N >= 8) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, true);  // row_half_mirror
   if constexpr (N >= 16) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, true); // row_mirror
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  if constexpr (N >= 32) x = add_xor16(x);
+  if constexpr (N >= 64) x = add_xor32(x);
+  return x;
+}
+
+// Reduction over the lanes that share lane % S (S a power of two < 64): every
+// lane receives the result.  Within a row, rotations by S, 2S, ... < 16 gather
+// the lanes of stride S (a rotation sum over a cyclic group covers each member
+// once); rows are then combined with the permlane swaps.
+template <int S>
+__device__ __forceinline__ float stride_sum(float x) {
+  if constexpr (S <= 1) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x121, 0xF, 0xF, true);  // row_ror:1
+  if constexpr (S <= 2) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x122, 0xF, 0xF, true);  // row_ror:2
+  if constexpr (S <= 4) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x124, 0xF, 0xF, true);  // row_ror:4
+  if constexpr (S <= 8) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x128, 0xF, 0xF, true);  // row_ror:8
+  if constexpr (S <= 16) x = add_xor16(x);
+  if constexpr (S <= 32) x = add_xor32(x);
+  return x;
+}
+template <int S>
+__device__ __forceinline__ float stride_max(float x) {
+  if constexpr (S <= 1) x = fmaxf(x, __builtin_amdgcn_update_dpp(0.0f, x, 0x121, 0xF, 0xF, true));
+  if constexpr (S <= 2) x = fmaxf(x, __builtin_amdgcn_update_dpp(0.0f, x, 0x122, 0xF, 0xF, true));
+  if constexpr (S <= 4) x = fmaxf(x, __builtin_amdgcn_update_dpp(0.0f, x, 0x124, 0xF, 0xF, true));
+  if constexpr (S <= 8) x = fmaxf(x, __builtin_amdgcn_update_dpp(0.0f, x, 0x128, 0xF, 0xF, true));
+  if constexpr (S <= 16) x = max_xor16(x);
+  if constexpr (S <= 32) x = max_xor32(x);
   return x;
 }
 

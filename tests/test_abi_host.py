@@ -46,8 +46,9 @@ def test_workspace_size():
     rows = 8 * 12
     o = rows * pieces * 128 * 4
     lse = rows * pieces * 4
+    tickets = 65536 * 4
     rnd = lambda x: (x + 255) // 256 * 256
-    assert n == rnd(o) + rnd(lse)
+    assert n == rnd(o) + rnd(lse) + rnd(tickets)
     # invalid sizes give 0
     assert lib.pa_workspace_size(8, 1, 12, 5, 128, 100, pa.PA_BF16, 0) == 0
     assert lib.pa_workspace_size(8, 1, 12, 2, 128, 100, pa.PA_BF16, 24) == 0
@@ -74,6 +75,7 @@ FAKE = 0x1000  # aligned non-null dummy address; never dereferenced on these pat
     (dict(D=96), pa.PA_ERR_UNSUPPORTED),
     (dict(bs=32), pa.PA_ERR_UNSUPPORTED),
     (dict(split=24), pa.PA_ERR_INVALID_ARG),
+    (dict(split=2048), pa.PA_ERR_INVALID_ARG),
     (dict(ML=65), pa.PA_ERR_INVALID_ARG),
     (dict(qd=pa.PA_F32, kd=pa.PA_BF16), pa.PA_ERR_UNSUPPORTED),
     (dict(qd=7), pa.PA_ERR_INVALID_ARG),

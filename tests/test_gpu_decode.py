@@ -251,3 +251,26 @@ def test_invalid_arguments_raise_before_launch():
         pa.decode(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
                   case.scale, 64 * 16 + 1)
     assert ei.value.status == pa.PA_ERR_INVALID_ARG
+
+
+def test_workspace_reuse_across_calls():
+    """Arrival counters return to zero: repeated calls on one workspace stay correct."""
+    _say("workspace reuse qwen2_1p5b_bf16 split 64/128")
+    case = wl.build_case("qwen2_1p5b_bf16")
+    dc = DevCase(case)
+    want = _oracle_decode(case)
+    need = max(pa.workspace_size(case.num_seqs, 1, 12, 2, 128, case.max_context_len,
+                                 torch.bfloat16, s) for s in (64, 128))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = None
+    for rep in range(3):
+        for split in (64, 128):
+            out = torch.full_like(dc.q, float("nan"))
+            pa.decode(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                      case.scale, case.max_context_len, split_tokens=split, workspace=ws)
+            torch.cuda.synchronize()
+            assert max_abs_err(out, want) < TOL["bf16"], (rep, split)
+            if split == 64:
+                if first is None:
+                    first = out.clone()
+                assert torch.equal(out.view(torch.int16), first.view(torch.int16))
