@@ -108,10 +108,9 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
 /*
  * Split-K over context.  A sequence's context is cut into consecutive pieces
  * of `split_tokens` positions (a multiple of block_size); each piece is
- * reduced to a partial (normalised output, log-sum-exp) pair in fp32, and the
- * last piece of a (sequence, KV head) to finish merges them in piece order:
- * with M = max_s lse_s and w_s = exp(lse_s - M),
- * out = sum_s w_s o_s / sum_s w_s.  This is the online-softmax rescaling
+ * reduced to a partial (normalised output, log-sum-exp) pair in fp32, and a
+ * second launch merges each row's pieces in piece order: with
+ * M = max_s lse_s and w_s = exp(lse_s - M), out = sum_s w_s o_s / sum_s w_s.  This is the online-softmax rescaling
  * applied across pieces instead of across tiles.  The piece length depends
  * only on the arguments given here, never on the lengths in the batch, so a
  * sequence's result does not depend on what it is batched with.
@@ -151,14 +150,10 @@ size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv
  * split_tokens  piece length, a multiple of block_size in [16, 1024], or 0
  *               for pa_default_split_tokens()
  * workspace     device scratch of at least pa_workspace_size(...) bytes,
- *               256-byte aligned (may be NULL when that size is 0).  Its
- *               first 256 KiB hold one arrival counter per (sequence, KV
- *               head); the rest holds the pieces' partial outputs.  Zero-fill
- *               it once before its first use: every completed call leaves the
- *               counters at zero again, so the same workspace then serves any
- *               later call it is large enough for.  Calls sharing one
- *               workspace must be ordered on one stream.  With more than one
- *               piece, num_seqs * kv_heads must be <= 65536.
+ *               256-byte aligned (may be NULL when that size is 0); it holds
+ *               the pieces' partial outputs.  Its contents on entry are
+ *               ignored.  Calls sharing one workspace must be ordered on one
+ *               stream.
  * Supported: head_dim 64 or 128; block_size 16; q_heads / kv_heads in 1..8
  * or 16; the dtype triples listed at the top.
  */
@@ -185,9 +180,11 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *
  * out, q        [num_seqs, num_query_tokens, q_heads, head_dim], q_dtype
  * other arguments as pa_decode.  num_query_tokens * (q_heads / kv_heads)
- * must be <= 16 (the row count of one matrix-core tile).
- * Supported dtypes: PA_BF16 / PA_BF16 and PA_F32 / PA_F32 (fp32 is rounded
- * to bf16... no: fp32 inputs take the vector path and are not rounded).
+ * must be <= 16 (the row count of one matrix-core tile), else
+ * PA_ERR_UNSUPPORTED.
+ * Supported dtypes: PA_BF16 q with a PA_BF16 cache (bf16 output); head_dim
+ * 64 or 128.  Scores and the output accumulate in fp32 on the matrix cores;
+ * the softmax weights are rounded to bf16 for the weighted sum of V.
  */
 int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,

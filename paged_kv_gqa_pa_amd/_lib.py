@@ -112,7 +112,7 @@ def default_split_tokens(q_heads: int, kv_heads: int, head_dim: int, kv_dtype: t
 def workspace_size(num_seqs: int, num_query_tokens: int, q_heads: int, kv_heads: int,
                    head_dim: int, max_context_len: int, kv_dtype: torch.dtype,
                    split_tokens: int = 0) -> int:
-    """Bytes of workspace decode/verify need; allocate it zero-filled (torch.zeros)."""
+    """Bytes of workspace decode/verify need (0 when one piece covers the context)."""
     return _load().pa_workspace_size(num_seqs, num_query_tokens, q_heads, kv_heads, head_dim,
                                      max_context_len, _DTYPE[kv_dtype], split_tokens)
 
@@ -171,7 +171,7 @@ def _attention(fn_verify: bool, out, q, k_cache, v_cache, block_tables, context_
         k_scale = v_scale = None
     need = _load().pa_workspace_size(N, T, Hq, Hkv, D, int(max_context_len), kvd, int(split_tokens))
     if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

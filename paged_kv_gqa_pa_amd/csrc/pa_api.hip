@@ -34,8 +34,7 @@ struct Plan {
   int max_pieces = 1;
   size_t o_bytes = 0;
   size_t lse_bytes = 0;
-  size_t ticket_bytes = 0;
-  size_t total() const { return max_pieces > 1 ? o_bytes + lse_bytes + ticket_bytes : 0; }
+  size_t total() const { return max_pieces > 1 ? o_bytes + lse_bytes : 0; }
 };
 
 int default_split(int q_heads, int kv_heads, int head_dim, int kv_dtype) {
@@ -74,13 +73,6 @@ int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
   const size_t rows = size_t(num_seqs) * T * q_heads;
   plan->o_bytes = round_up(rows * plan->max_pieces * head_dim * sizeof(float));
   plan->lse_bytes = round_up(rows * plan->max_pieces * sizeof(float));
-  // Arrival counters sit in a fixed region at the start of every workspace, so
-  // partial outputs of one call never overlap the counters of another call,
-  // whatever their shapes: a workspace zeroed once stays valid.
-  plan->ticket_bytes = size_t(pa::kMaxTicketPairs) * sizeof(int);
-  if (plan->max_pieces > 1 && long(num_seqs) * kv_heads > pa::kMaxTicketPairs)
-    return fail(PA_ERR_UNSUPPORTED, "num_seqs * kv_heads > %d with several pieces per sequence",
-                pa::kMaxTicketPairs);
   if (long(plan->max_pieces) * num_seqs * kv_heads > kMaxGrid)
     return fail(PA_ERR_UNSUPPORTED, "too many workgroups: pieces * num_seqs * kv_heads > %ld",
                 kMaxGrid);
@@ -162,9 +154,8 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   char* ws = static_cast<char*>(workspace);
-  a.tickets = need ? reinterpret_cast<int*>(ws) : nullptr;
-  a.part_lse = need ? reinterpret_cast<float*>(ws + plan.ticket_bytes) : nullptr;
-  a.part_o = need ? reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.lse_bytes) : nullptr;
+  a.part_lse = need ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_o = need ? reinterpret_cast<float*>(ws + plan.lse_bytes) : nullptr;
   a.num_seqs = num_seqs;
   a.num_query_tokens = T;
   a.q_heads = q_heads;
@@ -180,6 +171,22 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = is_verify ? pa::launch_verify_pass1(a, s) : pa::launch_decode_pass1(a, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pass-1 launch failed: %s", hipGetErrorString(e));
+  if (plan.max_pieces > 1) {
+    pa::MergeArgs m{};
+    m.out = out;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.context_lens = context_lens;
+    m.rows_per_seq = T * q_heads;
+    m.num_rows = num_seqs * m.rows_per_seq;
+    m.max_pieces = plan.max_pieces;
+    m.split_tokens = plan.split_tokens;
+    m.max_len_clamp = max_blocks_per_seq * block_size;
+    m.head_dim = head_dim;
+    m.out_dtype = q_dtype;
+    e = pa::launch_merge(m, s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
   return PA_OK;
 }
 

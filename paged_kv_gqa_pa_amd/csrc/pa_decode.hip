@@ -17,9 +17,11 @@
 // once at the end.
 //
 // With a single piece the workgroup writes the output row directly.  With
-// several pieces each workgroup writes a normalised partial output and its
-// log2-sum-exp to the workspace, and the last workgroup of a (sequence, KV
-// head) to finish merges them (no second launch).
+// several pieces it writes a normalised partial output and its log2-sum-exp
+// to the workspace, and a merge pass combines the pieces of each row.  (A
+// merge inside this kernel by the last workgroup to arrive needs agent-scope
+// fences, which write back and invalidate the XCD's L2 and cost far more than
+// the second launch.)
 // Piece length is fixed per call (never derived from the lengths in the
 // batch), so each sequence's arithmetic depends on its own length only.
 #include "pa_device.h"
@@ -181,48 +183,6 @@ template <typename T> __device__ __forceinline__ void store_out(T* p, float v);
 template <> __device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v) {
   p->bits = f32_to_bf16(v);
-}
-
-// ---------------------------------------------------------------------------
-// Merge of pieces inside the attention kernel.  Every workgroup of a
-// multi-piece (sequence, KV head) stores its partials, then takes a ticket;
-// the one that draws the last ticket merges all pieces in piece order (so the
-// result does not depend on arrival order) and resets the ticket to zero for
-// the next call.  The agent-scope fences order the partial stores before the
-// ticket and the ticket before the merging workgroup's reads, across XCDs.
-// ---------------------------------------------------------------------------
-template <typename O, int D, int R>
-__device__ __forceinline__ void merge_if_last(void* out, const float* part_o,
-                                              const float* part_lse, int* ticket, int n_pieces,
-                                              int max_pieces, size_t row0, int nthreads) {
-  __shared__ int s_last;
-  // The barrier orders every thread's partial stores before thread 0's
-  // agent-scope release; one fence per workgroup (an L2 write-back) instead of
-  // one per wave.
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    s_last = atomicAdd(ticket, 1) == n_pieces - 1;
-    if (s_last) __threadfence();  // acquire: the other pieces' partials
-  }
-  __syncthreads();
-  if (!s_last) return;
-  for (int t = threadIdx.x; t < R * D; t += nthreads) {
-    const int r = t / D, d = t % D;
-    const size_t prow = (row0 + r) * max_pieces;
-    const float* lse = part_lse + prow;
-    float M = kNegInf;
-    for (int s = 0; s < n_pieces; ++s) M = fmaxf(M, __builtin_nontemporal_load(lse + s));
-    float wsum = 0.0f, o = 0.0f;
-    for (int s = 0; s < n_pieces; ++s) {
-      const float ls = __builtin_nontemporal_load(lse + s);
-      const float w = ls == kNegInf ? 0.0f : fast_exp2(ls - M);
-      wsum += w;
-      o = __builtin_fmaf(w, __builtin_nontemporal_load(part_o + (prow + s) * D + d), o);
-    }
-    store_out(reinterpret_cast<O*>(out) + (row0 + r) * D + d, wsum > 0.0f ? o / wsum : 0.0f);
-  }
-  if (threadIdx.x == 0) *ticket = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -473,9 +433,44 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     }
   }
   PA_STAMP(4);
-  if (n_pieces > 1)
-    merge_if_last<Q, D, G>(a.out, a.part_o, a.part_lse, a.tickets + pair, n_pieces, a.max_pieces,
-                           size_t(b) * Hq + size_t(g) * G, NW * kWave);
+}
+
+// ---------------------------------------------------------------------------
+// Merge pass (only launched when a call has more than one piece): one wave per
+// output row merges that row's pieces in piece order with the log2-sum-exp
+// weights.  Rows of single-piece sequences were written by pass 1.
+// rows_per_seq is q_heads for decode and T * q_heads for verify.
+// ---------------------------------------------------------------------------
+template <typename O, int D>
+__global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.num_rows) return;
+  const int b = row / a.rows_per_seq;
+  const int L = min(a.context_lens[b], a.max_len_clamp);
+  const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
+  if (n_pieces <= 1) return;
+  const int lane = threadIdx.x & 63;
+  const float* lse = a.part_lse + size_t(row) * a.max_pieces;
+  const float* po = a.part_o + size_t(row) * a.max_pieces * D;
+  // Each lane reads some of the row's log2-sum-exps; the maximum and the
+  // weights are shared through wave reductions.
+  float M = kNegInf;
+  for (int s = lane; s < n_pieces; s += 64) M = fmaxf(M, lse[s]);
+  M = stride_max<1>(M);
+  constexpr int PER = D / 64;
+  float o[PER] = {};
+  float wsum = 0.0f;
+  for (int s = 0; s < n_pieces; ++s) {
+    const float ls = lse[s];
+    const float w = ls == kNegInf ? 0.0f : fast_exp2(ls - M);
+    wsum += w;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) o[j] = __builtin_fmaf(w, po[size_t(s) * D + j * 64 + lane], o[j]);
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    store_out(reinterpret_cast<O*>(a.out) + size_t(row) * D + j * 64 + lane, o[j] * inv);
 }
 
 #ifndef PA_DECODE_WAVES
@@ -528,6 +523,18 @@ extern "C" int pa_debug_times(unsigned long long* host, int n) {
 #endif
 
 bool decode_group_supported(int G) { return (G >= 1 && G <= 8) || G == 16; }
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+  dim3 grid(cdiv(a.num_rows, 4));
+  if (a.out_dtype == kF32) {
+    if (a.head_dim == 64) merge_pieces<float, 64><<<grid, 256, 0, stream>>>(a);
+    else merge_pieces<float, 128><<<grid, 256, 0, stream>>>(a);
+  } else {
+    if (a.head_dim == 64) merge_pieces<bf16_t, 64><<<grid, 256, 0, stream>>>(a);
+    else merge_pieces<bf16_t, 128><<<grid, 256, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_pass1(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.q_heads / a.kv_heads;

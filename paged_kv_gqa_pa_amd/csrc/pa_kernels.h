@@ -10,7 +10,6 @@ enum DType : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
 
 constexpr int kBlockSizeHost = 16;  // tokens per cache block
 constexpr int kMaxSplitTokens = 1024;  // a piece's table entries fit one wave (64 lanes)
-constexpr int kMaxTicketPairs = 65536;  // arrival counters reserved at the start of a workspace
 
 struct CacheArgs {
   const void* key;
@@ -35,7 +34,6 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* part_o;    // [rows, max_pieces, head_dim]  (rows = num_seqs * T * q_heads)
   float* part_lse;  // [rows, max_pieces], log2 domain
-  int* tickets;     // [num_seqs * kv_heads], zero between calls
   int num_seqs;
   int num_query_tokens;  // T (1 for decode)
   int q_heads;
@@ -51,6 +49,21 @@ struct DecodeArgs {
 };
 
 
+struct MergeArgs {
+  void* out;
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* context_lens;
+  int num_rows;
+  int rows_per_seq;
+  int max_pieces;
+  int split_tokens;
+  int max_len_clamp;  // max_blocks_per_seq * block_size
+  int head_dim;
+  int out_dtype;
+};
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheArgs& a, hipStream_t stream);
 hipError_t launch_decode_pass1(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_verify_pass1(const DecodeArgs& a, hipStream_t stream);

@@ -36,11 +36,12 @@ class DevCase:
         self.v_cache = dev(case.v_cache)
         self.block_tables = dev(case.block_tables)
         self.context_lens = dev(case.context_lens)
-        self.k_scale = None if case.k_scale is None else dev(case.k_scale)
-        self.v_scale = None if case.v_scale is None else dev(case.v_scale)
-        self.new_k = dev(case.new_k)
-        self.new_v = dev(case.new_v)
-        self.slot_mapping = dev(case.slot_mapping)
+        opt = lambda a: None if a is None else dev(a)
+        self.k_scale = opt(case.k_scale)
+        self.v_scale = opt(case.v_scale)
+        self.new_k = opt(case.new_k)
+        self.new_v = opt(case.new_v)
+        self.slot_mapping = opt(case.slot_mapping)
 
 
 def max_abs_err(gpu: torch.Tensor, want: np.ndarray) -> float:

@@ -46,9 +46,8 @@ def test_workspace_size():
     rows = 8 * 12
     o = rows * pieces * 128 * 4
     lse = rows * pieces * 4
-    tickets = 65536 * 4
     rnd = lambda x: (x + 255) // 256 * 256
-    assert n == rnd(o) + rnd(lse) + rnd(tickets)
+    assert n == rnd(o) + rnd(lse)
     # invalid sizes give 0
     assert lib.pa_workspace_size(8, 1, 12, 5, 128, 100, pa.PA_BF16, 0) == 0
     assert lib.pa_workspace_size(8, 1, 12, 2, 128, 100, pa.PA_BF16, 24) == 0

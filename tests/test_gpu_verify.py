@@ -1,0 +1,125 @@
+"""GPU parity of pa_verify (k+1 speculative tokens, causal among themselves)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_gqa_pa_amd import _lib as pa
+from paged_kv_gqa_pa_amd import workloads as wl
+from tests.gpu_util import TOL, DevCase, host_bits, max_abs_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _verify(dc, split=0, max_len=None):
+    case = dc.case
+    out = torch.empty_like(dc.q)
+    pa.verify(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, case.scale,
+              case.max_context_len if max_len is None else max_len, split_tokens=split)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_verify(case):
+    return oracle.verify(case.q, case.k_cache, case.v_cache, case.block_tables,
+                         case.context_lens, case.scale, case.spec.q_dtype, case.spec.kv_dtype)
+
+
+@pytest.mark.parametrize("split", [0, 256])
+def test_spec_verify_full_size(split):
+    """64 sequences, 5 new tokens each written first, then verified."""
+    _say("spec_verify_bf16 split", split)
+    case = wl.build_case("spec_verify_bf16", poison=True)
+    dc = DevCase(case)
+    pa.reshape_and_cache(dc.new_k, dc.new_v, dc.k_cache, dc.v_cache, dc.slot_mapping)
+    torch.cuda.synchronize()
+    want_k, want_v = oracle.reshape_and_cache(case.new_k, case.new_v, case.k_cache,
+                                              case.v_cache, case.slot_mapping)
+    assert host_bits(dc.k_cache).tobytes() == want_k.tobytes()
+    case.k_cache, case.v_cache = want_k, want_v
+    out = _verify(dc, split)
+    err = max_abs_err(out, _oracle_verify(case))
+    assert err < TOL["bf16"], err
+
+
+def _random_verify_case(rng, lens, Hkv, G, D, T, poison=False):
+    lens = np.asarray(lens, np.int32)
+    maxb = max(1, -(-int(lens.max()) // 16))
+    need = int(sum(-(-int(L) // 16) for L in lens))
+    nb = need + 5
+    table = wl.assign_blocks(lens, rng.permutation(nb).astype(np.int32), maxb)
+    k32 = rng.standard_normal((Hkv, nb, 16, D), dtype=np.float32)
+    v32 = rng.standard_normal((Hkv, nb, 16, D), dtype=np.float32)
+    if poison:
+        used = np.unique(table[table >= 0])
+        spare = np.setdiff1d(np.arange(nb), used)
+        k32[:, spare] = np.nan
+        v32[:, spare] = np.nan
+        for b, L in enumerate(lens):
+            if L % 16:
+                phys = table[b, (int(L) - 1) // 16]
+                k32[:, phys, L % 16:] = np.nan
+                v32[:, phys, L % 16:] = np.nan
+    q = wl.f32_to_bf16_bits(rng.standard_normal((len(lens), T, Hkv * G, D), dtype=np.float32))
+    spec = wl.Spec("random_verify", 0, len(lens), Hkv * G, Hkv, D, nb, "bf16", "bf16",
+                   max(16, int(lens.max())), num_query_tokens=T)
+    return wl.PagedCase(spec=spec, layer=0, context_lens=lens, block_tables=table, q=q,
+                        k_cache=wl.f32_to_bf16_bits(k32), v_cache=wl.f32_to_bf16_bits(v32),
+                        k_scale=None, v_scale=None, new_k=None, new_v=None,
+                        slot_mapping=None, scale=1.0 / np.sqrt(D))
+
+
+EDGE = [0, 1, 2, 3, 4, 5, 6, 15, 16, 17, 21, 33, 100, 255, 256, 257, 700]
+
+
+@pytest.mark.parametrize("G,T", [(1, 1), (1, 16), (2, 5), (3, 5), (2, 8), (8, 2), (16, 1), (6, 2)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_verify_edges(G, T, D):
+    _say("verify edges G", G, "T", T, "D", D)
+    rng = np.random.default_rng(1000 + 10 * G + T + D)
+    case = _random_verify_case(rng, EDGE, Hkv=2, G=G, D=D, T=T, poison=True)
+    dc = DevCase(case)
+    want = _oracle_verify(case)
+    for split in (0, 32):
+        out = _verify(dc, split)
+        err = max_abs_err(out, want)
+        assert err < TOL["bf16"], (split, err)
+    got = out.float().cpu().numpy()
+    # a row with no visible position (context shorter than the tokens before it) is zero
+    for b, L in enumerate(case.context_lens):
+        for t in range(T):
+            if L - T + t < 0:
+                assert (got[b, t] == 0).all()
+
+
+def test_verify_rows_match_decode_at_shorter_contexts():
+    """Row t of verify is decode with context L - T + t + 1 and that token's query."""
+    _say("verify vs decode rows")
+    rng = np.random.default_rng(7)
+    T = 5
+    case = _random_verify_case(rng, [40, 300, 517], Hkv=2, G=2, D=128, T=T)
+    dc = DevCase(case)
+    out = _verify(dc).float().cpu().numpy()
+    for t in range(T):
+        lens_t = (case.context_lens - T + t + 1).astype(np.int32)
+        want = oracle.decode(np.ascontiguousarray(case.q[:, t]), case.k_cache, case.v_cache,
+                             case.block_tables, lens_t, case.scale, "bf16", "bf16")
+        dec = torch.empty_like(dc.q[:, t])
+        pa.decode(dec, dc.q[:, t].contiguous(), dc.k_cache, dc.v_cache, dc.block_tables,
+                  torch.from_numpy(lens_t).cuda(), case.scale, case.max_context_len)
+        torch.cuda.synchronize()
+        assert np.abs(out[:, t] - want).max() < TOL["bf16"]
+        assert max_abs_err(dec, want) < TOL["bf16"]
+
+
+def test_verify_unsupported_shapes_rejected():
+    rng = np.random.default_rng(3)
+    case = _random_verify_case(rng, [20], Hkv=1, G=4, D=128, T=5)   # 20 rows > 16
+    dc = DevCase(case)
+    with pytest.raises(pa.PAError) as ei:
+        _verify(dc)
+    assert ei.value.status == pa.PA_ERR_UNSUPPORTED
