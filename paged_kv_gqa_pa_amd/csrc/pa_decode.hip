@@ -251,13 +251,19 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // Out-of-range table entries are clamped into the pool (unspecified
   // result, but no access outside the cache).
   const int lane_off = lane * 16;
-  auto fetch = [&](int blk, u32x4 (&kt)[LPB], u32x4 (&vt)[LPB], float& ks, float& vs) {
+  // A fetch with live == false (past the wave's last tile) keeps the
+  // instruction stream, and so the wait counts, identical but reads nothing:
+  // its buffer resource has zero records.
+  auto fetch = [&](int blk, bool live, u32x4 (&kt)[LPB], u32x4 (&vt)[LPB], float& ks, float& vs) {
     const int phys = min(max(__builtin_amdgcn_readlane(tab, blk - blk_begin), 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * GE::TILE_BYTES;
+    const int bytes = live ? GE::TILE_BYTES : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + tile, bytes);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) kt[i] = load16_stream(kbase + tile + i * 1024 + lane_off);
+    for (int i = 0; i < LPB; ++i) kt[i] = buffer_load16_stream(kr, i * 1024 + lane_off);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) vt[i] = load16_stream(vbase + tile + i * 1024 + lane_off);
+    for (int i = 0; i < LPB; ++i) vt[i] = buffer_load16_stream(vr, i * 1024 + lane_off);
     if constexpr (kInt8) {
       ks = a.k_scale[head_blocks + phys];
       vs = a.v_scale[head_blocks + phys];
@@ -342,10 +348,10 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // of DEPTH + 1 register buffers: while tile j is reduced, tiles j+1 ..
   // j+DEPTH are in flight.  The loop is unrolled over the ring so every
   // buffer index is a compile-time constant (the buffers stay in VGPRs).
-  // Fetches are issued unconditionally -- past the wave's last tile they
-  // re-read that tile (in bounds, served by the cache) -- so every path
-  // through the loop has the same number of loads outstanding and each wait
-  // covers exactly the tile about to be reduced.
+  // Fetches are issued unconditionally -- past the wave's last tile they read
+  // nothing (see fetch) -- so every path through the loop has the same number
+  // of loads outstanding and each wait covers exactly the tile about to be
+  // reduced.
   const int first = blk_begin + wave;
   const int n_my = first < blk_end ? cdiv(blk_end - first, NW) : 0;
   if (n_my > 0) {
@@ -353,7 +359,8 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     u32x4 kb[DEPTH + 1][LPB], vb[DEPTH + 1][LPB];
     float ksb[DEPTH + 1], vsb[DEPTH + 1];
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u) fetch(first + min(u, last) * NW, kb[u], vb[u], ksb[u], vsb[u]);
+    for (int u = 0; u < DEPTH; ++u)
+      fetch(first + min(u, last) * NW, u <= last, kb[u], vb[u], ksb[u], vsb[u]);
     int j = 0;
     // Full turns of the ring: tiles j .. j+DEPTH all exist.  The only exit is
     // the loop test, so the loop head always sees DEPTH tiles in flight.
@@ -361,7 +368,8 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
       for (int u = 0; u <= DEPTH; ++u) {
         const int nb = (u + DEPTH) % (DEPTH + 1);  // constant once unrolled
-        fetch(first + min(j + u + DEPTH, last) * NW, kb[nb], vb[nb], ksb[nb], vsb[nb]);
+        fetch(first + min(j + u + DEPTH, last) * NW, j + u + DEPTH <= last, kb[nb], vb[nb],
+              ksb[nb], vsb[nb]);
         process(first + (j + u) * NW, kb[u], vb[u], ksb[u], vsb[u]);
       }
     }

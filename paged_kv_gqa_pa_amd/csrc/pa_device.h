@@ -109,4 +109,14 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Buffer resource over [base, base + bytes): loads at offsets past `bytes`
+// return zeros without a memory access (raw buffer, gfx9-family format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// 16-byte buffer load, non-temporal (the data is read once).
+__device__ __forceinline__ u32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, int offset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 2));
+}
+
 }  // namespace pa
