@@ -24,6 +24,8 @@
 // the second launch.)
 // Piece length is fixed per call (never derived from the lengths in the
 // batch), so each sequence's arithmetic depends on its own length only.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -42,14 +44,29 @@ __device__ __forceinline__ float ubyte_f32(uint32_t x) {
   return float((x >> (8 * k)) & 0xFFu);
 }
 
-template <typename KV, int D>
+// Lane layout of a 16-token tile.  A lane holds PPL 16-byte pieces of one key
+// row (E = PPL * EPL elements): piece p covers dims p*D/PPL + c*EPL .. +EPL,
+// with c = lane % LPK.  LPK lanes share a key row, a wave-wide load covers KPL
+// rows, and load i reads piece i % PPL of key rows (i / PPL) * KPL + lane / LPK.
+// Every load still covers whole 64-byte spans of each row it touches.
+template <typename KV, int D, int G>
 struct Geo {
-  static constexpr int EPL = 16 / int(sizeof(KV));  // elements per lane per 16-byte load
-  static constexpr int LPK = D / EPL;               // lanes per key row
-  static constexpr int KPL = kWave / LPK;           // key rows per wave-wide load
-  static constexpr int LPB = kBlockSize / KPL;      // wave-wide loads per 16-token tile
-  static constexpr int TILE_BYTES = kBlockSize * D * int(sizeof(KV));
-  static_assert(LPK >= 1 && LPK <= kWave && kBlockSize % KPL == 0, "unsupported geometry");
+  static constexpr int EPL = 16 / int(sizeof(KV));   // elements per 16-byte piece
+  // Two pieces per lane halve the reduction steps per score but double the
+  // per-lane accumulator; worth it for small groups only.
+  static constexpr int PPL = (__is_same(KV, bf16_t) && G <= 4) ? 2 : 1;  // pieces per lane
+  static constexpr int E = PPL * EPL;                 // elements per lane per key row
+  static constexpr int LPK = D / E;                   // lanes per key row
+  static constexpr int KPL = kWave / LPK;             // key rows per wave-wide load
+  static constexpr int ROWB = D * int(sizeof(KV));    // bytes per key row
+  static constexpr int LPB = kBlockSize * ROWB / 1024;  // wave-wide loads per tile
+  static constexpr int KR = LPB / PPL;                // key rows per lane per tile
+  static constexpr int TILE_BYTES = kBlockSize * ROWB;
+  static_assert(LPK >= 1 && LPK <= kWave && KR * KPL == kBlockSize, "unsupported geometry");
+  // Byte offset of load i for this lane (r = lane / LPK, c = lane % LPK).
+  __device__ static int offset(int i, int r, int c) {
+    return (i / PPL) * (KPL * ROWB) + r * ROWB + (i % PPL) * (ROWB / PPL) + c * 16;
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -59,46 +76,51 @@ template <typename Q, typename KV, int D, int G> struct QRegs;
 
 // fp32 q, fp32 cache.
 template <int D, int G> struct QRegs<float, float, D, G> {
-  static constexpr int EPL = Geo<float, D>::EPL;
-  float q[G][EPL];
-  __device__ void load(const float* qrow, int c, int q_stride) {
+  float q[G][4];
+  __device__ void load(const float* qrow, int c) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      u32x4 w = load16(qrow + size_t(h) * q_stride + c * EPL);
+      u32x4 w = load16(qrow + size_t(h) * D + c * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) q[h][e] = __uint_as_float(w[e]);
     }
   }
-  __device__ float dot(int h, u32x4 k) const {
-    float s = q[h][0] * __uint_as_float(k[0]);
+  __device__ float dot_row(int h, const u32x4* k) const {
+    float s = q[h][0] * __uint_as_float(k[0][0]);
 #pragma unroll
-    for (int e = 1; e < 4; ++e) s = __builtin_fmaf(q[h][e], __uint_as_float(k[e]), s);
+    for (int e = 1; e < 4; ++e) s = __builtin_fmaf(q[h][e], __uint_as_float(k[0][e]), s);
     return s;
   }
 };
 
-// bf16 q, bf16 cache: packed bf16 dot products into fp32.
+// bf16 q, bf16 cache: packed bf16 dot products into fp32, PPL 16-byte pieces
+// per lane.
 template <int D, int G> struct QRegs<bf16_t, bf16_t, D, G> {
-  uint32_t q[G][4];
-  __device__ void load(const bf16_t* qrow, int c, int q_stride) {
+  static constexpr int PPL = Geo<bf16_t, D, G>::PPL;
+  uint32_t q[G][PPL][4];
+  __device__ void load(const bf16_t* qrow, int c) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      u32x4 w = load16(qrow + size_t(h) * q_stride + c * 8);
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q[h][e] = w[e];
-    }
+      for (int p = 0; p < PPL; ++p) {
+        u32x4 w = load16(qrow + size_t(h) * D + p * (D / PPL) + c * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[h][p][e] = w[e];
+      }
   }
-  __device__ float dot(int h, u32x4 k) const {
+  __device__ float dot_row(int h, const u32x4* k) const {
     float s = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // Copy the element out first: a bit cast applied directly to an element
-      // of a vector value reads element 0 with this compiler.
-      const uint32_t kw = k[e];
-      const uint32_t qw = q[h][e];
-      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw),
-                                          __builtin_bit_cast(bf16x2, kw), s, false);
-    }
+    for (int p = 0; p < PPL; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // Copy the element out first: a bit cast applied directly to an
+        // element of a vector value reads element 0 with this compiler.
+        const uint32_t kw = k[p][e];
+        const uint32_t qw = q[h][p][e];
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw),
+                                            __builtin_bit_cast(bf16x2, kw), s, false);
+      }
     return s;
   }
 };
@@ -109,10 +131,10 @@ template <int D, int G> struct QRegs<bf16_t, bf16_t, D, G> {
 template <int D, int G> struct QRegs<bf16_t, i8_t, D, G> {
   float q[G][16];
   float qsum[G];
-  __device__ void load(const bf16_t* qrow, int c, int q_stride) {
+  __device__ void load(const bf16_t* qrow, int c) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const bf16_t* p = qrow + size_t(h) * q_stride + c * 16;
+      const bf16_t* p = qrow + size_t(h) * D + c * 16;
       u32x4 w0 = load16(p);
       u32x4 w1 = load16(p + 8);
       float s = 0.0f;
@@ -190,10 +212,11 @@ template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v
 // ---------------------------------------------------------------------------
 // With 8 waves per workgroup, keep two workgroups per CU (4 waves per SIMD,
 // at most 128 VGPRs); with 4 the register budget is left to the compiler.
-template <typename Q, typename KV, int D, int G, int NW, int DEPTH>
+template <typename Q, typename KV, int D, int G, int NW>
 __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode_pass1(DecodeArgs a) {
-  using GE = Geo<KV, D>;
-  constexpr int EPL = GE::EPL, LPK = GE::LPK, KPL = GE::KPL, LPB = GE::LPB;
+  using GE = Geo<KV, D, G>;
+  constexpr int EPL = GE::EPL, PPL = GE::PPL, E = GE::E, LPK = GE::LPK, KPL = GE::KPL;
+  constexpr int LPB = GE::LPB, KR = GE::KR;
   constexpr bool kInt8 = __is_same(KV, i8_t);
 
   // 1-D grid, piece-major: ids 0 .. N*Hkv-1 are piece 0 of every (sequence,
@@ -209,7 +232,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPK;   // key row inside a load
-  const int c = lane % LPK;   // 16-byte column of the key row
+  const int c = lane % LPK;   // which 16-byte column of each piece
   const int split_blocks = a.split_tokens / kBlockSize;
   const int blk_begin = piece * split_blocks;
 
@@ -219,10 +242,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // read with readlane) and this group's query rows.
   const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
   const int tab = blk_begin + lane < a.max_blocks_per_seq ? bt[blk_begin + lane] : 0;
-  const int q_stride = a.head_dim;  // elements between consecutive heads
   const Q* qrow = reinterpret_cast<const Q*>(a.q) + (size_t(b) * a.q_heads + size_t(g) * G) * D;
   QRegs<Q, KV, D, G> qr;
-  qr.load(qrow, c, q_stride);
+  qr.load(qrow, c);
 
   // Lengths beyond the table are clamped so that no access leaves the
   // buffers (the result of such a call is unspecified).
@@ -237,20 +259,22 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
   const float sc_log2 = a.scale * kLog2e;
 
-  float m[G], l[G], acc[G][EPL];
+  float m[G], l[G], acc[G][E];
   float corr[kInt8 ? G : 1];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = kNegInf;
     l[h] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
     if constexpr (kInt8) corr[h] = 0.0f;
   }
 
   // Out-of-range table entries are clamped into the pool (unspecified
   // result, but no access outside the cache).
-  const int lane_off = lane * 16;
+  int lane_off[LPB];
+#pragma unroll
+  for (int i = 0; i < LPB; ++i) lane_off[i] = GE::offset(i, r, c);
   // A fetch with live == false (past the wave's last tile) keeps the
   // instruction stream, and so the wait counts, identical but reads nothing:
   // its buffer resource has zero records.
@@ -261,9 +285,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + tile, bytes);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) kt[i] = buffer_load16_stream(kr, i * 1024 + lane_off);
+    for (int i = 0; i < LPB; ++i) kt[i] = buffer_load16_stream(kr, lane_off[i]);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) vt[i] = buffer_load16_stream(vr, i * 1024 + lane_off);
+    for (int i = 0; i < LPB; ++i) vt[i] = buffer_load16_stream(vr, lane_off[i]);
     if constexpr (kInt8) {
       ks = a.k_scale[head_blocks + phys];
       vs = a.v_scale[head_blocks + phys];
@@ -273,117 +297,153 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     }
   };
 
-  auto process = [&](int blk, u32x4 (&kt)[LPB], u32x4 (&vt)[LPB], float ks, float vs) {
-    const bool partial = (blk + 1) * kBlockSize > L;  // uniform
-    float s[G][LPB];
+  // Reduce one tile.  MASK (only for a sequence's last, partial block) drops
+  // positions >= L and zeroes their V rows: rows past the context may hold
+  // anything, even NaN, and a zero weight must meet a finite value.
+  //
+  // Delayed rescaling: m is a reference maximum, not necessarily the running
+  // one.  Weights are exp2(s - m); the accumulator is rescaled only when some
+  // score of the wave exceeds its lane's reference by more than kSlack (log2
+  // units), so weights stay below 2^kSlack in fp32 and the rescale (one
+  // multiply per accumulator element) almost never runs.  The final
+  // normalisation by the running sum makes the result independent of m.
+  constexpr float kSlack = 8.0f;
+  auto process = [&](auto mask_tag, int blk, u32x4 (&kt)[LPB], u32x4 (&vt)[LPB], float ks,
+                     float vs) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float s[G][KR];
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) {
+    for (int k = 0; k < KR; ++k) {
       if constexpr (kInt8) {
         float u[16];
-        QRegs<Q, KV, D, G>::widen(kt[i], u);
+        QRegs<Q, KV, D, G>::widen(kt[k], u);
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[h][i] = qr.dot_widened(h, u);
+        for (int h = 0; h < G; ++h) s[h][k] = qr.dot_widened(h, u);
       } else {
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[h][i] = qr.dot(h, kt[i]);
+        for (int h = 0; h < G; ++h) s[h][k] = qr.dot_row(h, &kt[k * PPL]);
       }
     }
     const float sc = kInt8 ? sc_log2 * ks : sc_log2;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) s[h][i] = group_sum<LPK>(s[h][i]) * sc;
-    if (partial) {
+      for (int k = 0; k < KR; ++k) s[h][k] = group_sum<LPK>(s[h][k]) * sc;
+    if constexpr (MASK) {
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        const bool valid = blk * kBlockSize + i * KPL + r < L;
+      for (int k = 0; k < KR; ++k) {
+        const bool valid = blk * kBlockSize + k * KPL + r < L;
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[h][i] = valid ? s[h][i] : kNegInf;
-        // Rows past the context may hold anything (even NaN): zero them so a
-        // zero weight really contributes nothing.
+        for (int h = 0; h < G; ++h) s[h][k] = valid ? s[h][k] : kNegInf;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) vt[i][w] = valid ? vt[i][w] : 0u;
+        for (int p = 0; p < PPL; ++p)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vt[k * PPL + p][w] = valid ? vt[k * PPL + p][w] : 0u;
       }
     }
-    float vf[LPB][EPL];
+    bool grow = false;
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) VWiden<KV>::run(vt[i], vf[i]);
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int k = 0; k < KR; ++k) grow |= s[h][k] > m[h] + kSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float smax = s[h][0];
+#pragma unroll
+        for (int k = 1; k < KR; ++k) smax = fmaxf(smax, s[h][k]);
+        const float mnew = fmaxf(m[h], smax);
+        const float alpha = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mnew);
+        m[h] = mnew;
+        l[h] *= alpha;
+        if constexpr (kInt8) corr[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+      }
+    }
+    float vf[KR][E];
+#pragma unroll
+    for (int k = 0; k < KR; ++k)
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        float tmp[EPL];
+        VWiden<KV>::run(vt[k * PPL + p], tmp);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[k][p * EPL + e] = tmp[e];
+      }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float smax = s[h][0];
-#pragma unroll
-      for (int i = 1; i < LPB; ++i) smax = fmaxf(smax, s[h][i]);
-      const float mnew = fmaxf(m[h], smax);
-      const float mref = mnew == kNegInf ? 0.0f : mnew;
-      const float alpha = fast_exp2(m[h] - mref);
-      m[h] = mnew;
-      float p[LPB];
+      // A row that has seen no position yet keeps m = -inf and weight 0.
+      const float mref = m[h] == kNegInf ? 0.0f : m[h];
+      float pw[KR];
       float psum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        p[i] = fast_exp2(s[h][i] - mref);
-        psum += p[i];
+      for (int k = 0; k < KR; ++k) {
+        pw[k] = fast_exp2(s[h][k] - mref);
+        psum += pw[k];
       }
-      l[h] = __builtin_fmaf(l[h], alpha, psum);
+      l[h] += psum;
       if constexpr (kInt8) {
         float pv_sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) {
-          p[i] *= vs;
-          pv_sum += p[i];
+        for (int k = 0; k < KR; ++k) {
+          pw[k] *= vs;
+          pv_sum += pw[k];
         }
-        corr[h] = __builtin_fmaf(corr[h], alpha, pv_sum);
+        corr[h] += pv_sum;
       }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float x = acc[h][e] * alpha;
+      for (int e = 0; e < E; ++e) {
+        float x = acc[h][e];
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) x = __builtin_fmaf(p[i], vf[i][e], x);
+        for (int k = 0; k < KR; ++k) x = __builtin_fmaf(pw[k], vf[k][e], x);
         acc[h][e] = x;
       }
     }
   };
 
-  // Each wave takes every NW-th tile of the piece.  Tiles go through a ring
-  // of DEPTH + 1 register buffers: while tile j is reduced, tiles j+1 ..
-  // j+DEPTH are in flight.  The loop is unrolled over the ring so every
-  // buffer index is a compile-time constant (the buffers stay in VGPRs).
-  // Fetches are issued unconditionally -- past the wave's last tile they read
-  // nothing (see fetch) -- so every path through the loop has the same number
-  // of loads outstanding and each wait covers exactly the tile about to be
-  // reduced.
+  // Each wave takes every NW-th tile of the piece, with the next tile's loads
+  // in flight while one is reduced (two register buffers, loop unrolled over
+  // them so buffer indices are compile-time constants).  Fetches inside the
+  // loop are unconditional -- past the wave's last tile they read nothing (see
+  // fetch) -- so every path has the same loads outstanding and each wait covers
+  // exactly the tile about to be reduced.  The sequence's partial last block is
+  // reduced after the loop with the masked body.
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
   const int first = blk_begin + wave;
   const int n_my = first < blk_end ? cdiv(blk_end - first, NW) : 0;
   if (n_my > 0) {
     const int last = n_my - 1;
-    u32x4 kb[DEPTH + 1][LPB], vb[DEPTH + 1][LPB];
-    float ksb[DEPTH + 1], vsb[DEPTH + 1];
-#pragma unroll
-    for (int u = 0; u < DEPTH; ++u)
-      fetch(first + min(u, last) * NW, u <= last, kb[u], vb[u], ksb[u], vsb[u]);
+    // The wave's last tile needs the mask if it is the context's partial block.
+    const bool last_masked = (first + last * NW + 1) * kBlockSize > L;
+    const int last_plain = last_masked ? last - 1 : last;
+    u32x4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
+    float ksa, vsa, ksb, vsb;
+    fetch(first, true, ka, va, ksa, vsa);
     int j = 0;
-    // Full turns of the ring: tiles j .. j+DEPTH all exist.  The only exit is
-    // the loop test, so the loop head always sees DEPTH tiles in flight.
-    for (; j + DEPTH <= last; j += DEPTH + 1) {
-#pragma unroll
-      for (int u = 0; u <= DEPTH; ++u) {
-        const int nb = (u + DEPTH) % (DEPTH + 1);  // constant once unrolled
-        fetch(first + min(j + u + DEPTH, last) * NW, j + u + DEPTH <= last, kb[nb], vb[nb],
-              ksb[nb], vsb[nb]);
-        process(first + (j + u) * NW, kb[u], vb[u], ksb[u], vsb[u]);
-      }
+    for (; j + 1 <= last_plain; j += 2) {
+      fetch(first + (j + 1) * NW, true, kb2, vb2, ksb, vsb);
+      process(Plain{}, first + j * NW, ka, va, ksa, vsa);
+      fetch(first + min(j + 2, last) * NW, j + 2 <= last, ka, va, ksa, vsa);
+      process(Plain{}, first + (j + 1) * NW, kb2, vb2, ksb, vsb);
     }
-    // At most DEPTH tiles remain; they are already in flight in kb[0 ..].
-#pragma unroll
-    for (int u = 0; u < DEPTH; ++u)
-      if (j + u <= last) process(first + (j + u) * NW, kb[u], vb[u], ksb[u], vsb[u]);
+    // Left: tile j (already in ka) if j <= last, and possibly tile last.
+    if (j < last) {
+      fetch(first + last * NW, true, kb2, vb2, ksb, vsb);
+      process(Plain{}, first + j * NW, ka, va, ksa, vsa);
+      process(Masked{}, first + last * NW, kb2, vb2, ksb, vsb);
+    } else if (j == last) {
+      if (last_masked) process(Masked{}, first + j * NW, ka, va, ksa, vsa);
+      else process(Plain{}, first + j * NW, ka, va, ksa, vsa);
+    }
   }
 
   if constexpr (kInt8) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(-128.0f, corr[h], acc[h][e]);
+      for (int e = 0; e < E; ++e) acc[h][e] = __builtin_fmaf(-128.0f, corr[h], acc[h][e]);
   }
 
   PA_STAMP(2);
@@ -395,7 +455,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       const float f = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mw);
       l[h] = stride_sum<LPK>(l[h] * f);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = stride_sum<LPK>(acc[h][e] * f);
+      for (int e = 0; e < E; ++e) acc[h][e] = stride_sum<LPK>(acc[h][e] * f);
       m[h] = mw;
     }
   }
@@ -407,7 +467,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][h][c * EPL + e] = acc[h][e];
+      for (int e = 0; e < E; ++e) s_acc[wave][h][(e / EPL) * (D / PPL) + c * EPL + e % EPL] = acc[h][e];
       if (c == 0) {
         s_m[wave][h] = m[h];
         s_l[wave][h] = l[h];
@@ -484,16 +544,12 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4
 #endif
-#ifndef PA_DECODE_DEPTH
-#define PA_DECODE_DEPTH 1
-#endif
 
 template <typename Q, typename KV, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;      // waves per workgroup
-  constexpr int DEPTH = PA_DECODE_DEPTH;   // tiles in flight per wave beyond the one reduced
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
-  decode_pass1<Q, KV, D, G, NW, DEPTH><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+  decode_pass1<Q, KV, D, G, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 
