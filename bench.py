@@ -157,6 +157,11 @@ def main():
             pa.decode(outs[l], qs[l], kc[l], vc[l], bt, cl, scale, max_len,
                       split_tokens=args.split, workspace=ws)
 
+    def step_fused():
+        for l in range(Lyr):
+            pa.decode_append(outs[l], qs[l], nks[l], nvs[l], kc[l], vc[l], sm, bt, cl, scale,
+                             max_len, split_tokens=args.split, workspace=ws)
+
     def decode_only():
         for l in range(Lyr):
             pa.decode(outs[l], qs[l], kc[l], vc[l], bt, cl, scale, max_len,
@@ -172,15 +177,20 @@ def main():
 
     if args.eager:
         run_step = step
+        run_fused = step_fused
         run_decode = decode_only
     else:
         g_step = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_step):
             step()
+        g_fused = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_fused):
+            step_fused()
         g_dec = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_dec):
             decode_only()
         run_step = g_step.replay
+        run_fused = g_fused.replay
         run_decode = g_dec.replay
         for _ in range(max(1, args.warmup)):
             run_step()
@@ -205,6 +215,19 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     tok_s = N / (ms_step / 1e3)
     print(f"[bench] step {ms_step * 1e3:.1f} us", flush=True)
+
+    # The same step through pa_decode_append (write + decode in one launch).
+    for _ in range(max(1, args.warmup)):
+        run_fused()
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.steps):
+        run_fused()
+    f1.record()
+    torch.cuda.synchronize()
+    ms_fused = f0.elapsed_time(f1) / args.steps
+    print(f"[bench] fused step {ms_fused * 1e3:.1f} us", flush=True)
 
     # Decode kernel alone: back-to-back launches over the 28 layers (distinct caches,
     # 2.8 GB per pass, far beyond the 256 MB last-level cache), events on the launch stream.
@@ -249,6 +272,8 @@ def main():
                    "step": "28 x (reshape_and_cache + decode)",
                    "launch": "eager" if args.eager else "hipgraph",
                    "split_tokens": args.split or pa.default_split_tokens(Hq, Hkv, D, torch.bfloat16)},
+        "fused_step": {"ms_per_step": round(ms_fused, 4), "tokens_per_s": round(N / (ms_fused / 1e3), 1),
+                       "entry_point": "pa_decode_append (cache write + decode in one launch)"},
         "hbm_gbps": round(gbps, 1),
         "pct_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,

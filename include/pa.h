@@ -165,6 +165,31 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append -- pa_reshape_and_cache of one new token per sequence
+ * followed by pa_decode, in one launch.
+ *
+ * key, value     [num_seqs, kv_heads, head_dim], kv_dtype: the new token of
+ *                each sequence, written to slot_mapping[b] (skipped when
+ *                negative) exactly as pa_reshape_and_cache writes it.
+ * The attention covers positions 0 .. context_lens[b] - 1, where position
+ * context_lens[b] - 1 is the new token: its K/V are taken from key/value
+ * directly.  The result equals pa_reshape_and_cache followed by pa_decode
+ * whenever slot_mapping[b] is the slot of position context_lens[b] - 1, which
+ * is what a decode step passes (the write-then-attend order of "Anatomy of a
+ * Decode-Step Stall", "Full Source", engine.py).  For a padding row (negative
+ * slot) nothing is written and the row's output is unspecified.
+ * Other arguments as pa_decode.  Caches: PA_F32 or PA_BF16 (an int8 cache
+ * returns PA_ERR_UNSUPPORTED).
+ */
+int pa_decode_append(void* out, const void* q, const void* key, const void* value,
+                     void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                     const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                     int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
+                     int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
+                     int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
  * pa_verify -- T = num_query_tokens new tokens per sequence (a speculative
  * verify step of k+1 tokens), causal among themselves.
  *

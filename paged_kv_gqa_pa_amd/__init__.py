@@ -4,5 +4,5 @@ The kernels live in ``libpa.so`` (HIP, gfx950) behind the C ABI declared in
 ``include/pa.h``; this package is its thin Python binding plus the seeded
 synthetic workload generators used by the tests and the benchmark.
 """
-from ._lib import (PAError, decode, default_split_tokens, reshape_and_cache, verify,  # noqa: F401
-                   version, workspace_size)
+from ._lib import (PAError, decode, decode_append, default_split_tokens,  # noqa: F401
+                   reshape_and_cache, verify, version, workspace_size)

@@ -24,7 +24,7 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0,
 PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 
 EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_default_split_tokens",
-            "pa_workspace_size", "pa_decode", "pa_verify"]
+            "pa_workspace_size", "pa_decode", "pa_decode_append", "pa_verify"]
 
 _DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_INT8}
 
@@ -60,6 +60,10 @@ def _load():
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,           # pointers
                               i, i, i, i, i, i, i, i,                   # sizes
                               f, i, i, i, vp, sz, vp]
+    lib.pa_decode_append.restype = i
+    lib.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     i, i, i, i, i, i, i, i,
+                                     f, i, i, i, vp, sz, vp]
     lib.pa_verify.restype = i
     lib.pa_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                               i, i, i, i, i, i, i, i, i,
@@ -204,3 +208,38 @@ def verify(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_cont
     """Multi-token causal verify: q/out [num_seqs, num_query_tokens, q_heads, head_dim]."""
     return _attention(True, out, q, k_cache, v_cache, block_tables, context_lens, scale,
                       max_context_len, k_scale, v_scale, split_tokens, workspace, stream)
+
+
+def decode_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
+                  scale, max_context_len, split_tokens=0, workspace=None, stream=None):
+    """Cache write of one new token per sequence plus decode, in one launch.
+
+    key/value [num_seqs, kv_heads, head_dim]; slot_mapping int64 [num_seqs].
+    """
+    _need(q, "q", ndim=3)
+    _need(out, "out", dtype=q.dtype, ndim=3)
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _need(key, "key", dtype=k_cache.dtype, ndim=3)
+    _need(value, "value", dtype=k_cache.dtype, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    Hkv, NB, BS, D = k_cache.shape
+    N, Hq, Dq = q.shape
+    if (out.shape != q.shape or Dq != D or key.shape != (N, Hkv, D) or value.shape != key.shape
+            or slot_mapping.shape[0] != N or block_tables.shape[0] != N
+            or context_lens.shape[0] != N or v_cache.shape != k_cache.shape):
+        raise ValueError("decode_append: inconsistent shapes")
+    kvd = _DTYPE[k_cache.dtype]
+    need = _load().pa_workspace_size(N, 1, Hq, Hkv, D, int(max_context_len), kvd, int(split_tokens))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_load().pa_decode_append(_ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(slot_mapping), _ptr(block_tables),
+                                    _ptr(context_lens), N, Hq, Hkv, D, BS, NB,
+                                    block_tables.shape[1], int(max_context_len), float(scale),
+                                    _DTYPE[q.dtype], kvd, int(split_tokens), _ptr(workspace),
+                                    ws_bytes, _stream(stream)))
+    return out

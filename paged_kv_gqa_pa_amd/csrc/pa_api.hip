@@ -114,13 +114,20 @@ int check_attention_args(void* out, const void* q, const void* k_cache, const vo
   return PA_OK;
 }
 
+struct Append {
+  const void* key = nullptr;
+  const void* value = nullptr;
+  const int64_t* slot_mapping = nullptr;
+  bool on = false;
+};
+
 int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
                   const void* v_cache, const float* k_scale, const float* v_scale,
                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int T,
                   int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
                   int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
                   int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  void* stream, const Append& app = Append()) {
   Plan plan;
   int st = plan_pieces(num_seqs, T, q_heads, kv_heads, head_dim, max_context_len, kv_dtype,
                        split_tokens, &plan);
@@ -137,6 +144,14 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
                   kv_dtype, head_dim, G, T);
   } else if (!pa::decode_group_supported(G)) {
     return fail(PA_ERR_UNSUPPORTED, "group size %d not built (1..8 or 16)", G);
+  }
+  if (app.on) {
+    if (kv_dtype == PA_INT8)
+      return fail(PA_ERR_UNSUPPORTED, "append into an int8 cache is not built");
+    if (num_seqs > 0 && (!app.key || !app.value || !app.slot_mapping))
+      return fail(PA_ERR_INVALID_ARG, "null key, value or slot_mapping");
+    if (!aligned(app.key, 16) || !aligned(app.value, 16) || !aligned(app.slot_mapping, 8))
+      return fail(PA_ERR_INVALID_ARG, "misaligned key, value or slot_mapping");
   }
   if (num_seqs == 0) return PA_OK;
   const size_t need = plan.total();
@@ -169,7 +184,10 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.q_dtype = q_dtype;
   a.kv_dtype = kv_dtype;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = is_verify ? pa::launch_verify_pass1(a, s) : pa::launch_decode_pass1(a, s);
+  a.new_k = app.key;
+  a.new_v = app.value;
+  a.slot_mapping = app.slot_mapping;
+  hipError_t e = is_verify ? pa::launch_verify_pass1(a, s) : pa::launch_decode_pass1(a, app.on, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pass-1 launch failed: %s", hipGetErrorString(e));
   if (plan.max_pieces > 1) {
     pa::MergeArgs m{};
@@ -213,6 +231,8 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   if (kv_dtype != PA_F32 && kv_dtype != PA_BF16)
     return fail(PA_ERR_INVALID_ARG, "unknown kv dtype %d", kv_dtype);
   if (num_tokens == 0) return PA_OK;
+  if (long(num_tokens) * kv_heads * head_dim * elem_size(kv_dtype) / 16 > kMaxGrid)
+    return fail(PA_ERR_UNSUPPORTED, "num_tokens * kv_heads * head_dim too large");
   if (!key || !value || !k_cache || !v_cache || !slot_mapping)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
@@ -248,6 +268,24 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                        context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
                        num_blocks, max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
                        split_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append(void* out, const void* q, const void* key, const void* value,
+                     void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                     const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                     int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
+                     int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
+                     int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  Append app;
+  app.key = key;
+  app.value = value;
+  app.slot_mapping = slot_mapping;
+  app.on = true;
+  return run_attention(false, out, q, k_cache, v_cache, nullptr, nullptr, block_tables,
+                       context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
+                       split_tokens, workspace, workspace_bytes, stream, app);
 }
 
 int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache,

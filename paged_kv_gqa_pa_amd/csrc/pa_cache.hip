@@ -14,20 +14,21 @@ namespace {
 
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheArgs a) {
   const int chunks = a.row_bytes / 16;
-  const long total = long(a.num_tokens) * a.kv_heads * chunks;
-  const long stride = long(gridDim.x) * blockDim.x;
-  for (long i = long(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int ch = int(i % chunks);
-    const long rest = i / chunks;
-    const int g = int(rest % a.kv_heads);
-    const long tok = rest / a.kv_heads;
-    const int64_t slot = a.slot_mapping[tok];
-    if (slot < 0 || slot >= int64_t(a.num_blocks) * kBlockSize) continue;
+  const int total = a.num_tokens * a.kv_heads * chunks;  // < 2^31, checked by the host
+  const int stride = gridDim.x * blockDim.x;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int ch = i % chunks;
+    const int rest = i / chunks;
+    const int g = rest % a.kv_heads;
+    const int tok = rest / a.kv_heads;
+    // The slot and the data are loaded together (one memory round trip).
     const size_t src = (size_t(tok) * a.kv_heads + g) * a.row_bytes + size_t(ch) * 16;
-    const size_t dst = (size_t(g) * a.num_blocks * kBlockSize + size_t(slot)) * a.row_bytes +
-                       size_t(ch) * 16;
     const u32x4 k = load16(reinterpret_cast<const char*>(a.key) + src);
     const u32x4 v = load16(reinterpret_cast<const char*>(a.value) + src);
+    const int64_t slot = a.slot_mapping[tok];
+    if (slot < 0 || slot >= int64_t(a.num_blocks) * kBlockSize) continue;
+    const size_t dst = (size_t(g) * a.num_blocks * kBlockSize + size_t(slot)) * a.row_bytes +
+                       size_t(ch) * 16;
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.k_cache) + dst) = k;
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.v_cache) + dst) = v;
   }

@@ -212,7 +212,7 @@ template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v
 // ---------------------------------------------------------------------------
 // With 8 waves per workgroup, keep two workgroups per CU (4 waves per SIMD,
 // at most 128 VGPRs); with 4 the register budget is left to the compiler.
-template <typename Q, typename KV, int D, int G, int NW>
+template <typename Q, typename KV, int D, int G, int NW, bool APPEND>
 __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode_pass1(DecodeArgs a) {
   using GE = Geo<KV, D, G>;
   constexpr int EPL = GE::EPL, PPL = GE::PPL, E = GE::E, LPK = GE::LPK, KPL = GE::KPL;
@@ -246,12 +246,42 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   QRegs<Q, KV, D, G> qr;
   qr.load(qrow, c);
 
+  // Append mode: this lane's pieces of the new token's K and V (position
+  // L - 1), and its slot.
+  u32x4 nk[PPL], nv[PPL];
+  int64_t slot = -1;
+  if constexpr (APPEND) {
+    const size_t row = (size_t(b) * a.kv_heads + g) * GE::ROWB;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      const size_t off = row + size_t(p) * (GE::ROWB / PPL) + size_t(c) * 16;
+      nk[p] = load16(reinterpret_cast<const char*>(a.new_k) + off);
+      nv[p] = load16(reinterpret_cast<const char*>(a.new_v) + off);
+    }
+    slot = a.slot_mapping[b];
+  }
+
   // Lengths beyond the table are clamped so that no access leaves the
   // buffers (the result of such a call is unspecified).
   const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
   if (piece >= n_pieces) return;
   PA_STAMP(1);
+  if constexpr (APPEND) {
+    // The last piece writes the new row into the cache (one key row: the
+    // first LPK lanes of wave 0, PPL pieces each).  Only this workgroup uses
+    // position L - 1, and it takes that row from registers, not the cache.
+    if (piece == n_pieces - 1 && wave == 0 && r == 0 && slot >= 0 &&
+        slot < int64_t(a.num_blocks) * kBlockSize) {
+      const size_t dst = (size_t(g) * a.num_blocks * kBlockSize + size_t(slot)) * GE::ROWB;
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        const size_t off = dst + size_t(p) * (GE::ROWB / PPL) + size_t(c) * 16;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + off) = nk[p];
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + off) = nv[p];
+      }
+    }
+  }
 
   const int blk_end = min(cdiv(L, kBlockSize), blk_begin + split_blocks);
   const size_t head_blocks = size_t(g) * a.num_blocks;
@@ -311,6 +341,20 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   auto process = [&](auto mask_tag, int blk, u32x4 (&kt)[LPB], u32x4 (&vt)[LPB], float ks,
                      float vs) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    if constexpr (MASK && APPEND) {
+      // Position L - 1 is the token being appended: take its row from the input.
+#pragma unroll
+      for (int k = 0; k < KR; ++k) {
+        const bool is_new = blk * kBlockSize + k * KPL + r == L - 1;
+#pragma unroll
+        for (int p = 0; p < PPL; ++p)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kt[k * PPL + p][w] = is_new ? nk[p][w] : kt[k * PPL + p][w];
+            vt[k * PPL + p][w] = is_new ? nv[p][w] : vt[k * PPL + p][w];
+          }
+      }
+    }
     float s[G][KR];
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
@@ -415,8 +459,11 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   const int n_my = first < blk_end ? cdiv(blk_end - first, NW) : 0;
   if (n_my > 0) {
     const int last = n_my - 1;
-    // The wave's last tile needs the mask if it is the context's partial block.
-    const bool last_masked = (first + last * NW + 1) * kBlockSize > L;
+    // The wave's last tile takes the masked body if it is the context's
+    // partial block, or (append mode) the block holding position L - 1.
+    const int last_blk = first + last * NW;
+    const bool last_masked = (last_blk + 1) * kBlockSize > L ||
+                             (APPEND && last_blk == cdiv(L, kBlockSize) - 1);
     const int last_plain = last_masked ? last - 1 : last;
     u32x4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
     float ksa, vsa, ksb, vsb;
@@ -546,34 +593,40 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
 #endif
 
 template <typename Q, typename KV, int D, int G>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_t(const DecodeArgs& a, bool append, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;      // waves per workgroup
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
-  decode_pass1<Q, KV, D, G, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+  if constexpr (!__is_same(KV, i8_t)) {
+    if (append) {
+      decode_pass1<Q, KV, D, G, NW, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+      return hipGetLastError();
+    }
+  }
+  decode_pass1<Q, KV, D, G, NW, false><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <typename Q, typename KV, int D>
-hipError_t dispatch_group(const DecodeArgs& a, int G, hipStream_t stream) {
+hipError_t dispatch_group(const DecodeArgs& a, int G, bool ap, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_decode_t<Q, KV, D, 1>(a, stream);
-    case 2: return launch_decode_t<Q, KV, D, 2>(a, stream);
-    case 3: return launch_decode_t<Q, KV, D, 3>(a, stream);
-    case 4: return launch_decode_t<Q, KV, D, 4>(a, stream);
-    case 5: return launch_decode_t<Q, KV, D, 5>(a, stream);
-    case 6: return launch_decode_t<Q, KV, D, 6>(a, stream);
-    case 7: return launch_decode_t<Q, KV, D, 7>(a, stream);
-    case 8: return launch_decode_t<Q, KV, D, 8>(a, stream);
-    case 16: return launch_decode_t<Q, KV, D, 16>(a, stream);
+    case 1: return launch_decode_t<Q, KV, D, 1>(a, ap, stream);
+    case 2: return launch_decode_t<Q, KV, D, 2>(a, ap, stream);
+    case 3: return launch_decode_t<Q, KV, D, 3>(a, ap, stream);
+    case 4: return launch_decode_t<Q, KV, D, 4>(a, ap, stream);
+    case 5: return launch_decode_t<Q, KV, D, 5>(a, ap, stream);
+    case 6: return launch_decode_t<Q, KV, D, 6>(a, ap, stream);
+    case 7: return launch_decode_t<Q, KV, D, 7>(a, ap, stream);
+    case 8: return launch_decode_t<Q, KV, D, 8>(a, ap, stream);
+    case 16: return launch_decode_t<Q, KV, D, 16>(a, ap, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename Q, typename KV>
-hipError_t dispatch_dim(const DecodeArgs& a, int G, hipStream_t stream) {
+hipError_t dispatch_dim(const DecodeArgs& a, int G, bool ap, hipStream_t stream) {
   switch (a.head_dim) {
-    case 64: return dispatch_group<Q, KV, 64>(a, G, stream);
-    case 128: return dispatch_group<Q, KV, 128>(a, G, stream);
+    case 64: return dispatch_group<Q, KV, 64>(a, G, ap, stream);
+    case 128: return dispatch_group<Q, KV, 128>(a, G, ap, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -600,11 +653,13 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_pass1(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_pass1(const DecodeArgs& a, bool append, hipStream_t stream) {
   const int G = a.q_heads / a.kv_heads;
-  if (a.q_dtype == kF32 && a.kv_dtype == kF32) return dispatch_dim<float, float>(a, G, stream);
-  if (a.q_dtype == kBF16 && a.kv_dtype == kBF16) return dispatch_dim<bf16_t, bf16_t>(a, G, stream);
-  if (a.q_dtype == kBF16 && a.kv_dtype == kI8) return dispatch_dim<bf16_t, i8_t>(a, G, stream);
+  if (a.q_dtype == kF32 && a.kv_dtype == kF32) return dispatch_dim<float, float>(a, G, append, stream);
+  if (a.q_dtype == kBF16 && a.kv_dtype == kBF16)
+    return dispatch_dim<bf16_t, bf16_t>(a, G, append, stream);
+  if (a.q_dtype == kBF16 && a.kv_dtype == kI8 && !append)
+    return dispatch_dim<bf16_t, i8_t>(a, G, false, stream);
   return hipErrorInvalidValue;
 }
 

@@ -34,6 +34,11 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* part_o;    // [rows, max_pieces, head_dim]  (rows = num_seqs * T * q_heads)
   float* part_lse;  // [rows, max_pieces], log2 domain
+  // Append mode only: the new token's K/V per sequence [num_seqs, kv_heads,
+  // head_dim] and its cache slot [num_seqs].
+  const void* new_k;
+  const void* new_v;
+  const int64_t* slot_mapping;
   int num_seqs;
   int num_query_tokens;  // T (1 for decode)
   int q_heads;
@@ -65,7 +70,7 @@ struct MergeArgs {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheArgs& a, hipStream_t stream);
-hipError_t launch_decode_pass1(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_pass1(const DecodeArgs& a, bool append, hipStream_t stream);
 hipError_t launch_verify_pass1(const DecodeArgs& a, hipStream_t stream);
 bool decode_group_supported(int G);
 bool verify_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T);

@@ -274,3 +274,80 @@ def test_workspace_reuse_across_calls():
                 if first is None:
                     first = out.clone()
                 assert torch.equal(out.view(torch.int16), first.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------
+# pa_decode_append: cache write of the new token + decode in one launch
+# ----------------------------------------------------------------------------
+def test_decode_append_equals_write_then_decode_bitwise():
+    """Full-size batch-64 layer: same output bits and same cache bytes as the two calls."""
+    _say("decode_append batch64 layer 3")
+    case = wl.build_case("batch64_28layer_bf16", layer=3)
+    two = DevCase(case)
+    one = DevCase(case)
+    pa.reshape_and_cache(two.new_k, two.new_v, two.k_cache, two.v_cache, two.slot_mapping)
+    ref = torch.empty_like(two.q)
+    pa.decode(ref, two.q, two.k_cache, two.v_cache, two.block_tables, two.context_lens,
+              case.scale, case.max_context_len)
+    out = torch.empty_like(one.q)
+    pa.decode_append(out, one.q, one.new_k, one.new_v, one.k_cache, one.v_cache,
+                     one.slot_mapping, one.block_tables, one.context_lens, case.scale,
+                     case.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    want_k, want_v = oracle.reshape_and_cache(case.new_k, case.new_v, case.k_cache,
+                                              case.v_cache, case.slot_mapping)
+    assert host_bits(one.k_cache).tobytes() == want_k.tobytes()
+    assert host_bits(one.v_cache).tobytes() == want_v.tobytes()
+    case.k_cache, case.v_cache = want_k, want_v
+    assert max_abs_err(out, _oracle_decode(case)) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 2, 6])
+@pytest.mark.parametrize("split", [0, 32])
+def test_decode_append_edges(tag, G, split):
+    _say("decode_append edges", tag, "G", G, "split", split)
+    rng = np.random.default_rng(300 + G + split)
+    lens = [1, 2, 15, 16, 17, 32, 33, 100, 513]
+    case = _random_case(rng, lens, Hkv=2, G=G, D=128 if tag == "bf16" else 64, tag=tag)
+    D = case.spec.head_dim
+    lens_a = np.asarray(lens, np.int64)
+    slots = wl.slots_for_positions(case.block_tables, np.arange(len(lens)), lens_a - 1)
+    new = rng.standard_normal((len(lens), 2, D), dtype=np.float32)
+    newv = rng.standard_normal((len(lens), 2, D), dtype=np.float32)
+    nk, nv = wl.encode(new, tag), wl.encode(newv, tag)
+    dc = DevCase(case)
+    out = torch.empty_like(dc.q)
+    pa.decode_append(out, dc.q, dev(nk), dev(nv), dc.k_cache, dc.v_cache, dev(slots),
+                     dc.block_tables, dc.context_lens, case.scale, case.max_context_len,
+                     split_tokens=split)
+    torch.cuda.synchronize()
+    want_k, want_v = oracle.reshape_and_cache(nk, nv, case.k_cache, case.v_cache, slots)
+    assert host_bits(dc.k_cache).tobytes() == want_k.tobytes()
+    assert host_bits(dc.v_cache).tobytes() == want_v.tobytes()
+    case.k_cache, case.v_cache = want_k, want_v
+    assert max_abs_err(out, _oracle_decode(case)) < TOL[tag]
+
+
+def test_decode_append_negative_slot_writes_nothing():
+    _say("decode_append negative slot")
+    rng = np.random.default_rng(9)
+    lens = [20, 40]
+    case = _random_case(rng, lens, Hkv=2, G=2, D=128, tag="bf16")
+    slots = wl.slots_for_positions(case.block_tables, np.arange(2), np.asarray(lens) - 1)
+    slots[0] = -1
+    nk = wl.encode(rng.standard_normal((2, 2, 128), dtype=np.float32), "bf16")
+    nv = wl.encode(rng.standard_normal((2, 2, 128), dtype=np.float32), "bf16")
+    dc = DevCase(case)
+    out = torch.empty_like(dc.q)
+    pa.decode_append(out, dc.q, dev(nk), dev(nv), dc.k_cache, dc.v_cache, dev(slots),
+                     dc.block_tables, dc.context_lens, case.scale, case.max_context_len)
+    torch.cuda.synchronize()
+    want_k, _ = oracle.reshape_and_cache(nk, nv, case.k_cache, case.v_cache, slots)
+    assert host_bits(dc.k_cache).tobytes() == want_k.tobytes()
+    case.k_cache = want_k
+    _, want_v = oracle.reshape_and_cache(nk, nv, case.k_cache, case.v_cache, slots)
+    case.v_cache = want_v
+    want = _oracle_decode(case)
+    assert np.abs(out[1].double().cpu().numpy() - want[1]).max() < TOL["bf16"]
