@@ -125,45 +125,60 @@ template <int D, int G> struct QRegs<bf16_t, bf16_t, D, G> {
   }
 };
 
-// bf16 q, int8 cache.  Codes are biased to unsigned bytes (x ^ 0x80) so the
-// hardware byte-to-float conversion applies; the bias is removed with the
-// lane's precomputed sum of q (sum q*(u-128) = sum q*u - 128 * sum q).
+// bf16 q, int8 cache.  A code c becomes the fp16 number 1024 + u with
+// u = c + 128 (the biased byte): a byte permute puts u under the constant high
+// byte 0x64, which is exact.  Two products then take one v_dot2_f32_f16, with
+// q held as fp16 pairs (bf16 values are exact in fp16 within its normal range).
+// The bias comes off with the sum of this lane's (fp16-rounded) q:
+// sum q*(1152 + c) - 1152 * sum q = sum q*c.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+constexpr uint32_t kMagic = 0x64646464u;   // fp16 high byte of 1024
+constexpr float kI8Bias = 1152.0f;         // 1024 + 128
+
+__device__ __forceinline__ uint32_t f16pair_lo(uint32_t u) {  // bytes 0,1 -> (1024+u0, 1024+u1)
+  return __builtin_amdgcn_perm(kMagic, u, 0x04010400u);
+}
+__device__ __forceinline__ uint32_t f16pair_hi(uint32_t u) {  // bytes 2,3
+  return __builtin_amdgcn_perm(kMagic, u, 0x04030402u);
+}
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                false);
+}
+
 template <int D, int G> struct QRegs<bf16_t, i8_t, D, G> {
-  float q[G][16];
-  float qsum[G];
+  uint32_t qh[G][8];  // this lane's 16 dims as fp16 pairs
+  float qsum[G];      // sum of those fp16 values
   __device__ void load(const bf16_t* qrow, int c) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const bf16_t* p = qrow + size_t(h) * D + c * 16;
-      u32x4 w0 = load16(p);
-      u32x4 w1 = load16(p + 8);
+      const u32x4 w0 = load16(p);
+      const u32x4 w1 = load16(p + 8);
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        q[h][2 * e] = bf16_lo(w0[e]);
-        q[h][2 * e + 1] = bf16_hi(w0[e]);
-        q[h][8 + 2 * e] = bf16_lo(w1[e]);
-        q[h][8 + 2 * e + 1] = bf16_hi(w1[e]);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = e < 4 ? w0[e] : w1[e - 4];
+        const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w), bf16_hi(w));
+        qh[h][e] = __builtin_bit_cast(uint32_t, hp);
+        s += float(hp[0]) + float(hp[1]);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s += q[h][e];
       qsum[h] = s;
     }
   }
-  __device__ static void widen(u32x4 k, float (&u)[16]) {
+  // The 16 codes of one 16-byte load as fp16 pairs (1024 + u).
+  __device__ static void pairs(u32x4 k, uint32_t (&kp)[8]) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t x = k[w] ^ 0x80808080u;
-      u[4 * w + 0] = ubyte_f32<0>(x);
-      u[4 * w + 1] = ubyte_f32<1>(x);
-      u[4 * w + 2] = ubyte_f32<2>(x);
-      u[4 * w + 3] = ubyte_f32<3>(x);
+      const uint32_t u = k[w] ^ 0x80808080u;
+      kp[2 * w] = f16pair_lo(u);
+      kp[2 * w + 1] = f16pair_hi(u);
     }
   }
-  __device__ float dot_widened(int h, const float (&u)[16]) const {
-    float s = -128.0f * qsum[h];
+  __device__ float dot_pairs(int h, const uint32_t (&kp)[8]) const {
+    float s = -kI8Bias * qsum[h];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s = __builtin_fmaf(q[h][e], u[e], s);
+    for (int e = 0; e < 8; ++e) s = dot2h(qh[h][e], kp[e], s);
     return s;
   }
 };
@@ -218,6 +233,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   constexpr int EPL = GE::EPL, PPL = GE::PPL, E = GE::E, LPK = GE::LPK, KPL = GE::KPL;
   constexpr int LPB = GE::LPB, KR = GE::KR;
   constexpr bool kInt8 = __is_same(KV, i8_t);
+  // int8 with two key rows per lane per tile: V goes through fp16 pairs.
+  constexpr bool kPairedV = kInt8 && KR == 2;
+  constexpr float kVBias = kPairedV ? kI8Bias : 128.0f;
 
   // 1-D grid, piece-major: ids 0 .. N*Hkv-1 are piece 0 of every (sequence,
   // KV head), then piece 1, ...  Consecutive ids go to different XCDs, so the
@@ -359,10 +377,10 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
       if constexpr (kInt8) {
-        float u[16];
-        QRegs<Q, KV, D, G>::widen(kt[k], u);
+        uint32_t kp[8];
+        QRegs<Q, KV, D, G>::pairs(kt[k], kp);
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[h][k] = qr.dot_widened(h, u);
+        for (int h = 0; h < G; ++h) s[h][k] = qr.dot_pairs(h, kp);
       } else {
 #pragma unroll
         for (int h = 0; h < G; ++h) s[h][k] = qr.dot_row(h, &kt[k * PPL]);
@@ -404,6 +422,33 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
       }
+    }
+    if constexpr (kPairedV) {
+      // Two keys per lane: dim e of both keys as one fp16 pair (1024 + u),
+      // weighted by (p0, p1) in one dot2; the bias is removed at the end.
+      uint32_t vp[16];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t u0 = vt[0][w] ^ 0x80808080u, u1 = vt[1][w] ^ 0x80808080u;
+        const uint32_t t01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+        const uint32_t t23 = __builtin_amdgcn_perm(u1, u0, 0x07030602u);  // u0.b2 u1.b2 u0.b3 u1.b3
+        vp[4 * w + 0] = f16pair_lo(t01);
+        vp[4 * w + 1] = f16pair_hi(t01);
+        vp[4 * w + 2] = f16pair_lo(t23);
+        vp[4 * w + 3] = f16pair_hi(t23);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mref = m[h] == kNegInf ? 0.0f : m[h];
+        const float p0 = fast_exp2(s[h][0] - mref), p1 = fast_exp2(s[h][1] - mref);
+        l[h] += p0 + p1;
+        const auto pp = __builtin_amdgcn_cvt_pkrtz(p0 * vs, p1 * vs);
+        corr[h] += float(pp[0]) + float(pp[1]);
+        const uint32_t pw = __builtin_bit_cast(uint32_t, pp);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = dot2h(pw, vp[e], acc[h][e]);
+      }
+      return;
     }
     float vf[KR][E];
 #pragma unroll
@@ -490,7 +535,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] = __builtin_fmaf(-128.0f, corr[h], acc[h][e]);
+      for (int e = 0; e < E; ++e) acc[h][e] = __builtin_fmaf(-kVBias, corr[h], acc[h][e]);
   }
 
   PA_STAMP(2);
