@@ -44,28 +44,33 @@ __device__ __forceinline__ float ubyte_f32(uint32_t x) {
   return float((x >> (8 * k)) & 0xFFu);
 }
 
-// Lane layout of a 16-token tile.  A lane holds PPL 16-byte pieces of one key
-// row (E = PPL * EPL elements): piece p covers dims p*D/PPL + c*EPL .. +EPL,
-// with c = lane % LPK.  LPK lanes share a key row, a wave-wide load covers KPL
-// rows, and load i reads piece i % PPL of key rows (i / PPL) * KPL + lane / LPK.
-// Every load still covers whole 64-byte spans of each row it touches.
+// Lane layout of a 16-token tile.  A lane's load unit is a piece of PB bytes
+// (16, or 8 for int8 with large groups, which keeps their per-lane q and
+// accumulators small).  A lane holds PPL pieces of one key row (E = PPL * EPL
+// elements): piece p covers dims p*D/PPL + c*EPL .. +EPL, with c = lane % LPK.
+// LPK lanes share a key row, a wave-wide load covers KPL rows, and load i
+// reads piece i % PPL of key rows (i / PPL) * KPL + lane / LPK.  Every
+// wave-wide load covers whole spans of 64 bytes or more of each row it touches.
 template <typename KV, int D, int G>
 struct Geo {
-  static constexpr int EPL = 16 / int(sizeof(KV));   // elements per 16-byte piece
+  static constexpr int PB = (__is_same(KV, i8_t) && G > 4) ? 8 : 16;  // bytes per piece
+  static constexpr int WPP = PB / 4;                  // 32-bit words per piece
+  static constexpr int EPL = PB / int(sizeof(KV));    // elements per piece
   // Two pieces per lane halve the reduction steps per score but double the
-  // per-lane accumulator; worth it for small groups only.
+  // per-lane accumulator; worth it for small bf16 groups only.
   static constexpr int PPL = (__is_same(KV, bf16_t) && G <= 4) ? 2 : 1;  // pieces per lane
   static constexpr int E = PPL * EPL;                 // elements per lane per key row
   static constexpr int LPK = D / E;                   // lanes per key row
   static constexpr int KPL = kWave / LPK;             // key rows per wave-wide load
   static constexpr int ROWB = D * int(sizeof(KV));    // bytes per key row
-  static constexpr int LPB = kBlockSize * ROWB / 1024;  // wave-wide loads per tile
+  static constexpr int LPB = kBlockSize * ROWB / (kWave * PB);  // wave-wide loads per tile
   static constexpr int KR = LPB / PPL;                // key rows per lane per tile
   static constexpr int TILE_BYTES = kBlockSize * ROWB;
+  using Piece = typename PieceT<PB>::type;
   static_assert(LPK >= 1 && LPK <= kWave && KR * KPL == kBlockSize, "unsupported geometry");
   // Byte offset of load i for this lane (r = lane / LPK, c = lane % LPK).
   __device__ static int offset(int i, int r, int c) {
-    return (i / PPL) * (KPL * ROWB) + r * ROWB + (i % PPL) * (ROWB / PPL) + c * 16;
+    return (i / PPL) * (KPL * ROWB) + r * ROWB + (i % PPL) * (ROWB / PPL) + c * PB;
   }
 };
 
@@ -147,38 +152,45 @@ __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
 }
 
 template <int D, int G> struct QRegs<bf16_t, i8_t, D, G> {
-  uint32_t qh[G][8];  // this lane's 16 dims as fp16 pairs
-  float qsum[G];      // sum of those fp16 values
+  static constexpr int PB = Geo<i8_t, D, G>::PB;  // codes (dims) per lane
+  static constexpr int WPP = PB / 4;
+  uint32_t qh[G][PB / 2];  // this lane's PB dims as fp16 pairs
+  float qsum[G];           // sum of those fp16 values
   __device__ void load(const bf16_t* qrow, int c) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const bf16_t* p = qrow + size_t(h) * D + c * 16;
-      const u32x4 w0 = load16(p);
-      const u32x4 w1 = load16(p + 8);
+      const bf16_t* p = qrow + size_t(h) * D + c * PB;
+      uint32_t w[PB / 2];
+#pragma unroll
+      for (int j = 0; j < PB / 8; ++j) {
+        const u32x4 v = load16(p + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * j + e] = v[e];
+      }
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = e < 4 ? w0[e] : w1[e - 4];
-        const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w), bf16_hi(w));
+      for (int e = 0; e < PB / 2; ++e) {
+        const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e]), bf16_hi(w[e]));
         qh[h][e] = __builtin_bit_cast(uint32_t, hp);
         s += float(hp[0]) + float(hp[1]);
       }
       qsum[h] = s;
     }
   }
-  // The 16 codes of one 16-byte load as fp16 pairs (1024 + u).
-  __device__ static void pairs(u32x4 k, uint32_t (&kp)[8]) {
+  // The PB codes of one piece as fp16 pairs (1024 + u).
+  template <typename P>
+  __device__ static void pairs(const P& k, uint32_t (&kp)[PB / 2]) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < WPP; ++w) {
       const uint32_t u = k[w] ^ 0x80808080u;
       kp[2 * w] = f16pair_lo(u);
       kp[2 * w + 1] = f16pair_hi(u);
     }
   }
-  __device__ float dot_pairs(int h, const uint32_t (&kp)[8]) const {
+  __device__ float dot_pairs(int h, const uint32_t (&kp)[PB / 2]) const {
     float s = -kI8Bias * qsum[h];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s = dot2h(qh[h][e], kp[e], s);
+    for (int e = 0; e < PB / 2; ++e) s = dot2h(qh[h][e], kp[e], s);
     return s;
   }
 };
@@ -203,10 +215,10 @@ template <> struct VWiden<bf16_t> {
   }
 };
 template <> struct VWiden<i8_t> {
-  static constexpr int EPL = 16;
-  __device__ static void run(u32x4 v, float (&o)[16]) {
+  template <typename P, int N>
+  __device__ static void run(const P& v, float (&o)[N]) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < N / 4; ++w) {
       uint32_t x = v[w] ^ 0x80808080u;
       o[4 * w + 0] = ubyte_f32<0>(x);
       o[4 * w + 1] = ubyte_f32<1>(x);
@@ -227,14 +239,15 @@ template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v
 // ---------------------------------------------------------------------------
 // With 8 waves per workgroup, keep two workgroups per CU (4 waves per SIMD,
 // at most 128 VGPRs); with 4 the register budget is left to the compiler.
-template <typename Q, typename KV, int D, int G, int NW, bool APPEND>
+template <typename Q, typename KV, int D, int G, int NW, int RING, bool APPEND>
 __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode_pass1(DecodeArgs a) {
   using GE = Geo<KV, D, G>;
   constexpr int EPL = GE::EPL, PPL = GE::PPL, E = GE::E, LPK = GE::LPK, KPL = GE::KPL;
-  constexpr int LPB = GE::LPB, KR = GE::KR;
+  constexpr int LPB = GE::LPB, KR = GE::KR, WPP = GE::WPP;
+  using P = typename GE::Piece;
   constexpr bool kInt8 = __is_same(KV, i8_t);
   // int8 with two key rows per lane per tile: V goes through fp16 pairs.
-  constexpr bool kPairedV = kInt8 && KR == 2;
+  constexpr bool kPairedV = kInt8 && KR % 2 == 0;
   constexpr float kVBias = kPairedV ? kI8Bias : 128.0f;
 
   // 1-D grid, piece-major: ids 0 .. N*Hkv-1 are piece 0 of every (sequence,
@@ -266,15 +279,15 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 
   // Append mode: this lane's pieces of the new token's K and V (position
   // L - 1), and its slot.
-  u32x4 nk[PPL], nv[PPL];
+  P nk[PPL], nv[PPL];
   int64_t slot = -1;
   if constexpr (APPEND) {
     const size_t row = (size_t(b) * a.kv_heads + g) * GE::ROWB;
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
-      const size_t off = row + size_t(p) * (GE::ROWB / PPL) + size_t(c) * 16;
-      nk[p] = load16(reinterpret_cast<const char*>(a.new_k) + off);
-      nv[p] = load16(reinterpret_cast<const char*>(a.new_v) + off);
+      const size_t off = row + size_t(p) * (GE::ROWB / PPL) + size_t(c) * GE::PB;
+      nk[p] = *reinterpret_cast<const P*>(reinterpret_cast<const char*>(a.new_k) + off);
+      nv[p] = *reinterpret_cast<const P*>(reinterpret_cast<const char*>(a.new_v) + off);
     }
     slot = a.slot_mapping[b];
   }
@@ -294,9 +307,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       const size_t dst = (size_t(g) * a.num_blocks * kBlockSize + size_t(slot)) * GE::ROWB;
 #pragma unroll
       for (int p = 0; p < PPL; ++p) {
-        const size_t off = dst + size_t(p) * (GE::ROWB / PPL) + size_t(c) * 16;
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + off) = nk[p];
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + off) = nv[p];
+        const size_t off = dst + size_t(p) * (GE::ROWB / PPL) + size_t(c) * GE::PB;
+        *reinterpret_cast<P*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + off) = nk[p];
+        *reinterpret_cast<P*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + off) = nv[p];
       }
     }
   }
@@ -326,16 +339,16 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // A fetch with live == false (past the wave's last tile) keeps the
   // instruction stream, and so the wait counts, identical but reads nothing:
   // its buffer resource has zero records.
-  auto fetch = [&](int blk, bool live, u32x4 (&kt)[LPB], u32x4 (&vt)[LPB], float& ks, float& vs) {
+  auto fetch = [&](int blk, bool live, P (&kt)[LPB], P (&vt)[LPB], float& ks, float& vs) {
     const int phys = min(max(__builtin_amdgcn_readlane(tab, blk - blk_begin), 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * GE::TILE_BYTES;
     const int bytes = live ? GE::TILE_BYTES : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + tile, bytes);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) kt[i] = buffer_load16_stream(kr, lane_off[i]);
+    for (int i = 0; i < LPB; ++i) kt[i] = PieceT<GE::PB>::load(kr, lane_off[i]);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) vt[i] = buffer_load16_stream(vr, lane_off[i]);
+    for (int i = 0; i < LPB; ++i) vt[i] = PieceT<GE::PB>::load(vr, lane_off[i]);
     if constexpr (kInt8) {
       ks = a.k_scale[head_blocks + phys];
       vs = a.v_scale[head_blocks + phys];
@@ -356,8 +369,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // multiply per accumulator element) almost never runs.  The final
   // normalisation by the running sum makes the result independent of m.
   constexpr float kSlack = 8.0f;
-  auto process = [&](auto mask_tag, int blk, u32x4 (&kt)[LPB], u32x4 (&vt)[LPB], float ks,
-                     float vs) {
+  auto process = [&](auto mask_tag, int blk, P (&kt)[LPB], P (&vt)[LPB], float ks, float vs) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK && APPEND) {
       // Position L - 1 is the token being appended: take its row from the input.
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
         for (int p = 0; p < PPL; ++p)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
+          for (int w = 0; w < WPP; ++w) {
             kt[k * PPL + p][w] = is_new ? nk[p][w] : kt[k * PPL + p][w];
             vt[k * PPL + p][w] = is_new ? nv[p][w] : vt[k * PPL + p][w];
           }
@@ -377,7 +389,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
       if constexpr (kInt8) {
-        uint32_t kp[8];
+        uint32_t kp[GE::PB / 2];
         QRegs<Q, KV, D, G>::pairs(kt[k], kp);
 #pragma unroll
         for (int h = 0; h < G; ++h) s[h][k] = qr.dot_pairs(h, kp);
@@ -400,7 +412,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
         for (int p = 0; p < PPL; ++p)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) vt[k * PPL + p][w] = valid ? vt[k * PPL + p][w] : 0u;
+          for (int w = 0; w < WPP; ++w) vt[k * PPL + p][w] = valid ? vt[k * PPL + p][w] : 0u;
       }
     }
     bool grow = false;
@@ -424,29 +436,33 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       }
     }
     if constexpr (kPairedV) {
-      // Two keys per lane: dim e of both keys as one fp16 pair (1024 + u),
-      // weighted by (p0, p1) in one dot2; the bias is removed at the end.
-      uint32_t vp[16];
+      // Key rows 2m and 2m+1 of this lane: dim e of both as one fp16 pair
+      // (1024 + u), weighted by (p_2m, p_2m+1) in one dot2; the bias is removed
+      // at the end.
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t u0 = vt[0][w] ^ 0x80808080u, u1 = vt[1][w] ^ 0x80808080u;
-        const uint32_t t01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
-        const uint32_t t23 = __builtin_amdgcn_perm(u1, u0, 0x07030602u);  // u0.b2 u1.b2 u0.b3 u1.b3
-        vp[4 * w + 0] = f16pair_lo(t01);
-        vp[4 * w + 1] = f16pair_hi(t01);
-        vp[4 * w + 2] = f16pair_lo(t23);
-        vp[4 * w + 3] = f16pair_hi(t23);
-      }
+      for (int mp = 0; mp < KR / 2; ++mp) {
+        uint32_t vp[4 * WPP];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mref = m[h] == kNegInf ? 0.0f : m[h];
-        const float p0 = fast_exp2(s[h][0] - mref), p1 = fast_exp2(s[h][1] - mref);
-        l[h] += p0 + p1;
-        const auto pp = __builtin_amdgcn_cvt_pkrtz(p0 * vs, p1 * vs);
-        corr[h] += float(pp[0]) + float(pp[1]);
-        const uint32_t pw = __builtin_bit_cast(uint32_t, pp);
+        for (int w = 0; w < WPP; ++w) {
+          const uint32_t u0 = vt[2 * mp][w] ^ 0x80808080u, u1 = vt[2 * mp + 1][w] ^ 0x80808080u;
+          const uint32_t t01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+          const uint32_t t23 = __builtin_amdgcn_perm(u1, u0, 0x07030602u);  // u0.b2 u1.b2 u0.b3 u1.b3
+          vp[4 * w + 0] = f16pair_lo(t01);
+          vp[4 * w + 1] = f16pair_hi(t01);
+          vp[4 * w + 2] = f16pair_lo(t23);
+          vp[4 * w + 3] = f16pair_hi(t23);
+        }
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] = dot2h(pw, vp[e], acc[h][e]);
+        for (int h = 0; h < G; ++h) {
+          const float mref = m[h] == kNegInf ? 0.0f : m[h];
+          const float p0 = fast_exp2(s[h][2 * mp] - mref), p1 = fast_exp2(s[h][2 * mp + 1] - mref);
+          l[h] += p0 + p1;
+          const auto pp = __builtin_amdgcn_cvt_pkrtz(p0 * vs, p1 * vs);
+          corr[h] += float(pp[0]) + float(pp[1]);
+          const uint32_t pw = __builtin_bit_cast(uint32_t, pp);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[h][e] = dot2h(pw, vp[e], acc[h][e]);
+        }
       }
       return;
     }
@@ -491,43 +507,49 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     }
   };
 
-  // Each wave takes every NW-th tile of the piece, with the next tile's loads
-  // in flight while one is reduced (two register buffers, loop unrolled over
-  // them so buffer indices are compile-time constants).  Fetches inside the
-  // loop are unconditional -- past the wave's last tile they read nothing (see
-  // fetch) -- so every path has the same loads outstanding and each wait covers
-  // exactly the tile about to be reduced.  The sequence's partial last block is
-  // reduced after the loop with the masked body.
+  // Each wave takes every NW-th tile of the piece.  Tiles go through a ring
+  // of RING register buffers: while tile j is reduced, tiles j+1 .. j+RING-1
+  // are in flight.  The loop is unrolled over the ring so buffer indices are
+  // compile-time constants.  Fetches inside the loop are unconditional (past
+  // the wave's last tile they read nothing, see fetch), so every path has the
+  // same loads outstanding and each wait covers exactly the tile about to be
+  // reduced.  The sequence's masked last tile (and, in append mode, the tile
+  // holding position L - 1) is reduced after the loop.
   using Plain = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
   const int first = blk_begin + wave;
   const int n_my = first < blk_end ? cdiv(blk_end - first, NW) : 0;
   if (n_my > 0) {
     const int last = n_my - 1;
-    // The wave's last tile takes the masked body if it is the context's
-    // partial block, or (append mode) the block holding position L - 1.
     const int last_blk = first + last * NW;
     const bool last_masked = (last_blk + 1) * kBlockSize > L ||
                              (APPEND && last_blk == cdiv(L, kBlockSize) - 1);
-    const int last_plain = last_masked ? last - 1 : last;
-    u32x4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
-    float ksa, vsa, ksb, vsb;
-    fetch(first, true, ka, va, ksa, vsa);
+    const int n_plain = last_masked ? last : n_my;
+    auto tile = [&](int j) { return first + min(j, last) * NW; };
+    P kb[RING][LPB], vb[RING][LPB];
+    float ksb[RING], vsb[RING];
+#pragma unroll
+    for (int v = 0; v < RING - 1; ++v) fetch(tile(v), v <= last, kb[v], vb[v], ksb[v], vsb[v]);
     int j = 0;
-    for (; j + 1 <= last_plain; j += 2) {
-      fetch(first + (j + 1) * NW, true, kb2, vb2, ksb, vsb);
-      process(Plain{}, first + j * NW, ka, va, ksa, vsa);
-      fetch(first + min(j + 2, last) * NW, j + 2 <= last, ka, va, ksa, vsa);
-      process(Plain{}, first + (j + 1) * NW, kb2, vb2, ksb, vsb);
+    for (; j + RING - 1 < n_plain; j += RING) {
+#pragma unroll
+      for (int v = 0; v < RING; ++v) {
+        const int nb = (v + RING - 1) % RING;  // constant once unrolled
+        fetch(tile(j + v + RING - 1), j + v + RING - 1 <= last, kb[nb], vb[nb], ksb[nb], vsb[nb]);
+        process(Plain{}, tile(j + v), kb[v], vb[v], ksb[v], vsb[v]);
+      }
     }
-    // Left: tile j (already in ka) if j <= last, and possibly tile last.
-    if (j < last) {
-      fetch(first + last * NW, true, kb2, vb2, ksb, vsb);
-      process(Plain{}, first + j * NW, ka, va, ksa, vsa);
-      process(Masked{}, first + last * NW, kb2, vb2, ksb, vsb);
-    } else if (j == last) {
-      if (last_masked) process(Masked{}, first + j * NW, ka, va, ksa, vsa);
-      else process(Plain{}, first + j * NW, ka, va, ksa, vsa);
+    // Fewer than RING plain tiles remain, then possibly the masked one; tiles
+    // up to j + RING - 2 are already in flight.
+#pragma unroll
+    for (int v = 0; v < RING; ++v) {
+      if (j + v <= last) {
+        if (v == RING - 1) fetch(tile(j + v), true, kb[v], vb[v], ksb[v], vsb[v]);
+        if (j + v < n_plain)
+          process(Plain{}, tile(j + v), kb[v], vb[v], ksb[v], vsb[v]);
+        else
+          process(Masked{}, tile(j + v), kb[v], vb[v], ksb[v], vsb[v]);
+      }
     }
   }
 
@@ -618,14 +640,25 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
   for (int s = lane; s < n_pieces; s += 64) M = fmaxf(M, lse[s]);
   M = stride_max<1>(M);
   constexpr int PER = D / 64;
+  constexpr int BATCH = 8;  // pieces whose loads are in flight together
   float o[PER] = {};
   float wsum = 0.0f;
-  for (int s = 0; s < n_pieces; ++s) {
-    const float ls = lse[s];
-    const float w = ls == kNegInf ? 0.0f : fast_exp2(ls - M);
-    wsum += w;
+  for (int s0 = 0; s0 < n_pieces; s0 += BATCH) {
+    float ls[BATCH], ov[BATCH][PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) o[j] = __builtin_fmaf(w, po[size_t(s) * D + j * 64 + lane], o[j]);
+    for (int u = 0; u < BATCH; ++u) {
+      const int sp = min(s0 + u, n_pieces - 1);
+      ls[u] = s0 + u < n_pieces ? lse[sp] : kNegInf;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) ov[u][j] = po[size_t(sp) * D + j * 64 + lane];
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const float w = ls[u] == kNegInf ? 0.0f : fast_exp2(ls[u] - M);
+      wsum += w;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) o[j] = __builtin_fmaf(w, ov[u][j], o[j]);
+    }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
 #pragma unroll
@@ -636,18 +669,24 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4
 #endif
+#ifndef PA_I8_RING
+#define PA_I8_RING 2
+#endif
 
 template <typename Q, typename KV, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, bool append, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;      // waves per workgroup
+  // Tiles in flight per wave (ring buffers).  int8 kernels hold many
+  // registers (one wave per SIMD), so a deeper ring hides their latency.
+  constexpr int kRing = __is_same(KV, i8_t) ? (G <= 8 ? PA_I8_RING : 2) : 2;
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
   if constexpr (!__is_same(KV, i8_t)) {
     if (append) {
-      decode_pass1<Q, KV, D, G, NW, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+      decode_pass1<Q, KV, D, G, NW, kRing, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
       return hipGetLastError();
     }
   }
-  decode_pass1<Q, KV, D, G, NW, false><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+  decode_pass1<Q, KV, D, G, NW, kRing, false><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 

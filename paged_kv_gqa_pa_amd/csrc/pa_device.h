@@ -20,6 +20,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -118,5 +119,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ u32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, int offset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 2));
 }
+__device__ __forceinline__ u32x2 buffer_load8_stream(__amdgpu_buffer_rsrc_t r, int offset) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, offset, 0, 2));
+}
+
+// The unit of a lane's load: 16 bytes (u32x4) or 8 bytes (u32x2).
+template <int PB> struct PieceT;
+template <> struct PieceT<16> {
+  using type = u32x4;
+  static constexpr int W = 4;
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) { return buffer_load16_stream(r, off); }
+};
+template <> struct PieceT<8> {
+  using type = u32x2;
+  static constexpr int W = 2;
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) { return buffer_load8_stream(r, off); }
+};
 
 }  // namespace pa
