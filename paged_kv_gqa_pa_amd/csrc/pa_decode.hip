@@ -36,6 +36,12 @@ __device__ unsigned long long g_times[8192 * 6];
 #else
 #define PA_STAMP(k) do { } while (0)
 #endif
+#ifdef PA_TIMING
+__device__ unsigned long long g_wtimes[8192 * 8];
+#define PA_WSTAMP(w) do { if ((threadIdx.x & 63) == 0 && blockIdx.x < 8192) g_wtimes[blockIdx.x * 8 + (w)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define PA_WSTAMP(w) do { } while (0)
+#endif
 namespace {
 
 // Byte k of x as a float; the backend selects v_cvt_f32_ubyte{k}.
@@ -560,29 +566,61 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       for (int e = 0; e < E; ++e) acc[h][e] = __builtin_fmaf(-kVBias, corr[h], acc[h][e]);
   }
 
+  PA_WSTAMP(wave);
   PA_STAMP(2);
-  // Merge the key rows of this wave (lanes c, c + LPK, c + 2 LPK, ...).
-  if constexpr (LPK < kWave) {
+  // Merge the key rows of this wave (lanes c, c + LPK, c + 2 LPK, ...): all
+  // rows are brought to the wave's running max, then the accumulators are
+  // reduce-scattered over lane ^ 32 and lane ^ 16 (each swap step halves the
+  // values a lane holds), and the row groups left inside a 16-lane row are
+  // summed with the other waves through LDS.
+  constexpr int V = G * E;                                   // accumulator values per lane
+  constexpr int X32 = LPK <= 32 ? 2 : 1, X16 = LPK <= 16 ? 2 : 1;
+  constexpr int KEEP = V / (X32 * X16);                      // values a lane keeps
+  constexpr int RG = LPK < 16 ? 16 / LPK : 1;                // row groups left per lane row
+  float red[V];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mw = stride_max<LPK>(m[h]);
-      const float f = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mw);
-      l[h] = stride_sum<LPK>(l[h] * f);
+  for (int h = 0; h < G; ++h) {
+    const float mw = stride_max<LPK>(m[h]);
+    const float f = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mw);
+    l[h] = stride_sum<LPK>(l[h] * f);
+    m[h] = mw;
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] = stride_sum<LPK>(acc[h][e] * f);
-      m[h] = mw;
+    for (int e = 0; e < E; ++e) red[h * E + e] = acc[h][e] * f;
+  }
+  if constexpr (X32 == 2) {
+    // Lanes 0-31 keep the reduced first half of the values, lanes 32-63 the second.
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(red[i]),
+                                                      __float_as_uint(red[i + V / 2]), false, false);
+      red[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+  if constexpr (X16 == 2) {
+    // Even 16-lane rows keep the first half of what is left, odd rows the second.
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(red[i]),
+                                                      __float_as_uint(red[i + V / 4]), false, false);
+      red[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
   }
 
   // Merge the waves through LDS.
   __shared__ float s_m[NW][G], s_l[NW][G];
-  __shared__ float s_acc[NW][G][D];
-  if (lane < LPK) {
+  __shared__ float s_acc[NW][RG][G][D];
+  {
+    const int kbase = ((X32 == 2 ? (lane >> 5) * X16 : 0) + (X16 == 2 ? (lane >> 4) & 1 : 0)) * KEEP;
+    const int rg = RG > 1 ? (lane & 15) / LPK : 0;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int i = 0; i < KEEP; ++i) {
+      const int v = kbase + i;
+      const int h = v / E, e = v - h * E;
+      s_acc[wave][rg][h][(e / EPL) * (D / PPL) + c * EPL + e % EPL] = red[i];
+    }
+    if (lane == 0) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s_acc[wave][h][(e / EPL) * (D / PPL) + c * EPL + e % EPL] = acc[h][e];
-      if (c == 0) {
+      for (int h = 0; h < G; ++h) {
         s_m[wave][h] = m[h];
         s_l[wave][h] = l[h];
       }
@@ -602,7 +640,10 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     for (int w = 0; w < NW; ++w) {
       const float f = s_m[w][h] == kNegInf ? 0.0f : fast_exp2(s_m[w][h] - M);
       lsum = __builtin_fmaf(s_l[w][h], f, lsum);
-      o = __builtin_fmaf(s_acc[w][h][d], f, o);
+      float x = s_acc[w][0][h][d];
+#pragma unroll
+      for (int j = 1; j < RG; ++j) x += s_acc[w][j][h][d];
+      o = __builtin_fmaf(x, f, o);
     }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
     const size_t row = size_t(b) * Hq + size_t(g) * G + h;
@@ -672,13 +713,16 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
 #ifndef PA_I8_RING
 #define PA_I8_RING 2
 #endif
+#ifndef PA_RING
+#define PA_RING 2
+#endif
 
 template <typename Q, typename KV, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, bool append, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;      // waves per workgroup
   // Tiles in flight per wave (ring buffers).  int8 kernels hold many
   // registers (one wave per SIMD), so a deeper ring hides their latency.
-  constexpr int kRing = __is_same(KV, i8_t) ? (G <= 8 ? PA_I8_RING : 2) : 2;
+  constexpr int kRing = __is_same(KV, i8_t) ? (G <= 8 ? PA_I8_RING : 2) : PA_RING;
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
   if constexpr (!__is_same(KV, i8_t)) {
     if (append) {
@@ -720,6 +764,9 @@ hipError_t dispatch_dim(const DecodeArgs& a, int G, bool ap, hipStream_t stream)
 #ifdef PA_TIMING
 extern "C" int pa_debug_times(unsigned long long* host, int n) {
   return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_times), sizeof(unsigned long long) * n) == hipSuccess ? 0 : -1;
+}
+extern "C" int pa_debug_wtimes(unsigned long long* host, int n) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_wtimes), sizeof(unsigned long long) * n) == hipSuccess ? 0 : -1;
 }
 #endif
 
