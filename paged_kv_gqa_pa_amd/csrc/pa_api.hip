@@ -138,7 +138,7 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   if (st != PA_OK) return st;
   const int G = q_heads / kv_heads;
   if (is_verify) {
-    if (!pa::verify_supported(q_dtype, kv_dtype, head_dim, G, T))
+    if (!pa::rows_supported(q_dtype, kv_dtype, head_dim, G, T))
       return fail(PA_ERR_UNSUPPORTED,
                   "verify not built for q=%d kv=%d head_dim=%d group=%d tokens=%d", q_dtype,
                   kv_dtype, head_dim, G, T);
@@ -187,7 +187,9 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.new_k = app.key;
   a.new_v = app.value;
   a.slot_mapping = app.slot_mapping;
-  hipError_t e = is_verify ? pa::launch_verify_pass1(a, s) : pa::launch_decode_pass1(a, app.on, s);
+  // Verify calls, and decode over an int8 cache, run on the matrix cores.
+  const bool rows = is_verify || kv_dtype == PA_INT8;
+  hipError_t e = rows ? pa::launch_rows_pass1(a, s) : pa::launch_decode_pass1(a, app.on, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pass-1 launch failed: %s", hipGetErrorString(e));
   if (plan.max_pieces > 1) {
     pa::MergeArgs m{};

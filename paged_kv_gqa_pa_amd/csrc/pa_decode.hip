@@ -29,6 +29,16 @@
 #include "pa_device.h"
 #include "pa_kernels.h"
 
+#ifndef PA_I8_PB8_MIN_G
+#define PA_I8_PB8_MIN_G 5
+#endif
+#ifndef PA_I8_MINW
+#define PA_I8_MINW 1
+#endif
+#ifndef PA_PPL2_MAX_G
+#define PA_PPL2_MAX_G 4
+#endif
+
 namespace pa {
 #ifdef PA_TIMING
 __device__ unsigned long long g_times[8192 * 6];
@@ -59,12 +69,12 @@ __device__ __forceinline__ float ubyte_f32(uint32_t x) {
 // wave-wide load covers whole spans of 64 bytes or more of each row it touches.
 template <typename KV, int D, int G>
 struct Geo {
-  static constexpr int PB = (__is_same(KV, i8_t) && G > 4) ? 8 : 16;  // bytes per piece
+  static constexpr int PB = (__is_same(KV, i8_t) && G >= PA_I8_PB8_MIN_G) ? 8 : 16;  // bytes per piece
   static constexpr int WPP = PB / 4;                  // 32-bit words per piece
   static constexpr int EPL = PB / int(sizeof(KV));    // elements per piece
   // Two pieces per lane halve the reduction steps per score but double the
   // per-lane accumulator; worth it for small bf16 groups only.
-  static constexpr int PPL = (__is_same(KV, bf16_t) && G <= 4) ? 2 : 1;  // pieces per lane
+  static constexpr int PPL = (__is_same(KV, bf16_t) && G <= PA_PPL2_MAX_G) ? 2 : 1;  // pieces per lane
   static constexpr int E = PPL * EPL;                 // elements per lane per key row
   static constexpr int LPK = D / E;                   // lanes per key row
   static constexpr int KPL = kWave / LPK;             // key rows per wave-wide load
@@ -142,16 +152,6 @@ template <int D, int G> struct QRegs<bf16_t, bf16_t, D, G> {
 // q held as fp16 pairs (bf16 values are exact in fp16 within its normal range).
 // The bias comes off with the sum of this lane's (fp16-rounded) q:
 // sum q*(1152 + c) - 1152 * sum q = sum q*c.
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-constexpr uint32_t kMagic = 0x64646464u;   // fp16 high byte of 1024
-constexpr float kI8Bias = 1152.0f;         // 1024 + 128
-
-__device__ __forceinline__ uint32_t f16pair_lo(uint32_t u) {  // bytes 0,1 -> (1024+u0, 1024+u1)
-  return __builtin_amdgcn_perm(kMagic, u, 0x04010400u);
-}
-__device__ __forceinline__ uint32_t f16pair_hi(uint32_t u) {  // bytes 2,3
-  return __builtin_amdgcn_perm(kMagic, u, 0x04030402u);
-}
 __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
                                 false);
@@ -246,7 +246,7 @@ template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v
 // With 8 waves per workgroup, keep two workgroups per CU (4 waves per SIMD,
 // at most 128 VGPRs); with 4 the register budget is left to the compiler.
 template <typename Q, typename KV, int D, int G, int NW, int RING, bool APPEND>
-__global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode_pass1(DecodeArgs a) {
+__global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV, i8_t) ? PA_I8_MINW : 1)) void decode_pass1(DecodeArgs a) {
   using GE = Geo<KV, D, G>;
   constexpr int EPL = GE::EPL, PPL = GE::PPL, E = GE::E, LPK = GE::LPK, KPL = GE::KPL;
   constexpr int LPB = GE::LPB, KR = GE::KR, WPP = GE::WPP;
@@ -626,6 +626,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       }
     }
   }
+  PA_WSTAMP(4 + wave);
   __syncthreads();
   PA_STAMP(3);
 

@@ -98,6 +98,18 @@ __device__ __forceinline__ float stride_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// int8 codes as exact fp16: with u = c + 128 (the biased byte), placing u under
+// the constant high byte 0x64 gives the fp16 number 1024 + u = c + 1152.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+constexpr uint32_t kMagic = 0x64646464u;   // fp16 high byte of 1024
+constexpr float kI8Bias = 1152.0f;         // 1024 + 128
+__device__ __forceinline__ uint32_t f16pair_lo(uint32_t u) {  // bytes 0,1 -> (1024+u0, 1024+u1)
+  return __builtin_amdgcn_perm(kMagic, u, 0x04010400u);
+}
+__device__ __forceinline__ uint32_t f16pair_hi(uint32_t u) {  // bytes 2,3
+  return __builtin_amdgcn_perm(kMagic, u, 0x04030402u);
+}
+
 __device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // 16-byte streaming load (data read once: marked non-temporal).

@@ -71,8 +71,10 @@ struct MergeArgs {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheArgs& a, hipStream_t stream);
 hipError_t launch_decode_pass1(const DecodeArgs& a, bool append, hipStream_t stream);
-hipError_t launch_verify_pass1(const DecodeArgs& a, hipStream_t stream);
+// Matrix-core kernel for R = T * G <= 16 query rows per (sequence, KV head):
+// every verify call, and decode over an int8 cache.
+hipError_t launch_rows_pass1(const DecodeArgs& a, hipStream_t stream);
 bool decode_group_supported(int G);
-bool verify_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T);
+bool rows_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T);
 
 }  // namespace pa

@@ -1,26 +1,35 @@
-// Multi-token (speculative verify) paged attention on the matrix cores.
+// Paged attention on the matrix cores for several query rows per
+// (sequence, KV head): the T query tokens of a speculative verify step times
+// the G heads of a group ("From 183 ms to 19 ms per decode step", section
+// "Then speculative decoding got slower": query tokens times group heads as the
+// rows of one matrix product), and the G heads of an int8-cache decode step,
+// whose per-key work would otherwise bind on the vector ALUs.
 //
-// A verify step checks k+1 guessed tokens per sequence in one pass, with a
-// causal mask among the new tokens ("From 183 ms to 19 ms per decode step",
-// section "Then speculative decoding got slower": query tokens times group
-// heads on the rows of one matrix product, on the tensor cores).  For one
-// (sequence, KV head) the T query tokens of the G heads of the group form
-// R = T*G <= 16 query rows, so each 16-token cache tile is one dense 16x16
-// block of scores:
+// The R = T*G <= 16 rows of one (sequence, KV head) make each 16-token cache
+// tile a dense 16x16 block of scores.  Per tile:
 //
-//   S^T[key, row] = sum_d K[key, d] * Q[row, d]      v_mfma_f32_16x16x32_bf16
-//       A = K tile (key = lane % 16, 8 contiguous dims per lane: a 16-byte
-//       load straight from the cache), B = the query rows (loaded once).
-//   online softmax per row (fp32 running max and sum, rescaled per tile)
-//   O[row, d] += sum_key P[row, key] * V[key, d]     v_mfma_f32_16x16x16_bf16
-//       A = P: the score accumulator already holds, per lane, 4 keys of one
-//       row -- exactly the A layout of the 16x16x16 product, so P needs no
-//       shuffle.  B needs 4 keys of one dim per lane: the V tile goes through
-//       LDS (row pitch padded so the transposed reads hit distinct banks).
+//   K and V tiles arrive as contiguous 1 KiB wave loads and are staged in the
+//   wave's LDS (whole 128-byte lines per load; loading the product layouts
+//   straight from the cache touches half lines and was measurably slower).
+//   S^T[key, row] = sum_d K[key, d] Q[row, d]     16x16x32 products; A = key n's
+//       8 dims per lane read from LDS, B = the query rows, loaded once.
+//   online softmax per row: fp32 reference maximum with delayed rescaling.
+//   O[row, d] += sum_key P[row, key] V[key, d]    16x16x16 products; A = P, which
+//       the score accumulator already holds in the A layout; B = four keys of
+//       one dim per lane.  bf16: transposed reads from LDS.  int8: each lane
+//       reads 4 dims of one key and a product with the identity hands it 4 keys
+//       of one dim instead (the result layout of a product is the B layout of
+//       the next), the values passing through exactly.
+//
+// bf16 caches run all products in bf16 (P rounded to bf16).  int8 caches run
+// them in fp16: a code c becomes the exact fp16 number c + 1152 (byte permute
+// under a constant high byte), the scores lose the K bias as
+// -1152 * sum_d q[row, d], the V bias is removed by starting the transposing
+// product's accumulator at -1152, and P carries the tile's V scale.
 //
 // Row t*G + i is query token t of head g*G + i; token t sees positions
 // 0 .. L - T + t.  Pieces, workspace partials and the merge pass are shared
-// with decode (rows_per_seq = T * q_heads).
+// with the vector-ALU decode kernel (rows_per_seq = T * q_heads).
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -28,16 +37,71 @@ namespace pa {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRows = 16;  // query rows of one matrix tile
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * kWave) void verify_pass1(DecodeArgs a) {
-  constexpr int KCH = D / 32;            // 32-dim chunks of the score product
-  constexpr int VLD = D / 32;            // 1 KiB wave loads per V tile (16 * D * 2 bytes)
-  constexpr int OT = D / 16;             // 16-dim output tiles
-  constexpr int PITCH = D + 4;           // LDS row pitch in bf16 elements
-  constexpr int TILE_BYTES = kBlockSize * D * 2;
+// Products and conversions per cache element type.
+template <typename KV> struct MOps;
+template <> struct MOps<bf16_t> {
+  static constexpr uint32_t kOne = 0x3F80u;  // bf16 1.0
+  static constexpr float kVInit = 0.0f;
+  __device__ static f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                  __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+  }
+  __device__ static f32x4 mm16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
+  // Two fp32 values that are bf16 numbers: their high halves.
+  __device__ static uint32_t pack_exact(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
+  __device__ static uint32_t pack_round(float lo, float hi) {
+    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  }
+};
+template <> struct MOps<i8_t> {
+  static constexpr uint32_t kOne = 0x3C00u;  // fp16 1.0
+  static constexpr float kVInit = -kI8Bias;
+  __device__ static f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, k),
+                                                 __builtin_bit_cast(h16x8, q), c, 0, 0, 0);
+  }
+  __device__ static f32x4 mm16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4, a),
+                                                 __builtin_bit_cast(h16x4, b), c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack_exact(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  __device__ static uint32_t pack_round(float lo, float hi) { return pack_exact(lo, hi); }
+};
+
+// Eight codes (two words) as the fp16 numbers c + 1152.
+__device__ __forceinline__ u32x4 codes8_f16(uint32_t w0, uint32_t w1) {
+  const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+  return u32x4{f16pair_lo(u0), f16pair_hi(u0), f16pair_lo(u1), f16pair_hi(u1)};
+}
+
+template <typename KV, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
+  constexpr bool kInt8 = __is_same(KV, i8_t);
+  constexpr int ROWB = D * int(sizeof(KV));  // bytes per key row
+  constexpr int NL = ROWB / 64;              // 1 KiB wave loads per tile (16 rows)
+  constexpr int NQ = D / 32;                 // score products per tile
+  constexpr int NT = D / 16;                 // output blocks of 16 dims
+  constexpr int TILE_BYTES = kBlockSize * ROWB;
+  // Per-wave LDS: the staged K and V tiles (row pitches padded so the reads
+  // below hit distinct banks), reused for the wave's O rows after its loop.
+  constexpr int KPB = ROWB + 16;
+  constexpr int VPB = kInt8 ? ROWB + 16 : ROWB + 8;
+  constexpr int STAGE = kBlockSize * (KPB + VPB);
+  constexpr int OBYTES = kRows * D * 4;
+  constexpr int WBYTES = STAGE > OBYTES ? STAGE : OBYTES;
+  using M = MOps<KV>;
 
   const int pairs = a.num_seqs * a.kv_heads;
   const int piece = blockIdx.x / pairs;
@@ -51,8 +115,8 @@ __global__ __launch_bounds__(NW * kWave) void verify_pass1(DecodeArgs a) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;     // key row of the K operand / query row of S and P
-  const int grp = lane >> 4;   // which 8 dims (scores) or 4 keys (P, O rows)
+  const int n = lane & 15;     // key row of an operand read / query row of S, P
+  const int grp = lane >> 4;   // 8-dim group of a score product / key quad of S, P, O
   const int split_blocks = a.split_tokens / kBlockSize;
   const int blk_begin = piece * split_blocks;
 
@@ -61,16 +125,30 @@ __global__ __launch_bounds__(NW * kWave) void verify_pass1(DecodeArgs a) {
   const int tab = blk_begin + lane < a.max_blocks_per_seq ? bt[blk_begin + lane] : 0;
   const int t_row = n / G;
   const int h_row = g * G + (n - t_row * G);
-  bf16x8 qb[KCH];
+  // Query rows as the B operand of score product c: lane (row n, group grp)
+  // holds q[n][32c + 8grp .. +7] (fp16 for an int8 cache).
+  u32x4 qb[NQ];
+  float qpart = 0.0f;
   {
     const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) +
                        ((size_t(b) * T + t_row) * Hq + h_row) * D + 8 * grp;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      u32x4 w = n < R ? load16(qp + 32 * j) : u32x4{0u, 0u, 0u, 0u};
-      qb[j] = __builtin_bit_cast(bf16x8, w);
+    for (int c = 0; c < NQ; ++c) {
+      const u32x4 w = n < R ? load16(qp + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kInt8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e]), bf16_hi(w[e]));
+          qb[c][e] = __builtin_bit_cast(uint32_t, hp);
+          qpart += float(hp[0]) + float(hp[1]);
+        }
+      } else {
+        qb[c] = w;
+      }
     }
   }
+  // Row n's sum of (fp16) q over all dims: the four groups of row n.
+  const float qsum = kInt8 ? add_xor32(add_xor16(qpart)) : 0.0f;
 
   const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
@@ -84,78 +162,136 @@ __global__ __launch_bounds__(NW * kWave) void verify_pass1(DecodeArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
   const float sc = a.scale * kLog2e;
 
-  __shared__ uint16_t s_v[NW][kBlockSize][PITCH];
+  __shared__ __attribute__((aligned(16))) char s_raw[NW * WBYTES];
   __shared__ float s_m[NW][kRows], s_l[NW][kRows];
-  __shared__ float s_o[NW][kRows][D];
+  char* const s_k = s_raw + wave * WBYTES;
+  char* const s_v = s_k + kBlockSize * KPB;
 
-  float m = kNegInf;   // running max of row n (log2 units)
-  float lsum = 0.0f;   // this lane's share of row n's running sum
-  f32x4 o[OT];
+  // Identity as the B operand of the int8 V transposes: lane l holds I[4*grp + j][n].
+  u32x2 ident;
+  {
+    uint32_t e[4];
 #pragma unroll
-  for (int c = 0; c < OT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) e[j] = 4 * grp + j == n ? M::kOne : 0u;
+    ident = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+  }
+  const f32x4 vinit = {M::kVInit, M::kVInit, M::kVInit, M::kVInit};
 
-  auto fetch = [&](int blk, u32x4 (&kt)[KCH], u32x4 (&vt)[VLD]) {
+  float m = kNegInf;   // reference maximum of row n (log2 units)
+  float lsum = 0.0f;   // this lane's share of row n's sum
+  f32x4 o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Tiles are read as contiguous 1 KiB wave loads.  A fetch with live == false
+  // reads nothing (zero-record buffer resource), so the loop keeps one
+  // instruction stream and one set of wait counts.
+  auto fetch = [&](int blk, bool live, u32x4 (&kt)[NL], u32x4 (&vt)[NL], float& ks, float& vs) {
     const int phys = min(max(__builtin_amdgcn_readlane(tab, blk - blk_begin), 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * TILE_BYTES;
+    const int bytes = live ? TILE_BYTES : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + tile, bytes);
 #pragma unroll
-    for (int j = 0; j < KCH; ++j)
-      kt[j] = load16_stream(kbase + tile + n * (2 * D) + 64 * j + 16 * grp);
+    for (int c = 0; c < NL; ++c) kt[c] = buffer_load16_stream(kr, c * 1024 + lane * 16);
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) vt[i] = load16_stream(vbase + tile + i * 1024 + lane * 16);
+    for (int c = 0; c < NL; ++c) vt[c] = buffer_load16_stream(vr, c * 1024 + lane * 16);
+    if constexpr (kInt8) {
+      ks = a.k_scale[head_blocks + phys];
+      vs = a.v_scale[head_blocks + phys];
+    } else {
+      ks = 1.0f;
+      vs = 1.0f;
+    }
   };
 
-  auto process = [&](int blk, u32x4 (&kt)[KCH], u32x4 (&vt)[VLD]) {
-    // Stage V (zeros past the context: a zero weight must meet a finite value).
+  // Delayed rescaling: m is a reference maximum; weights are exp2(s - m), and
+  // O and the sum are rescaled only when a row's tile maximum exceeds its
+  // reference by more than kSlack (log2 units), so weights stay below 2^kSlack
+  // and the rescale almost never runs.  The final division by the sum makes
+  // the result independent of the reference.
+  constexpr float kSlack = 8.0f;
+  auto process = [&](int blk, u32x4 (&kt)[NL], u32x4 (&vt)[NL], float ks, float vs) {
+    // Stage the tile.  bf16 key rows past the context may hold anything, even
+    // NaN: their V rows are cleared (a zero weight must meet a finite value);
+    // their scores are replaced, not multiplied, below.
+    const bool tail = (blk + 1) * kBlockSize > L;
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int byte = i * 1024 + lane * 16;
-      const int key = byte / (2 * D);
-      const int d0 = (byte % (2 * D)) / 2;
-      const bool valid = blk * kBlockSize + key < L;
-      uint2* dst = reinterpret_cast<uint2*>(&s_v[wave][key][d0]);
-      dst[0] = valid ? uint2{vt[i][0], vt[i][1]} : uint2{0u, 0u};
-      dst[1] = valid ? uint2{vt[i][2], vt[i][3]} : uint2{0u, 0u};
+    for (int c = 0; c < NL; ++c) {
+      const int byte = c * 1024 + lane * 16;
+      const int key = byte / ROWB, col = byte % ROWB;
+      *reinterpret_cast<u32x4*>(s_k + key * KPB + col) = kt[c];
+      u32x4 v = vt[c];
+      if constexpr (!kInt8) {
+        if (tail && blk * kBlockSize + key >= L) v = u32x4{0u, 0u, 0u, 0u};
+      }
+      uint2* dst = reinterpret_cast<uint2*>(s_v + key * VPB + col);
+      dst[0] = uint2{v[0], v[1]};
+      dst[1] = uint2{v[2], v[3]};
     }
-    // Scores of keys 4*grp .. 4*grp+3 for row n.
+    // Scores of keys 4*grp .. 4*grp+3 for row n: product c takes key n's dims
+    // 32c + 8grp .. +7 as the A operand.
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < KCH; ++j)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[j]), qb[j], s, 0,
-                                                  0, 0);
+    for (int c = 0; c < NQ; ++c) {
+      u32x4 kop;
+      if constexpr (kInt8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(s_k + n * KPB + 32 * c + 8 * grp);
+        kop = codes8_f16(w.x, w.y);
+      } else {
+        kop = *reinterpret_cast<const u32x4*>(s_k + n * KPB + 64 * c + 16 * grp);
+      }
+      s = M::qk(kop, qb[c], s);
+    }
+    const float ssc = sc * ks;
     float tmax = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = blk * kBlockSize + 4 * grp + e;
-      s[e] = pos <= last_vis ? s[e] * sc : kNegInf;
-      tmax = fmaxf(tmax, s[e]);
+    for (int j = 0; j < 4; ++j) {
+      const int pos = blk * kBlockSize + 4 * grp + j;
+      const float x = (kInt8 ? s[j] - kI8Bias * qsum : s[j]) * ssc;
+      s[j] = pos <= last_vis ? x : kNegInf;
+      tmax = fmaxf(tmax, s[j]);
     }
-    tmax = max_xor32(max_xor16(tmax));   // over the 16 keys of the tile
-    const float mnew = fmaxf(m, tmax);
-    const float mref = mnew == kNegInf ? 0.0f : mnew;
-    const float alpha = fast_exp2(m - mref);
-    m = mnew;
+    tmax = max_xor32(max_xor16(tmax));   // row n over the 16 keys of the tile
+    if (__builtin_amdgcn_ballot_w64(tmax > m + kSlack) != 0) {
+      const float mnew = fmaxf(m, tmax);
+      const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+      // O rows 4*grp + j take the factor of that row (held by lane 4*grp + j).
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float ar = __shfl(alpha, 4 * grp + j);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[t][j] *= ar;
+      }
+    }
+    const float mref = m == kNegInf ? 0.0f : m;
     float p[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(s[e] - mref);
-    lsum = __builtin_fmaf(lsum, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-    // P as the A operand (row n, keys 4*grp ..), rounded to bf16.
-    s16x4 pa;
+    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[j] - mref);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    // P as the A operand (row n, keys 4*grp ..); an int8 tile's V scale rides on it.
+    const u32x2 pa = {M::pack_round(p[0] * vs, p[1] * vs), M::pack_round(p[2] * vs, p[3] * vs)};
+    // V of keys 4*grp .. 4*grp+3 at dim 16t + n (the B operand).
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pa[e] = short(f32_to_bf16(p[e]));
-    // O rows 4*grp + e take the rescale factor of that row.
+    for (int t = 0; t < NT; ++t) {
+      u32x2 vb;
+      if constexpr (kInt8) {
+        // key n's codes of dims 16t + 4grp .. +3, turned by the identity product
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(s_v + n * VPB + 16 * t + 4 * grp) ^
+                           0x80808080u;
+        const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
+        vb = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
+      } else {
+        // transposed reads: four keys of one dim
+        const uint16_t* col = reinterpret_cast<const uint16_t*>(s_v) + 16 * t + n;
+        uint32_t e[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ar = __shfl(alpha, 4 * grp + e);
-#pragma unroll
-      for (int c = 0; c < OT; ++c) o[c][e] *= ar;
-    }
-    // V of keys 4*grp .. 4*grp+3 at dim 16*c + n: the transposed read.
-#pragma unroll
-    for (int c = 0; c < OT; ++c) {
-      s16x4 vb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vb[e] = short(s_v[wave][4 * grp + e][16 * c + n]);
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[c], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) e[j] = col[(4 * grp + j) * (VPB / 2)];
+        vb = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+      }
+      o[t] = M::mm16(pa, vb, o[t]);
     }
   };
 
@@ -163,42 +299,45 @@ __global__ __launch_bounds__(NW * kWave) void verify_pass1(DecodeArgs a) {
   const int n_my = first < blk_end ? cdiv(blk_end - first, NW) : 0;
   if (n_my > 0) {
     const int last = n_my - 1;
-    u32x4 k0[KCH], v0[VLD], k1[KCH], v1[VLD];
-    fetch(first, k0, v0);
+    u32x4 k0[NL], v0[NL], k1[NL], v1[NL];
+    float ks0, vs0, ks1, vs1;
+    fetch(first, true, k0, v0, ks0, vs0);
     int j = 0;
     for (; j + 1 <= last; j += 2) {
-      fetch(first + (j + 1) * NW, k1, v1);
-      process(first + j * NW, k0, v0);
-      fetch(first + min(j + 2, last) * NW, k0, v0);
-      process(first + (j + 1) * NW, k1, v1);
+      fetch(first + (j + 1) * NW, true, k1, v1, ks1, vs1);
+      process(first + j * NW, k0, v0, ks0, vs0);
+      fetch(first + min(j + 2, last) * NW, j + 2 <= last, k0, v0, ks0, vs0);
+      process(first + (j + 1) * NW, k1, v1, ks1, vs1);
     }
-    if (j == last) process(first + j * NW, k0, v0);
+    if (j == last) process(first + j * NW, k0, v0, ks0, vs0);
   }
 
-  // Row totals (all four lane groups share each row's max), then the waves
-  // are merged through LDS.
+  // Row totals (the four key quads of each row); the wave's O rows go to its
+  // own LDS region (its staging buffers are no longer read), then the waves
+  // are merged.
   const float lrow = add_xor32(add_xor16(lsum));
   if (grp == 0) {
     s_m[wave][n] = m;
     s_l[wave][n] = lrow;
   }
+  float* const s_ow = reinterpret_cast<float*>(s_k);
 #pragma unroll
-  for (int c = 0; c < OT; ++c)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[wave][4 * grp + e][16 * c + n] = o[c][e];
+    for (int j = 0; j < 4; ++j) s_ow[(4 * grp + j) * D + 16 * t + n] = o[t][j];
   __syncthreads();
 
   for (int t = threadIdx.x; t < R * D; t += NW * kWave) {
     const int row = t / D, d = t % D;
-    float M = s_m[0][row];
+    float mx = s_m[0][row];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][row]);
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_m[w][row]);
     float lt = 0.0f, ot = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = s_m[w][row] == kNegInf ? 0.0f : fast_exp2(s_m[w][row] - M);
+      const float f = s_m[w][row] == kNegInf ? 0.0f : fast_exp2(s_m[w][row] - mx);
       lt = __builtin_fmaf(s_l[w][row], f, lt);
-      ot = __builtin_fmaf(s_o[w][row][d], f, ot);
+      ot = __builtin_fmaf(reinterpret_cast<const float*>(s_raw + w * WBYTES)[row * D + d], f, ot);
     }
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int tq = row / G;
@@ -208,26 +347,31 @@ __global__ __launch_bounds__(NW * kWave) void verify_pass1(DecodeArgs a) {
     } else {
       const size_t prow = orow * a.max_pieces + piece;
       a.part_o[prow * D + d] = ot * inv;
-      if (d == 0) a.part_lse[prow] = lt > 0.0f ? M + __log2f(lt) : kNegInf;
+      if (d == 0) a.part_lse[prow] = lt > 0.0f ? mx + __log2f(lt) : kNegInf;
     }
   }
 }
 
-}  // namespace
-
-bool verify_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T) {
-  return q_dtype == kBF16 && kv_dtype == kBF16 && (head_dim == 64 || head_dim == 128) &&
-         G >= 1 && T >= 1 && long(G) * T <= kRows;
-}
-
-hipError_t launch_verify_pass1(const DecodeArgs& a, hipStream_t stream) {
+template <typename KV>
+hipError_t launch_rows_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = 4;
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
   if (a.head_dim == 128)
-    verify_pass1<128, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    rows_pass1<KV, 128, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   else
-    verify_pass1<64, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    rows_pass1<KV, 64, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+bool rows_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T) {
+  return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kI8) &&
+         (head_dim == 64 || head_dim == 128) && G >= 1 && T >= 1 && long(G) * T <= kRows;
+}
+
+hipError_t launch_rows_pass1(const DecodeArgs& a, hipStream_t stream) {
+  return a.kv_dtype == kI8 ? launch_rows_t<i8_t>(a, stream) : launch_rows_t<bf16_t>(a, stream);
 }
 
 }  // namespace pa

@@ -19,14 +19,16 @@ def _verify(dc, split=0, max_len=None):
     case = dc.case
     out = torch.empty_like(dc.q)
     pa.verify(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, case.scale,
-              case.max_context_len if max_len is None else max_len, split_tokens=split)
+              case.max_context_len if max_len is None else max_len, dc.k_scale, dc.v_scale,
+              split_tokens=split)
     torch.cuda.synchronize()
     return out
 
 
 def _oracle_verify(case):
     return oracle.verify(case.q, case.k_cache, case.v_cache, case.block_tables,
-                         case.context_lens, case.scale, case.spec.q_dtype, case.spec.kv_dtype)
+                         case.context_lens, case.scale, case.spec.q_dtype, case.spec.kv_dtype,
+                         case.k_scale, case.v_scale)
 
 
 @pytest.mark.parametrize("split", [0, 256])
@@ -46,7 +48,7 @@ def test_spec_verify_full_size(split):
     assert err < TOL["bf16"], err
 
 
-def _random_verify_case(rng, lens, Hkv, G, D, T, poison=False):
+def _random_verify_case(rng, lens, Hkv, G, D, T, poison=False, kv="bf16"):
     lens = np.asarray(lens, np.int32)
     maxb = max(1, -(-int(lens.max()) // 16))
     need = int(sum(-(-int(L) // 16) for L in lens))
@@ -65,29 +67,35 @@ def _random_verify_case(rng, lens, Hkv, G, D, T, poison=False):
                 k32[:, phys, L % 16:] = np.nan
                 v32[:, phys, L % 16:] = np.nan
     q = wl.f32_to_bf16_bits(rng.standard_normal((len(lens), T, Hkv * G, D), dtype=np.float32))
-    spec = wl.Spec("random_verify", 0, len(lens), Hkv * G, Hkv, D, nb, "bf16", "bf16",
+    spec = wl.Spec("random_verify", 0, len(lens), Hkv * G, Hkv, D, nb, "bf16", kv,
                    max(16, int(lens.max())), num_query_tokens=T)
+    if kv == "int8":
+        # codes are finite whatever sits past the context; scales of unused blocks stay random
+        kc, ks = wl.quantize_int8_blocks(np.nan_to_num(k32, nan=100.0))
+        vc, vs = wl.quantize_int8_blocks(np.nan_to_num(v32, nan=-100.0))
+    else:
+        kc, vc, ks, vs = wl.f32_to_bf16_bits(k32), wl.f32_to_bf16_bits(v32), None, None
     return wl.PagedCase(spec=spec, layer=0, context_lens=lens, block_tables=table, q=q,
-                        k_cache=wl.f32_to_bf16_bits(k32), v_cache=wl.f32_to_bf16_bits(v32),
-                        k_scale=None, v_scale=None, new_k=None, new_v=None,
+                        k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs, new_k=None, new_v=None,
                         slot_mapping=None, scale=1.0 / np.sqrt(D))
 
 
 EDGE = [0, 1, 2, 3, 4, 5, 6, 15, 16, 17, 21, 33, 100, 255, 256, 257, 700]
 
 
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
 @pytest.mark.parametrize("G,T", [(1, 1), (1, 16), (2, 5), (3, 5), (2, 8), (8, 2), (16, 1), (6, 2)])
 @pytest.mark.parametrize("D", [64, 128])
-def test_verify_edges(G, T, D):
-    _say("verify edges G", G, "T", T, "D", D)
+def test_verify_edges(G, T, D, kv):
+    _say("verify edges", kv, "G", G, "T", T, "D", D)
     rng = np.random.default_rng(1000 + 10 * G + T + D)
-    case = _random_verify_case(rng, EDGE, Hkv=2, G=G, D=D, T=T, poison=True)
+    case = _random_verify_case(rng, EDGE, Hkv=2, G=G, D=D, T=T, poison=True, kv=kv)
     dc = DevCase(case)
     want = _oracle_verify(case)
     for split in (0, 32):
         out = _verify(dc, split)
         err = max_abs_err(out, want)
-        assert err < TOL["bf16"], (split, err)
+        assert err < TOL[kv], (split, err)
     got = out.float().cpu().numpy()
     # a row with no visible position (context shorter than the tokens before it) is zero
     for b, L in enumerate(case.context_lens):
