@@ -116,9 +116,12 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  * sequence's result does not depend on what it is batched with.
  *
  * pa_default_split_tokens returns the piece length used when a call passes
- * split_tokens = 0.
+ * split_tokens = 0 (num_query_tokens is 1 for pa_decode): 512 * kv_heads
+ * clamped to [1024, 2048] for calls that run on the matrix cores (pa_verify,
+ * and pa_decode over an int8 cache), else 64 * kv_heads clamped to [128, 512].
  */
-int pa_default_split_tokens(int q_heads, int kv_heads, int head_dim, int kv_dtype);
+int pa_default_split_tokens(int num_query_tokens, int q_heads, int kv_heads, int head_dim,
+                            int kv_dtype);
 
 /*
  * Workspace bytes pa_decode / pa_verify need for these sizes (0 when one
@@ -147,7 +150,7 @@ size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv
  * max_context_len  host-side upper bound of context_lens (sizes the grid and
  *               the workspace; does not change the arithmetic)
  * scale         softmax scale (typically 1/sqrt(head_dim))
- * split_tokens  piece length, a multiple of block_size in [16, 1024], or 0
+ * split_tokens  piece length, a multiple of block_size in [16, 4096], or 0
  *               for pa_default_split_tokens()
  * workspace     device scratch of at least pa_workspace_size(...) bytes,
  *               256-byte aligned (may be NULL when that size is 0); it holds

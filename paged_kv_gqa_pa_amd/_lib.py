@@ -53,7 +53,7 @@ def _load():
     lib.pa_reshape_and_cache.restype = i
     lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.pa_default_split_tokens.restype = i
-    lib.pa_default_split_tokens.argtypes = [i, i, i, i]
+    lib.pa_default_split_tokens.argtypes = [i, i, i, i, i]
     lib.pa_workspace_size.restype = sz
     lib.pa_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     lib.pa_decode.restype = i
@@ -109,8 +109,10 @@ def version() -> int:
     return _load().pa_version()
 
 
-def default_split_tokens(q_heads: int, kv_heads: int, head_dim: int, kv_dtype: torch.dtype) -> int:
-    return _load().pa_default_split_tokens(q_heads, kv_heads, head_dim, _DTYPE[kv_dtype])
+def default_split_tokens(q_heads: int, kv_heads: int, head_dim: int, kv_dtype: torch.dtype,
+                         num_query_tokens: int = 1) -> int:
+    return _load().pa_default_split_tokens(num_query_tokens, q_heads, kv_heads, head_dim,
+                                           _DTYPE[kv_dtype])
 
 
 def workspace_size(num_seqs: int, num_query_tokens: int, q_heads: int, kv_heads: int,
@@ -175,7 +177,7 @@ def _attention(fn_verify: bool, out, q, k_cache, v_cache, block_tables, context_
         k_scale = v_scale = None
     need = _load().pa_workspace_size(N, T, Hq, Hkv, D, int(max_context_len), kvd, int(split_tokens))
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -234,7 +236,7 @@ def decode_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tabl
     kvd = _DTYPE[k_cache.dtype]
     need = _load().pa_workspace_size(N, 1, Hq, Hkv, D, int(max_context_len), kvd, int(split_tokens))
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_load().pa_decode_append(_ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache),
                                     _ptr(v_cache), _ptr(slot_mapping), _ptr(block_tables),

@@ -37,15 +37,23 @@ struct Plan {
   size_t total() const { return max_pieces > 1 ? o_bytes + lse_bytes : 0; }
 };
 
-int default_split(int q_heads, int kv_heads, int head_dim, int kv_dtype) {
+// Piece length for split_tokens = 0.  It depends on the shape only, never on
+// the batch.  Pieces trade parallelism (more workgroups for few, long
+// sequences) against the partial-result traffic and the merge launch; with
+// few KV heads a sequence feeds few workgroups, so its context is cut finer.
+//  - matrix-core kernel (verify, int8 cache): 512 positions per KV head,
+//    within [1024, 2048].
+//  - vector-ALU kernel: 64 positions per KV head, within [128, 512].
+int clamp_int(int x, int lo, int hi) { return x < lo ? lo : x > hi ? hi : x; }
+int default_split(int T, int q_heads, int kv_heads, int head_dim, int kv_dtype) {
   (void)q_heads;
-  (void)kv_heads;
   (void)head_dim;
-  (void)kv_dtype;
 #ifdef PA_DEFAULT_SPLIT
   return PA_DEFAULT_SPLIT;
 #else
-  return 512;
+  const int kv = kv_heads < 64 ? kv_heads : 64;
+  if (T > 1 || kv_dtype == PA_INT8) return clamp_int(512 * kv, 1024, 2048);
+  return clamp_int(64 * kv, 128, 512);
 #endif
 }
 
@@ -64,7 +72,7 @@ int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
   if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_INT8)
     return fail(PA_ERR_INVALID_ARG, "unknown kv dtype %d", kv_dtype);
-  int st = split_tokens == 0 ? default_split(q_heads, kv_heads, head_dim, kv_dtype) : split_tokens;
+  int st = split_tokens == 0 ? default_split(T, q_heads, kv_heads, head_dim, kv_dtype) : split_tokens;
   if (st <= 0 || st % pa::kBlockSizeHost != 0 || st > pa::kMaxSplitTokens)
     return fail(PA_ERR_INVALID_ARG, "split_tokens %d must be a multiple of %d in [%d, %d]",
                 split_tokens, pa::kBlockSizeHost, pa::kBlockSizeHost, pa::kMaxSplitTokens);
@@ -247,8 +255,9 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   return PA_OK;
 }
 
-int pa_default_split_tokens(int q_heads, int kv_heads, int head_dim, int kv_dtype) {
-  return default_split(q_heads, kv_heads, head_dim, kv_dtype);
+int pa_default_split_tokens(int num_query_tokens, int q_heads, int kv_heads, int head_dim,
+                            int kv_dtype) {
+  return default_split(num_query_tokens, q_heads, kv_heads, head_dim, kv_dtype);
 }
 
 size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv_heads,

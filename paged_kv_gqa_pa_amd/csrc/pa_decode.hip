@@ -19,22 +19,20 @@
 // With a single piece the workgroup writes the output row directly.  With
 // several pieces it writes a normalised partial output and its log2-sum-exp
 // to the workspace, and a merge pass combines the pieces of each row.  (A
-// merge inside this kernel by the last workgroup to arrive needs agent-scope
-// fences, which write back and invalidate the XCD's L2 and cost far more than
-// the second launch.)
+// merge inside this kernel by the last workgroup to arrive was measured: the
+// arrival counter, the write-through of the partials and their reads put
+// several microseconds on the tail, more than the second launch costs.)
 // Piece length is fixed per call (never derived from the lengths in the
 // batch), so each sequence's arithmetic depends on its own length only.
+//
+// This kernel serves fp32 and bf16 caches.  Over an int8 cache the per-key
+// conversions and products bind on the vector ALUs; that case runs on the
+// matrix cores (pa_verify.hip).
 #include <type_traits>
 
 #include "pa_device.h"
 #include "pa_kernels.h"
 
-#ifndef PA_I8_PB8_MIN_G
-#define PA_I8_PB8_MIN_G 5
-#endif
-#ifndef PA_I8_MINW
-#define PA_I8_MINW 1
-#endif
 #ifndef PA_PPL2_MAX_G
 #define PA_PPL2_MAX_G 4
 #endif
@@ -54,23 +52,15 @@ __device__ unsigned long long g_wtimes[8192 * 8];
 #endif
 namespace {
 
-// Byte k of x as a float; the backend selects v_cvt_f32_ubyte{k}.
-template <int k>
-__device__ __forceinline__ float ubyte_f32(uint32_t x) {
-  return float((x >> (8 * k)) & 0xFFu);
-}
-
-// Lane layout of a 16-token tile.  A lane's load unit is a piece of PB bytes
-// (16, or 8 for int8 with large groups, which keeps their per-lane q and
-// accumulators small).  A lane holds PPL pieces of one key row (E = PPL * EPL
-// elements): piece p covers dims p*D/PPL + c*EPL .. +EPL, with c = lane % LPK.
-// LPK lanes share a key row, a wave-wide load covers KPL rows, and load i
-// reads piece i % PPL of key rows (i / PPL) * KPL + lane / LPK.  Every
-// wave-wide load covers whole spans of 64 bytes or more of each row it touches.
+// Lane layout of a 16-token tile.  A lane's load unit is a 16-byte piece.  A
+// lane holds PPL pieces of one key row (E = PPL * EPL elements): piece p
+// covers dims p*D/PPL + c*EPL .. +EPL, with c = lane % LPK.  LPK lanes share
+// a key row, a wave-wide load covers KPL rows, and load i reads piece i % PPL
+// of key rows (i / PPL) * KPL + lane / LPK.  Every wave-wide load covers whole
+// spans of 128 bytes or more of each row it touches.
 template <typename KV, int D, int G>
 struct Geo {
-  static constexpr int PB = (__is_same(KV, i8_t) && G >= PA_I8_PB8_MIN_G) ? 8 : 16;  // bytes per piece
-  static constexpr int WPP = PB / 4;                  // 32-bit words per piece
+  static constexpr int PB = 16;                       // bytes per piece
   static constexpr int EPL = PB / int(sizeof(KV));    // elements per piece
   // Two pieces per lane halve the reduction steps per score but double the
   // per-lane accumulator; worth it for small bf16 groups only.
@@ -82,7 +72,6 @@ struct Geo {
   static constexpr int LPB = kBlockSize * ROWB / (kWave * PB);  // wave-wide loads per tile
   static constexpr int KR = LPB / PPL;                // key rows per lane per tile
   static constexpr int TILE_BYTES = kBlockSize * ROWB;
-  using Piece = typename PieceT<PB>::type;
   static_assert(LPK >= 1 && LPK <= kWave && KR * KPL == kBlockSize, "unsupported geometry");
   // Byte offset of load i for this lane (r = lane / LPK, c = lane % LPK).
   __device__ static int offset(int i, int r, int c) {
@@ -146,62 +135,7 @@ template <int D, int G> struct QRegs<bf16_t, bf16_t, D, G> {
   }
 };
 
-// bf16 q, int8 cache.  A code c becomes the fp16 number 1024 + u with
-// u = c + 128 (the biased byte): a byte permute puts u under the constant high
-// byte 0x64, which is exact.  Two products then take one v_dot2_f32_f16, with
-// q held as fp16 pairs (bf16 values are exact in fp16 within its normal range).
-// The bias comes off with the sum of this lane's (fp16-rounded) q:
-// sum q*(1152 + c) - 1152 * sum q = sum q*c.
-__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
-                                false);
-}
-
-template <int D, int G> struct QRegs<bf16_t, i8_t, D, G> {
-  static constexpr int PB = Geo<i8_t, D, G>::PB;  // codes (dims) per lane
-  static constexpr int WPP = PB / 4;
-  uint32_t qh[G][PB / 2];  // this lane's PB dims as fp16 pairs
-  float qsum[G];           // sum of those fp16 values
-  __device__ void load(const bf16_t* qrow, int c) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const bf16_t* p = qrow + size_t(h) * D + c * PB;
-      uint32_t w[PB / 2];
-#pragma unroll
-      for (int j = 0; j < PB / 8; ++j) {
-        const u32x4 v = load16(p + 8 * j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[4 * j + e] = v[e];
-      }
-      float s = 0.0f;
-#pragma unroll
-      for (int e = 0; e < PB / 2; ++e) {
-        const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e]), bf16_hi(w[e]));
-        qh[h][e] = __builtin_bit_cast(uint32_t, hp);
-        s += float(hp[0]) + float(hp[1]);
-      }
-      qsum[h] = s;
-    }
-  }
-  // The PB codes of one piece as fp16 pairs (1024 + u).
-  template <typename P>
-  __device__ static void pairs(const P& k, uint32_t (&kp)[PB / 2]) {
-#pragma unroll
-    for (int w = 0; w < WPP; ++w) {
-      const uint32_t u = k[w] ^ 0x80808080u;
-      kp[2 * w] = f16pair_lo(u);
-      kp[2 * w + 1] = f16pair_hi(u);
-    }
-  }
-  __device__ float dot_pairs(int h, const uint32_t (&kp)[PB / 2]) const {
-    float s = -kI8Bias * qsum[h];
-#pragma unroll
-    for (int e = 0; e < PB / 2; ++e) s = dot2h(qh[h][e], kp[e], s);
-    return s;
-  }
-};
-
-// V tile values of one load, widened to fp32 (int8: biased, see above).
+// V tile values of one load, widened to fp32.
 template <typename KV> struct VWiden;
 template <> struct VWiden<float> {
   static constexpr int EPL = 4;
@@ -220,20 +154,6 @@ template <> struct VWiden<bf16_t> {
     }
   }
 };
-template <> struct VWiden<i8_t> {
-  template <typename P, int N>
-  __device__ static void run(const P& v, float (&o)[N]) {
-#pragma unroll
-    for (int w = 0; w < N / 4; ++w) {
-      uint32_t x = v[w] ^ 0x80808080u;
-      o[4 * w + 0] = ubyte_f32<0>(x);
-      o[4 * w + 1] = ubyte_f32<1>(x);
-      o[4 * w + 2] = ubyte_f32<2>(x);
-      o[4 * w + 3] = ubyte_f32<3>(x);
-    }
-  }
-};
-
 template <typename T> __device__ __forceinline__ void store_out(T* p, float v);
 template <> __device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v) {
@@ -246,15 +166,11 @@ template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v
 // With 8 waves per workgroup, keep two workgroups per CU (4 waves per SIMD,
 // at most 128 VGPRs); with 4 the register budget is left to the compiler.
 template <typename Q, typename KV, int D, int G, int NW, int RING, bool APPEND>
-__global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV, i8_t) ? PA_I8_MINW : 1)) void decode_pass1(DecodeArgs a) {
+__global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode_pass1(DecodeArgs a) {
   using GE = Geo<KV, D, G>;
   constexpr int EPL = GE::EPL, PPL = GE::PPL, E = GE::E, LPK = GE::LPK, KPL = GE::KPL;
-  constexpr int LPB = GE::LPB, KR = GE::KR, WPP = GE::WPP;
-  using P = typename GE::Piece;
-  constexpr bool kInt8 = __is_same(KV, i8_t);
-  // int8 with two key rows per lane per tile: V goes through fp16 pairs.
-  constexpr bool kPairedV = kInt8 && KR % 2 == 0;
-  constexpr float kVBias = kPairedV ? kI8Bias : 128.0f;
+  constexpr int LPB = GE::LPB, KR = GE::KR;
+  using P = u32x4;
 
   // 1-D grid, piece-major: ids 0 .. N*Hkv-1 are piece 0 of every (sequence,
   // KV head), then piece 1, ...  Consecutive ids go to different XCDs, so the
@@ -275,10 +191,11 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
 
   // Issue the loads that do not depend on the context length first, so the
   // length, the block-table row and q arrive in one round trip: the piece's
-  // table entries (at most 64, one per lane; a tile's physical block is then
+  // table entries (spread over the lanes; a tile's physical block is then
   // read with readlane) and this group's query rows.
   const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
-  const int tab = blk_begin + lane < a.max_blocks_per_seq ? bt[blk_begin + lane] : 0;
+  PieceTable<kTabRegs> tab;
+  tab.load(bt, blk_begin, min(a.max_blocks_per_seq, blk_begin + split_blocks), lane);
   const Q* qrow = reinterpret_cast<const Q*>(a.q) + (size_t(b) * a.q_heads + size_t(g) * G) * D;
   QRegs<Q, KV, D, G> qr;
   qr.load(qrow, c);
@@ -327,14 +244,12 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
   const float sc_log2 = a.scale * kLog2e;
 
   float m[G], l[G], acc[G][E];
-  float corr[kInt8 ? G : 1];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = kNegInf;
     l[h] = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
-    if constexpr (kInt8) corr[h] = 0.0f;
   }
 
   // Out-of-range table entries are clamped into the pool (unspecified
@@ -345,23 +260,16 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
   // A fetch with live == false (past the wave's last tile) keeps the
   // instruction stream, and so the wait counts, identical but reads nothing:
   // its buffer resource has zero records.
-  auto fetch = [&](int blk, bool live, P (&kt)[LPB], P (&vt)[LPB], float& ks, float& vs) {
-    const int phys = min(max(__builtin_amdgcn_readlane(tab, blk - blk_begin), 0), a.num_blocks - 1);
+  auto fetch = [&](int blk, bool live, P (&kt)[LPB], P (&vt)[LPB]) {
+    const int phys = min(max(tab.at(blk - blk_begin), 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * GE::TILE_BYTES;
     const int bytes = live ? GE::TILE_BYTES : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + tile, bytes);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) kt[i] = PieceT<GE::PB>::load(kr, lane_off[i]);
+    for (int i = 0; i < LPB; ++i) kt[i] = buffer_load16_stream(kr, lane_off[i]);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) vt[i] = PieceT<GE::PB>::load(vr, lane_off[i]);
-    if constexpr (kInt8) {
-      ks = a.k_scale[head_blocks + phys];
-      vs = a.v_scale[head_blocks + phys];
-    } else {
-      ks = 1.0f;
-      vs = 1.0f;
-    }
+    for (int i = 0; i < LPB; ++i) vt[i] = buffer_load16_stream(vr, lane_off[i]);
   };
 
   // Reduce one tile.  MASK (only for a sequence's last, partial block) drops
@@ -375,7 +283,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
   // multiply per accumulator element) almost never runs.  The final
   // normalisation by the running sum makes the result independent of m.
   constexpr float kSlack = 8.0f;
-  auto process = [&](auto mask_tag, int blk, P (&kt)[LPB], P (&vt)[LPB], float ks, float vs) {
+  auto process = [&](auto mask_tag, int blk, P (&kt)[LPB], P (&vt)[LPB]) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK && APPEND) {
       // Position L - 1 is the token being appended: take its row from the input.
@@ -385,7 +293,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
 #pragma unroll
         for (int p = 0; p < PPL; ++p)
 #pragma unroll
-          for (int w = 0; w < WPP; ++w) {
+          for (int w = 0; w < 4; ++w) {
             kt[k * PPL + p][w] = is_new ? nk[p][w] : kt[k * PPL + p][w];
             vt[k * PPL + p][w] = is_new ? nv[p][w] : vt[k * PPL + p][w];
           }
@@ -393,22 +301,13 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
     }
     float s[G][KR];
 #pragma unroll
-    for (int k = 0; k < KR; ++k) {
-      if constexpr (kInt8) {
-        uint32_t kp[GE::PB / 2];
-        QRegs<Q, KV, D, G>::pairs(kt[k], kp);
+    for (int k = 0; k < KR; ++k)
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[h][k] = qr.dot_pairs(h, kp);
-      } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[h][k] = qr.dot_row(h, &kt[k * PPL]);
-      }
-    }
-    const float sc = kInt8 ? sc_log2 * ks : sc_log2;
+      for (int h = 0; h < G; ++h) s[h][k] = qr.dot_row(h, &kt[k * PPL]);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int k = 0; k < KR; ++k) s[h][k] = group_sum<LPK>(s[h][k]) * sc;
+      for (int k = 0; k < KR; ++k) s[h][k] = group_sum<LPK>(s[h][k]) * sc_log2;
     if constexpr (MASK) {
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
@@ -418,7 +317,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
 #pragma unroll
         for (int p = 0; p < PPL; ++p)
 #pragma unroll
-          for (int w = 0; w < WPP; ++w) vt[k * PPL + p][w] = valid ? vt[k * PPL + p][w] : 0u;
+          for (int w = 0; w < 4; ++w) vt[k * PPL + p][w] = valid ? vt[k * PPL + p][w] : 0u;
       }
     }
     bool grow = false;
@@ -436,41 +335,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
         const float alpha = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mnew);
         m[h] = mnew;
         l[h] *= alpha;
-        if constexpr (kInt8) corr[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
       }
-    }
-    if constexpr (kPairedV) {
-      // Key rows 2m and 2m+1 of this lane: dim e of both as one fp16 pair
-      // (1024 + u), weighted by (p_2m, p_2m+1) in one dot2; the bias is removed
-      // at the end.
-#pragma unroll
-      for (int mp = 0; mp < KR / 2; ++mp) {
-        uint32_t vp[4 * WPP];
-#pragma unroll
-        for (int w = 0; w < WPP; ++w) {
-          const uint32_t u0 = vt[2 * mp][w] ^ 0x80808080u, u1 = vt[2 * mp + 1][w] ^ 0x80808080u;
-          const uint32_t t01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
-          const uint32_t t23 = __builtin_amdgcn_perm(u1, u0, 0x07030602u);  // u0.b2 u1.b2 u0.b3 u1.b3
-          vp[4 * w + 0] = f16pair_lo(t01);
-          vp[4 * w + 1] = f16pair_hi(t01);
-          vp[4 * w + 2] = f16pair_lo(t23);
-          vp[4 * w + 3] = f16pair_hi(t23);
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float mref = m[h] == kNegInf ? 0.0f : m[h];
-          const float p0 = fast_exp2(s[h][2 * mp] - mref), p1 = fast_exp2(s[h][2 * mp + 1] - mref);
-          l[h] += p0 + p1;
-          const auto pp = __builtin_amdgcn_cvt_pkrtz(p0 * vs, p1 * vs);
-          corr[h] += float(pp[0]) + float(pp[1]);
-          const uint32_t pw = __builtin_bit_cast(uint32_t, pp);
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[h][e] = dot2h(pw, vp[e], acc[h][e]);
-        }
-      }
-      return;
     }
     float vf[KR][E];
 #pragma unroll
@@ -494,15 +361,6 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
         psum += pw[k];
       }
       l[h] += psum;
-      if constexpr (kInt8) {
-        float pv_sum = 0.0f;
-#pragma unroll
-        for (int k = 0; k < KR; ++k) {
-          pw[k] *= vs;
-          pv_sum += pw[k];
-        }
-        corr[h] += pv_sum;
-      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float x = acc[h][e];
@@ -533,16 +391,15 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
     const int n_plain = last_masked ? last : n_my;
     auto tile = [&](int j) { return first + min(j, last) * NW; };
     P kb[RING][LPB], vb[RING][LPB];
-    float ksb[RING], vsb[RING];
 #pragma unroll
-    for (int v = 0; v < RING - 1; ++v) fetch(tile(v), v <= last, kb[v], vb[v], ksb[v], vsb[v]);
+    for (int v = 0; v < RING - 1; ++v) fetch(tile(v), v <= last, kb[v], vb[v]);
     int j = 0;
     for (; j + RING - 1 < n_plain; j += RING) {
 #pragma unroll
       for (int v = 0; v < RING; ++v) {
         const int nb = (v + RING - 1) % RING;  // constant once unrolled
-        fetch(tile(j + v + RING - 1), j + v + RING - 1 <= last, kb[nb], vb[nb], ksb[nb], vsb[nb]);
-        process(Plain{}, tile(j + v), kb[v], vb[v], ksb[v], vsb[v]);
+        fetch(tile(j + v + RING - 1), j + v + RING - 1 <= last, kb[nb], vb[nb]);
+        process(Plain{}, tile(j + v), kb[v], vb[v]);
       }
     }
     // Fewer than RING plain tiles remain, then possibly the masked one; tiles
@@ -550,20 +407,13 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : (__is_same(KV,
 #pragma unroll
     for (int v = 0; v < RING; ++v) {
       if (j + v <= last) {
-        if (v == RING - 1) fetch(tile(j + v), true, kb[v], vb[v], ksb[v], vsb[v]);
+        if (v == RING - 1) fetch(tile(j + v), true, kb[v], vb[v]);
         if (j + v < n_plain)
-          process(Plain{}, tile(j + v), kb[v], vb[v], ksb[v], vsb[v]);
+          process(Plain{}, tile(j + v), kb[v], vb[v]);
         else
-          process(Masked{}, tile(j + v), kb[v], vb[v], ksb[v], vsb[v]);
+          process(Masked{}, tile(j + v), kb[v], vb[v]);
       }
     }
-  }
-
-  if constexpr (kInt8) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] = __builtin_fmaf(-kVBias, corr[h], acc[h][e]);
   }
 
   PA_WSTAMP(wave);
@@ -711,9 +561,6 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4
 #endif
-#ifndef PA_I8_RING
-#define PA_I8_RING 2
-#endif
 #ifndef PA_RING
 #define PA_RING 2
 #endif
@@ -721,15 +568,11 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
 template <typename Q, typename KV, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, bool append, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;      // waves per workgroup
-  // Tiles in flight per wave (ring buffers).  int8 kernels hold many
-  // registers (one wave per SIMD), so a deeper ring hides their latency.
-  constexpr int kRing = __is_same(KV, i8_t) ? (G <= 8 ? PA_I8_RING : 2) : PA_RING;
+  constexpr int kRing = PA_RING;           // tiles in flight per wave
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
-  if constexpr (!__is_same(KV, i8_t)) {
-    if (append) {
-      decode_pass1<Q, KV, D, G, NW, kRing, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
-      return hipGetLastError();
-    }
+  if (append) {
+    decode_pass1<Q, KV, D, G, NW, kRing, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    return hipGetLastError();
   }
   decode_pass1<Q, KV, D, G, NW, kRing, false><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
@@ -790,8 +633,6 @@ hipError_t launch_decode_pass1(const DecodeArgs& a, bool append, hipStream_t str
   if (a.q_dtype == kF32 && a.kv_dtype == kF32) return dispatch_dim<float, float>(a, G, append, stream);
   if (a.q_dtype == kBF16 && a.kv_dtype == kBF16)
     return dispatch_dim<bf16_t, bf16_t>(a, G, append, stream);
-  if (a.q_dtype == kBF16 && a.kv_dtype == kI8 && !append)
-    return dispatch_dim<bf16_t, i8_t>(a, G, false, stream);
   return hipErrorInvalidValue;
 }
 

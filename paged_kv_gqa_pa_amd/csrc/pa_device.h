@@ -112,6 +112,33 @@ __device__ __forceinline__ uint32_t f16pair_hi(uint32_t u) {  // bytes 2,3
 
 __device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// The block-table entries of one piece, held across the wave: entry i of the
+// piece sits in element i / 64 of lane i % 64 (a vector value, so it stays in
+// registers).  NREG elements cover 64 * NREG blocks.
+template <int NREG>
+struct PieceTable {
+  typedef int vec __attribute__((ext_vector_type(NREG)));
+  vec e;
+  // row: the sequence's table row; entries at or past `limit` are not read.
+  __device__ void load(const int32_t* row, int begin, int limit, int lane) {
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      const int j = begin + 64 * i + lane;
+      e[i] = j < limit ? row[j] : 0;
+    }
+  }
+  // Entry idx (the same idx in every lane of the wave).
+  __device__ int at(int idx) const {
+    int v = e[0];
+#pragma unroll
+    for (int i = 1; i < NREG; ++i) {
+      const int x = e[i];
+      v = (idx >> 6) == i ? x : v;
+    }
+    return __builtin_amdgcn_readlane(v, idx & 63);
+  }
+};
+
 // 16-byte streaming load (data read once: marked non-temporal).
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -131,21 +158,5 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ u32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, int offset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 2));
 }
-__device__ __forceinline__ u32x2 buffer_load8_stream(__amdgpu_buffer_rsrc_t r, int offset) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, offset, 0, 2));
-}
-
-// The unit of a lane's load: 16 bytes (u32x4) or 8 bytes (u32x2).
-template <int PB> struct PieceT;
-template <> struct PieceT<16> {
-  using type = u32x4;
-  static constexpr int W = 4;
-  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) { return buffer_load16_stream(r, off); }
-};
-template <> struct PieceT<8> {
-  using type = u32x2;
-  static constexpr int W = 2;
-  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) { return buffer_load8_stream(r, off); }
-};
 
 }  // namespace pa

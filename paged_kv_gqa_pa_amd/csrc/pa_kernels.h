@@ -9,7 +9,8 @@ namespace pa {
 enum DType : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
 
 constexpr int kBlockSizeHost = 16;  // tokens per cache block
-constexpr int kMaxSplitTokens = 1024;  // a piece's table entries fit one wave (64 lanes)
+constexpr int kMaxSplitTokens = 4096;  // a piece's table entries: kTabRegs per lane
+constexpr int kTabRegs = kMaxSplitTokens / (kBlockSizeHost * 64);
 
 struct CacheArgs {
   const void* key;

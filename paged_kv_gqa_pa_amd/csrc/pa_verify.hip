@@ -122,7 +122,8 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
 
   // Length-independent loads first: the piece's table entries and the query rows.
   const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
-  const int tab = blk_begin + lane < a.max_blocks_per_seq ? bt[blk_begin + lane] : 0;
+  PieceTable<kTabRegs> tab;
+  tab.load(bt, blk_begin, min(a.max_blocks_per_seq, blk_begin + split_blocks), lane);
   const int t_row = n / G;
   const int h_row = g * G + (n - t_row * G);
   // Query rows as the B operand of score product c: lane (row n, group grp)
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   // reads nothing (zero-record buffer resource), so the loop keeps one
   // instruction stream and one set of wait counts.
   auto fetch = [&](int blk, bool live, u32x4 (&kt)[NL], u32x4 (&vt)[NL], float& ks, float& vs) {
-    const int phys = min(max(__builtin_amdgcn_readlane(tab, blk - blk_begin), 0), a.num_blocks - 1);
+    const int phys = min(max(tab.at(blk - blk_begin), 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * TILE_BYTES;
     const int bytes = live ? TILE_BYTES : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);

@@ -31,16 +31,26 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_default_split():
-    assert pa.lib().pa_version() >= 100
-    st = pa.lib().pa_default_split_tokens(16, 8, 128, pa.PA_BF16)
-    assert st > 0 and st % 16 == 0
+    lib = pa.lib()
+    assert lib.pa_version() >= 100
+    # vector-ALU decode: 64 positions per KV head within [128, 512]
+    assert lib.pa_default_split_tokens(1, 16, 8, 128, pa.PA_BF16) == 512
+    assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_BF16) == 128
+    assert lib.pa_default_split_tokens(1, 2, 1, 64, pa.PA_F32) == 128
+    assert lib.pa_default_split_tokens(1, 64, 16, 128, pa.PA_BF16) == 512
+    # matrix-core kernel (verify, or an int8 cache): 512 per KV head within [1024, 2048]
+    assert lib.pa_default_split_tokens(5, 16, 8, 128, pa.PA_BF16) == 2048
+    assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_INT8) == 1024
+    assert lib.pa_default_split_tokens(2, 4, 1, 64, pa.PA_BF16) == 1024
+    # it never depends on the batch: the same for any num_seqs / lengths, by signature
 
 
 def test_workspace_size():
     lib = pa.lib()
-    st = lib.pa_default_split_tokens(12, 2, 128, pa.PA_INT8)
+    st = lib.pa_default_split_tokens(1, 16, 8, 128, pa.PA_BF16)
     # one piece covers the context: no workspace
     assert lib.pa_workspace_size(64, 1, 16, 8, 128, st, pa.PA_BF16, 0) == 0
+    assert lib.pa_workspace_size(64, 1, 16, 8, 128, st + 1, pa.PA_BF16, 0) > 0
     n = lib.pa_workspace_size(8, 1, 12, 2, 128, 32768, pa.PA_INT8, 512)
     pieces = 32768 // 512
     rows = 8 * 12
@@ -74,7 +84,7 @@ FAKE = 0x1000  # aligned non-null dummy address; never dereferenced on these pat
     (dict(D=96), pa.PA_ERR_UNSUPPORTED),
     (dict(bs=32), pa.PA_ERR_UNSUPPORTED),
     (dict(split=24), pa.PA_ERR_INVALID_ARG),
-    (dict(split=2048), pa.PA_ERR_INVALID_ARG),
+    (dict(split=4096 + 16), pa.PA_ERR_INVALID_ARG),
     (dict(ML=65), pa.PA_ERR_INVALID_ARG),
     (dict(qd=pa.PA_F32, kd=pa.PA_BF16), pa.PA_ERR_UNSUPPORTED),
     (dict(qd=7), pa.PA_ERR_INVALID_ARG),

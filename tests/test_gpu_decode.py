@@ -351,3 +351,17 @@ def test_decode_append_negative_slot_writes_nothing():
     case.v_cache = want_v
     want = _oracle_decode(case)
     assert np.abs(out[1].double().cpu().numpy() - want[1]).max() < TOL["bf16"]
+
+
+@pytest.mark.parametrize("tag,G", [("f32", 2), ("bf16", 6), ("int8", 6)])
+def test_long_pieces_span_several_table_registers(tag, G):
+    """A piece longer than 64 blocks reads its table entries from several lane registers."""
+    _say("long pieces", tag, "G", G)
+    rng = np.random.default_rng(77 + G)
+    lens = [1, 1000, 1025, 2048, 2049, 4096, 4097, 5000]
+    case = _random_case(rng, lens, Hkv=2, G=G, D=128, tag=tag)
+    dc = DevCase(case)
+    want = _oracle_decode(case)
+    for split in (1040, 2048, 4096, 0):
+        out = _decode(dc, split)
+        assert max_abs_err(out, want) < TOL[tag], (split, max_abs_err(out, want))
