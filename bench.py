@@ -10,8 +10,10 @@ every kernel from Python instead.
 
 Printed: one JSON line with tokens/s for the whole step (``value``), the decode
 kernel's achieved HBM bandwidth on algorithmic bytes against the 8 TB/s peak
-(``roofline``), and the CPU oracle timed on a bounded sample
-(``cpu_baseline``).
+(``roofline``), the CPU oracle timed on a bounded sample (``cpu_baseline``),
+and (``other_workloads``) the per-call time, bandwidth and roofline fraction
+of the other seeded workloads: the Qwen2-1.5B-shaped decode, the speculative
+verify and the long-context int8 decode.
 """
 from __future__ import annotations
 
@@ -43,6 +45,8 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 256 MiB device-to-device copy (known bytes) so hardware "
                         "byte counters can be scaled")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip the per-call timings of the other workloads")
     p.add_argument("--traffic-file", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "profiles", "pa_decode_batch64_traffic.json"))
     return p.parse_args()
@@ -56,6 +60,87 @@ def algorithmic_bytes(lens, q_heads, kv_heads, head_dim, elem=2):
     qo = len(lens) * q_heads * head_dim * elem * 2
     tables = int(((lens + 15) // 16).sum()) * 4 + len(lens) * 4
     return kv + qo + tables
+
+
+def attention_bytes(lens, T, q_heads, kv_heads, head_dim, kv_elem, q_elem=2):
+    """Algorithmic bytes of one pa_decode / pa_verify call: K and V of exactly L_b
+    positions per (sequence, KV head), q in and out, the used table entries, the
+    lengths, and for an int8 cache the two fp32 scales of each used block."""
+    lens = np.asarray(lens, np.int64)
+    blocks = int(((lens + 15) // 16).sum())
+    kv = int(lens.sum()) * kv_heads * head_dim * kv_elem * 2
+    qo = len(lens) * T * q_heads * head_dim * q_elem * 2
+    scales = blocks * kv_heads * 8 if kv_elem == 1 else 0
+    return kv + qo + blocks * 4 + len(lens) * 4 + scales
+
+
+def other_workloads(torch, pa, wl, dev, reps=10):
+    """Per-call timings of the other seeded workloads.  Each call reads its own
+    replica of the caches (enough replicas to pass 1 GB per round, far beyond the
+    256 MB last-level cache), launched from one HIP graph; events on the launch
+    stream.  Cache contents are random (the timing does not depend on them); the
+    lengths and block tables are the seeded ones."""
+    out = {}
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "int8": torch.int8}
+    for name in ("qwen2_1p5b_bf16", "spec_verify_bf16", "long_ctx_int8"):
+        spec = wl.CONFIGS[name]
+        lens, table = wl.structure(spec)
+        N, T, Hq, Hkv, D, NB = (spec.num_seqs, spec.num_query_tokens, spec.q_heads,
+                                spec.kv_heads, spec.head_dim, spec.num_blocks)
+        kdt = tdt[spec.kv_dtype]
+        elem = {torch.bfloat16: 2, torch.float32: 4, torch.int8: 1}[kdt]
+        cache_bytes = Hkv * NB * 16 * D * elem
+        R = max(1, min(64, int(np.ceil(1.0e9 / (2 * cache_bytes)))))
+
+        def mk():
+            if kdt == torch.int8:
+                return torch.randint(-127, 128, (Hkv, NB, 16, D), device=dev, dtype=torch.int8)
+            return torch.randn((Hkv, NB, 16, D), device=dev, dtype=kdt)
+        kc = [mk() for _ in range(R)]
+        vc = [mk() for _ in range(R)]
+        ks = vs = None
+        if kdt == torch.int8:
+            ks = torch.rand((Hkv, NB), device=dev) * 0.02 + 0.01
+            vs = torch.rand((Hkv, NB), device=dev) * 0.02 + 0.01
+        bt = torch.from_numpy(table).to(dev)
+        cl = torch.from_numpy(lens).to(dev)
+        q = torch.randn((N, T, Hq, D) if T > 1 else (N, Hq, D), device=dev, dtype=torch.bfloat16)
+        o = torch.empty_like(q)
+        split = pa.default_split_tokens(Hq, Hkv, D, kdt, num_query_tokens=T)
+        wsb = pa.workspace_size(N, T, Hq, Hkv, D, spec.max_len, kdt, split)
+        ws = torch.zeros(max(256, wsb), dtype=torch.uint8, device=dev)
+        fn = pa.verify if T > 1 else pa.decode
+
+        def calls():
+            for r in range(R):
+                fn(o, q, kc[r], vc[r], bt, cl, 1.0 / float(np.sqrt(D)), spec.max_len, ks, vs,
+                   split_tokens=split, workspace=ws)
+        calls()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+        alg = attention_bytes(lens, T, Hq, Hkv, D, elem)
+        gbps = alg / (us * 1e-6) / 1e9
+        out[name] = {"us_per_call": round(us, 2), "algorithmic_bytes": alg,
+                     "hbm_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "query_tokens_per_s": round(N * T / (us * 1e-6), 1),
+                     "split_tokens": split, "kernel": "rows_pass1" if (T > 1 or elem == 1) else "decode_pass1",
+                     "shape": f"N={N} T={T} Hq={Hq} Hkv={Hkv} D={D} kv={spec.kv_dtype}"}
+        print(f"[bench] {name}: {us:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}%)",
+              flush=True)
+        del kc, vc, g
+        torch.cuda.empty_cache()
+    return out
 
 
 def cache_write_bytes(num_tokens, kv_heads, head_dim, elem=2):
@@ -281,6 +366,8 @@ def main():
                      "traffic": traffic, "kernel": "decode_pass1",
                      "us_per_launch": round(us_decode, 3), "algorithmic_bytes_per_launch": bytes_launch},
     }
+    if not args.no_other_workloads:
+        res["other_workloads"] = other_workloads(torch, pa, wl, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline ...", flush=True)
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

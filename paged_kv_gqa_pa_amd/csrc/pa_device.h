@@ -129,6 +129,7 @@ struct PieceTable {
   }
   // Entry idx (the same idx in every lane of the wave).
   __device__ int at(int idx) const {
+    if (idx < 64) return __builtin_amdgcn_readlane(e[0], idx);
     int v = e[0];
 #pragma unroll
     for (int i = 1; i < NREG; ++i) {
