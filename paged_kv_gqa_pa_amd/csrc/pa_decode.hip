@@ -526,31 +526,44 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const float* lse = a.part_lse + size_t(row) * a.max_pieces;
   const float* po = a.part_o + size_t(row) * a.max_pieces * D;
-  // Each lane reads some of the row's log2-sum-exps; the maximum and the
-  // weights are shared through wave reductions.
-  float M = kNegInf;
-  for (int s = lane; s < n_pieces; s += 64) M = fmaxf(M, lse[s]);
-  M = stride_max<1>(M);
+  // Pieces are taken CH at a time with every load of the chunk in flight at
+  // once: lane u reads piece s0 + u's log2-sum-exp, every lane reads its dims
+  // of all CH partial outputs.  Chunks combine in piece order with a running
+  // maximum.  CH is 8 for calls of up to 8 pieces, else 32.
   constexpr int PER = D / 64;
-  constexpr int BATCH = 8;  // pieces whose loads are in flight together
+  float M = kNegInf, wsum = 0.0f;
   float o[PER] = {};
-  float wsum = 0.0f;
-  for (int s0 = 0; s0 < n_pieces; s0 += BATCH) {
-    float ls[BATCH], ov[BATCH][PER];
+  auto chunk = [&](auto ch_tag, int s0) {
+    constexpr int CH = decltype(ch_tag)::value;
+    const int cnt = min(CH, n_pieces - s0);
+    const float my_lse = lane < cnt ? lse[s0 + lane] : kNegInf;
+    float ov[CH][PER];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int sp = min(s0 + u, n_pieces - 1);
-      ls[u] = s0 + u < n_pieces ? lse[sp] : kNegInf;
+    for (int u = 0; u < CH; ++u) {
+      const int sp = s0 + min(u, cnt - 1);
 #pragma unroll
       for (int j = 0; j < PER; ++j) ov[u][j] = po[size_t(sp) * D + j * 64 + lane];
     }
+    const float cm = fmaxf(M, stride_max<1>(my_lse));
+    if (cm == kNegInf) return;
+    const float f = M == kNegInf ? 0.0f : fast_exp2(M - cm);
+    M = cm;
+    wsum *= f;
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const float w = ls[u] == kNegInf ? 0.0f : fast_exp2(ls[u] - M);
+    for (int j = 0; j < PER; ++j) o[j] *= f;
+    const float w_lane = my_lse == kNegInf ? 0.0f : fast_exp2(my_lse - M);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), u));
       wsum += w;
 #pragma unroll
       for (int j = 0; j < PER; ++j) o[j] = __builtin_fmaf(w, ov[u][j], o[j]);
     }
+  };
+  if (n_pieces <= 8) {
+    chunk(std::integral_constant<int, 8>{}, 0);
+  } else {
+    for (int s0 = 0; s0 < n_pieces; s0 += 32) chunk(std::integral_constant<int, 32>{}, s0);
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
 #pragma unroll
