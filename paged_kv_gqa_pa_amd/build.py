@@ -52,7 +52,8 @@ def build(verbose: bool = True, extra_flags=()) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    # --no-undefined: a kernel whose host stub was not emitted fails here, not at load time.
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")

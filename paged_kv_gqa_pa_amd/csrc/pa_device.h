@@ -28,10 +28,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // v_cvt_pk_bf16_f32
 }
 
 // Exchange across 16-lane rows without LDS: permlane16_swap of a value with
@@ -158,6 +155,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // 16-byte buffer load, non-temporal (the data is read once).
 __device__ __forceinline__ u32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, int offset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 2));
+}
+// 16 bytes per lane from a buffer straight into LDS, non-temporal: lane i's
+// bytes land at lds + 16 i (lds is the same in every lane).
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, int offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds, 16, offset, 0, 0, 2);
 }
 
 }  // namespace pa

@@ -30,6 +30,8 @@
 // Row t*G + i is query token t of head g*G + i; token t sees positions
 // 0 .. L - T + t.  Pieces, workspace partials and the merge pass are shared
 // with the vector-ALU decode kernel (rows_per_seq = T * q_heads).
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -94,13 +96,18 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   constexpr int NQ = D / 32;                 // score products per tile
   constexpr int NT = D / 16;                 // output blocks of 16 dims
   constexpr int TILE_BYTES = kBlockSize * ROWB;
-  // Per-wave LDS: the staged K and V tiles (row pitches padded so the reads
-  // below hit distinct banks), reused for the wave's O rows after its loop.
-  constexpr int KPB = ROWB + 16;
-  constexpr int VPB = kInt8 ? ROWB + 16 : ROWB + 8;
-  constexpr int STAGE = kBlockSize * (KPB + VPB);
-  constexpr int OBYTES = kRows * D * 4;
-  constexpr int WBYTES = STAGE > OBYTES ? STAGE : OBYTES;
+  // Per-wave LDS: a ring of two staged (K, V) tile pairs, written by the load
+  // units directly (no registers), reused for the wave's O rows after its
+  // loop.  Within a staged K tile (and an int8 V tile), 16-byte chunk k of key
+  // row r sits at position k ^ ((r / RPB) mod CPR) of its row (RPB rows share
+  // one 256-byte bank period), so that the operand reads below hit distinct
+  // banks.  A bf16 V tile stays in row order: its transposed reads then take
+  // one base address and immediate offsets (at a 4-way bank conflict).
+  constexpr int CPR = ROWB / 16;             // 16-byte chunks per key row
+  constexpr int RPB = ROWB >= 256 ? 1 : 256 / ROWB;
+  constexpr int SLOT = 2 * TILE_BYTES;       // one (K, V) tile pair
+  constexpr int OHALF = kRows / 2 * D * 4;   // O rows of one half
+  constexpr int WBYTES = SLOT > OHALF ? SLOT : OHALF;
   using M = MOps<KV>;
 
   const int pairs = a.num_seqs * a.kv_heads;
@@ -163,10 +170,23 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
   const float sc = a.scale * kLog2e;
 
-  __shared__ __attribute__((aligned(16))) char s_raw[NW * WBYTES];
-  __shared__ float s_m[NW][kRows], s_l[NW][kRows];
-  char* const s_k = s_raw + wave * WBYTES;
-  char* const s_v = s_k + kBlockSize * KPB;
+  // The two ring slots are separate LDS objects, so the compiler's wait for a
+  // slot's direct-to-LDS loads does not also wait for the other slot's.
+  __shared__ __attribute__((aligned(16))) char s_ring0[NW * WBYTES];
+  __shared__ __attribute__((aligned(16))) char s_ring1[NW * WBYTES];
+  // Each wave's row maxima and sums: in its slot-1 region behind its O rows
+  // when there is room (keeps a bf16, D = 128 workgroup within 64 KiB).
+  constexpr bool kMLInRing = WBYTES - OHALF >= 2 * kRows * 4;
+  __shared__ float s_ml_own[kMLInRing ? 1 : NW][2][kRows];
+  auto ml_of = [&](int w) {
+    return kMLInRing ? reinterpret_cast<float*>(s_ring1 + w * WBYTES + OHALF) : &s_ml_own[w][0][0];
+  };
+  char* const s_w0 = s_ring0 + wave * WBYTES;
+  char* const s_w1 = s_ring1 + wave * WBYTES;
+  auto kbuf = [&](int slot) { return slot ? s_w1 : s_w0; };
+  auto vbuf = [&](int slot) { return (slot ? s_w1 : s_w0) + TILE_BYTES; };
+  // Byte offset inside a staged tile of chunk k of key row r.
+  auto sw = [](int r, int k) { return r * ROWB + 16 * (k ^ ((r / RPB) & (CPR - 1))); };
 
   // Identity as the B operand of the int8 V transposes: lane l holds I[4*grp + j][n].
   u32x2 ident;
@@ -184,19 +204,32 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Tiles are read as contiguous 1 KiB wave loads.  A fetch with live == false
-  // reads nothing (zero-record buffer resource), so the loop keeps one
-  // instruction stream and one set of wait counts.
-  auto fetch = [&](int blk, bool live, u32x4 (&kt)[NL], u32x4 (&vt)[NL], float& ks, float& vs) {
+  // Tiles are loaded straight into the wave's LDS ring: load c of a tile
+  // fills 1 KiB of LDS, lane i writing 16 bytes at i * 16; the lane fetches
+  // the cache chunk that belongs at that position, so every load still reads
+  // whole 128-byte lines of the tile.  A fetch with live == false reads
+  // nothing (zero-record buffer resource), so the loop keeps one instruction
+  // stream and one set of wait counts.
+  int src_off[NL];
+#pragma unroll
+  for (int c = 0; c < NL; ++c) {
+    const int slot = 64 * c + lane;          // destination 16-byte slot
+    const int r = slot / CPR, p = slot % CPR;
+    src_off[c] = r * ROWB + 16 * (p ^ ((r / RPB) & (CPR - 1)));
+  }
+  constexpr bool kSwizzleV = kInt8;
+  auto fetch = [&](int blk, bool live, int slot, float& ks, float& vs) {
     const int phys = min(max(tab.at(blk - blk_begin), 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * TILE_BYTES;
     const int bytes = live ? TILE_BYTES : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + tile, bytes);
 #pragma unroll
-    for (int c = 0; c < NL; ++c) kt[c] = buffer_load16_stream(kr, c * 1024 + lane * 16);
+    for (int c = 0; c < NL; ++c)
+      buffer_load16_to_lds(kr, kbuf(slot) + 1024 * c, src_off[c]);
 #pragma unroll
-    for (int c = 0; c < NL; ++c) vt[c] = buffer_load16_stream(vr, c * 1024 + lane * 16);
+    for (int c = 0; c < NL; ++c)
+      buffer_load16_to_lds(vr, vbuf(slot) + 1024 * c, kSwizzleV ? src_off[c] : 1024 * c + 16 * lane);
     if constexpr (kInt8) {
       ks = a.k_scale[head_blocks + phys];
       vs = a.v_scale[head_blocks + phys];
@@ -205,6 +238,8 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
       vs = 1.0f;
     }
   };
+  // Loads a fetch issues (tile chunks, then the two int8 scales).
+  constexpr int kFetchLoads = 2 * NL + (kInt8 ? 2 : 0);
 
   // Delayed rescaling: m is a reference maximum; weights are exp2(s - m), and
   // O and the sum are rescaled only when a row's tile maximum exceeds its
@@ -212,23 +247,26 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   // and the rescale almost never runs.  The final division by the sum makes
   // the result independent of the reference.
   constexpr float kSlack = 8.0f;
-  auto process = [&](int blk, u32x4 (&kt)[NL], u32x4 (&vt)[NL], float ks, float vs) {
-    // Stage the tile.  bf16 key rows past the context may hold anything, even
-    // NaN: their V rows are cleared (a zero weight must meet a finite value);
-    // their scores are replaced, not multiplied, below.
-    const bool tail = (blk + 1) * kBlockSize > L;
+  // PENDING: loads issued after this tile's fetch that may still be in flight.
+  auto process = [&](auto pending_tag, int blk, int slot, float ks, float vs) {
+    constexpr int PENDING = decltype(pending_tag)::value;
+    // The tile's LDS writes are counted with the vector-memory loads.
+    __builtin_amdgcn_s_waitcnt((PENDING & 15) | ((PENDING >> 4) << 14) | (7 << 4) | (15 << 8));
+    __asm__ __volatile__("" ::: "memory");
+    const char* const sk = kbuf(slot);
+    char* const sv = vbuf(slot);
+    // bf16 key rows past the context may hold anything, even NaN: their V rows
+    // are cleared (a zero weight must meet a finite value); their scores are
+    // replaced, not multiplied, below.
+    if constexpr (!kInt8) {
+      if ((blk + 1) * kBlockSize > L) {
 #pragma unroll
-    for (int c = 0; c < NL; ++c) {
-      const int byte = c * 1024 + lane * 16;
-      const int key = byte / ROWB, col = byte % ROWB;
-      *reinterpret_cast<u32x4*>(s_k + key * KPB + col) = kt[c];
-      u32x4 v = vt[c];
-      if constexpr (!kInt8) {
-        if (tail && blk * kBlockSize + key >= L) v = u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < NL; ++c) {
+          const int key = (64 * c + lane) / CPR;
+          if (blk * kBlockSize + key >= L)
+            *reinterpret_cast<u32x4*>(sv + 1024 * c + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        }
       }
-      uint2* dst = reinterpret_cast<uint2*>(s_v + key * VPB + col);
-      dst[0] = uint2{v[0], v[1]};
-      dst[1] = uint2{v[2], v[3]};
     }
     // Scores of keys 4*grp .. 4*grp+3 for row n: product c takes key n's dims
     // 32c + 8grp .. +7 as the A operand.
@@ -237,10 +275,11 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
     for (int c = 0; c < NQ; ++c) {
       u32x4 kop;
       if constexpr (kInt8) {
-        const uint2 w = *reinterpret_cast<const uint2*>(s_k + n * KPB + 32 * c + 8 * grp);
+        const int k = (32 * c + 8 * grp) / 16;
+        const uint2 w = *reinterpret_cast<const uint2*>(sk + sw(n, k) + 8 * (grp & 1));
         kop = codes8_f16(w.x, w.y);
       } else {
-        kop = *reinterpret_cast<const u32x4*>(s_k + n * KPB + 64 * c + 16 * grp);
+        kop = *reinterpret_cast<const u32x4*>(sk + sw(n, 4 * c + grp));
       }
       s = M::qk(kop, qb[c], s);
     }
@@ -280,65 +319,74 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
       u32x2 vb;
       if constexpr (kInt8) {
         // key n's codes of dims 16t + 4grp .. +3, turned by the identity product
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(s_v + n * VPB + 16 * t + 4 * grp) ^
-                           0x80808080u;
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(sv + sw(n, t) + 4 * grp) ^ 0x80808080u;
         const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
         vb = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
       } else {
         // transposed reads: four keys of one dim
-        const uint16_t* col = reinterpret_cast<const uint16_t*>(s_v) + 16 * t + n;
+        const uint16_t* col = reinterpret_cast<const uint16_t*>(sv) + 4 * grp * D + 16 * t + n;
         uint32_t e[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) e[j] = col[(4 * grp + j) * (VPB / 2)];
+        for (int j = 0; j < 4; ++j) e[j] = col[j * D];
         vb = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
       }
       o[t] = M::mm16(pa, vb, o[t]);
     }
+    // This slot is loaded again next: its reads must be done first.
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
   };
 
+  using Pend = std::integral_constant<int, kFetchLoads>;
+  using Pend0 = std::integral_constant<int, 0>;
   const int first = blk_begin + wave;
   const int n_my = first < blk_end ? cdiv(blk_end - first, NW) : 0;
   if (n_my > 0) {
     const int last = n_my - 1;
-    u32x4 k0[NL], v0[NL], k1[NL], v1[NL];
     float ks0, vs0, ks1, vs1;
-    fetch(first, true, k0, v0, ks0, vs0);
+    fetch(first, true, 0, ks0, vs0);
     int j = 0;
     for (; j + 1 <= last; j += 2) {
-      fetch(first + (j + 1) * NW, true, k1, v1, ks1, vs1);
-      process(first + j * NW, k0, v0, ks0, vs0);
-      fetch(first + min(j + 2, last) * NW, j + 2 <= last, k0, v0, ks0, vs0);
-      process(first + (j + 1) * NW, k1, v1, ks1, vs1);
+      fetch(first + (j + 1) * NW, true, 1, ks1, vs1);
+      process(Pend{}, first + j * NW, 0, ks0, vs0);
+      fetch(first + min(j + 2, last) * NW, j + 2 <= last, 0, ks0, vs0);
+      process(Pend{}, first + (j + 1) * NW, 1, ks1, vs1);
     }
-    if (j == last) process(first + j * NW, k0, v0, ks0, vs0);
+    if (j == last) process(Pend0{}, first + j * NW, 0, ks0, vs0);
   }
+  // The last prefetch (reading nothing) may still be writing its LDS slot:
+  // wait for it before the slots are reused below.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  __asm__ __volatile__("" ::: "memory");
 
   // Row totals (the four key quads of each row); the wave's O rows go to its
   // own LDS region (its staging buffers are no longer read), then the waves
   // are merged.
   const float lrow = add_xor32(add_xor16(lsum));
   if (grp == 0) {
-    s_m[wave][n] = m;
-    s_l[wave][n] = lrow;
+    ml_of(wave)[n] = m;
+    ml_of(wave)[kRows + n] = lrow;
   }
-  float* const s_ow = reinterpret_cast<float*>(s_k);
+  // O rows 0-7 go to the wave's slot-0 region, rows 8-15 to its slot-1 region.
+  float* const s_ow = reinterpret_cast<float*>(grp < 2 ? s_w0 : s_w1);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s_ow[(4 * grp + j) * D + 16 * t + n] = o[t][j];
+    for (int j = 0; j < 4; ++j) s_ow[(4 * (grp & 1) + j) * D + 16 * t + n] = o[t][j];
   __syncthreads();
 
   for (int t = threadIdx.x; t < R * D; t += NW * kWave) {
     const int row = t / D, d = t % D;
-    float mx = s_m[0][row];
+    float mx = ml_of(0)[row];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_m[w][row]);
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, ml_of(w)[row]);
     float lt = 0.0f, ot = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = s_m[w][row] == kNegInf ? 0.0f : fast_exp2(s_m[w][row] - mx);
-      lt = __builtin_fmaf(s_l[w][row], f, lt);
-      ot = __builtin_fmaf(reinterpret_cast<const float*>(s_raw + w * WBYTES)[row * D + d], f, ot);
+      const float mw = ml_of(w)[row];
+      const float f = mw == kNegInf ? 0.0f : fast_exp2(mw - mx);
+      lt = __builtin_fmaf(ml_of(w)[kRows + row], f, lt);
+      const char* rb = (row < kRows / 2 ? s_ring0 : s_ring1) + w * WBYTES;
+      ot = __builtin_fmaf(reinterpret_cast<const float*>(rb)[(row % (kRows / 2)) * D + d], f, ot);
     }
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int tq = row / G;
