@@ -117,8 +117,9 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  *
  * pa_default_split_tokens returns the piece length used when a call passes
  * split_tokens = 0 (num_query_tokens is 1 for pa_decode): 512 * kv_heads
- * clamped to [1024, 2048] for calls that run on the matrix cores (pa_verify,
- * and pa_decode over an int8 cache), else 64 * kv_heads clamped to [128, 512].
+ * clamped to [1024, 2048] for calls that run on the matrix cores (pa_verify;
+ * pa_decode over an int8 cache or with bf16 groups of 4 or more query heads
+ * per KV head), else 64 * kv_heads clamped to [128, 512].
  */
 int pa_default_split_tokens(int num_query_tokens, int q_heads, int kv_heads, int head_dim,
                             int kv_dtype);
@@ -169,7 +170,9 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 
 /*
  * pa_decode_append -- pa_reshape_and_cache of one new token per sequence
- * followed by pa_decode, in one launch.
+ * followed by pa_decode, in one launch where pa_decode runs on the vector
+ * ALUs (fp32, bf16 groups below 4 query heads per KV head); elsewhere the
+ * cache-write launch and then the matrix-core decode, with pa_decode's result.
  *
  * key, value     [num_seqs, kv_heads, head_dim], kv_dtype: the new token of
  *                each sequence, written to slot_mapping[b] (skipped when

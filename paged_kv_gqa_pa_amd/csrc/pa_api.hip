@@ -37,22 +37,29 @@ struct Plan {
   size_t total() const { return max_pieces > 1 ? o_bytes + lse_bytes : 0; }
 };
 
+// Which kernel serves a call.  The matrix cores take every verify call and
+// every int8 cache; a bf16 decode call goes there too from groups of 4 query
+// heads up (measured: at G = 2 the vector-ALU kernel is ~5 % faster, at G = 6
+// the matrix-core one ~15 %).  fp32 decode stays on the vector ALUs.
+bool rows_kernel(int T, int G, int kv_dtype) {
+  return T > 1 || kv_dtype == PA_INT8 || (kv_dtype == PA_BF16 && G >= 4);
+}
+
 // Piece length for split_tokens = 0.  It depends on the shape only, never on
 // the batch.  Pieces trade parallelism (more workgroups for few, long
 // sequences) against the partial-result traffic and the merge launch; with
 // few KV heads a sequence feeds few workgroups, so its context is cut finer.
-//  - matrix-core kernel (verify, int8 cache): 512 positions per KV head,
-//    within [1024, 2048].
+//  - matrix-core kernel: 512 positions per KV head, within [1024, 2048].
 //  - vector-ALU kernel: 64 positions per KV head, within [128, 512].
 int clamp_int(int x, int lo, int hi) { return x < lo ? lo : x > hi ? hi : x; }
 int default_split(int T, int q_heads, int kv_heads, int head_dim, int kv_dtype) {
-  (void)q_heads;
   (void)head_dim;
 #ifdef PA_DEFAULT_SPLIT
   return PA_DEFAULT_SPLIT;
 #else
   const int kv = kv_heads < 64 ? kv_heads : 64;
-  if (T > 1 || kv_dtype == PA_INT8) return clamp_int(512 * kv, 1024, 2048);
+  const int G = kv_heads > 0 ? q_heads / kv_heads : 1;
+  if (rows_kernel(T, G, kv_dtype)) return clamp_int(512 * kv, 1024, 2048);
   return clamp_int(64 * kv, 128, 512);
 #endif
 }
@@ -196,8 +203,18 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.new_v = app.value;
   a.slot_mapping = app.slot_mapping;
   // Verify calls, and decode over an int8 cache, run on the matrix cores.
-  const bool rows = is_verify || kv_dtype == PA_INT8;
-  hipError_t e = rows ? pa::launch_rows_pass1(a, s) : pa::launch_decode_pass1(a, app.on, s);
+  const bool rows = rows_kernel(T, G, kv_dtype);
+  hipError_t e = hipSuccess;
+  if (rows && app.on) {
+    // The matrix-core kernel has no fused write: the cache write runs first,
+    // then the same decode as pa_decode (identical results).
+    pa::CacheArgs c{app.key, app.value, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                    app.slot_mapping, num_seqs, kv_heads, num_blocks,
+                    head_dim * elem_size(kv_dtype)};
+    e = pa::launch_reshape_and_cache(c, s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
+  }
+  e = rows ? pa::launch_rows_pass1(a, s) : pa::launch_decode_pass1(a, app.on, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pass-1 launch failed: %s", hipGetErrorString(e));
   if (plan.max_pieces > 1) {
     pa::MergeArgs m{};

@@ -33,14 +33,15 @@ def test_library_exports_every_declared_function():
 def test_version_and_default_split():
     lib = pa.lib()
     assert lib.pa_version() >= 100
-    # vector-ALU decode: 64 positions per KV head within [128, 512]
+    # vector-ALU decode (fp32, bf16 groups below 4): 64 positions per KV head within [128, 512]
     assert lib.pa_default_split_tokens(1, 16, 8, 128, pa.PA_BF16) == 512
-    assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_BF16) == 128
+    assert lib.pa_default_split_tokens(1, 6, 2, 128, pa.PA_BF16) == 128
     assert lib.pa_default_split_tokens(1, 2, 1, 64, pa.PA_F32) == 128
-    assert lib.pa_default_split_tokens(1, 64, 16, 128, pa.PA_BF16) == 512
-    # matrix-core kernel (verify, or an int8 cache): 512 per KV head within [1024, 2048]
+    assert lib.pa_default_split_tokens(1, 96, 16, 128, pa.PA_F32) == 512
+    # matrix-core kernel (verify, int8, bf16 groups of 4+): 512 per KV head within [1024, 2048]
     assert lib.pa_default_split_tokens(5, 16, 8, 128, pa.PA_BF16) == 2048
     assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_INT8) == 1024
+    assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_BF16) == 1024
     assert lib.pa_default_split_tokens(2, 4, 1, 64, pa.PA_BF16) == 1024
     # it never depends on the batch: the same for any num_seqs / lengths, by signature
 
