@@ -116,8 +116,8 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  * sequence's result does not depend on what it is batched with.
  *
  * pa_default_split_tokens returns the piece length used when a call passes
- * split_tokens = 0 (num_query_tokens is 1 for pa_decode): 512 * kv_heads
- * clamped to [1024, 2048] for calls that run on the matrix cores (pa_verify;
+ * split_tokens = 0 (num_query_tokens is 1 for pa_decode): 1024 * kv_heads
+ * clamped to [2048, 4096] for calls that run on the matrix cores (pa_verify;
  * pa_decode over an int8 cache or with bf16 groups of 4 or more query heads
  * per KV head), else 64 * kv_heads clamped to [128, 512].
  */

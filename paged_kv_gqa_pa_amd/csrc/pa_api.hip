@@ -49,7 +49,7 @@ bool rows_kernel(int T, int G, int kv_dtype) {
 // the batch.  Pieces trade parallelism (more workgroups for few, long
 // sequences) against the partial-result traffic and the merge launch; with
 // few KV heads a sequence feeds few workgroups, so its context is cut finer.
-//  - matrix-core kernel: 512 positions per KV head, within [1024, 2048].
+//  - matrix-core kernel: 1024 positions per KV head, within [2048, 4096].
 //  - vector-ALU kernel: 64 positions per KV head, within [128, 512].
 int clamp_int(int x, int lo, int hi) { return x < lo ? lo : x > hi ? hi : x; }
 int default_split(int T, int q_heads, int kv_heads, int head_dim, int kv_dtype) {
@@ -59,7 +59,7 @@ int default_split(int T, int q_heads, int kv_heads, int head_dim, int kv_dtype) 
 #else
   const int kv = kv_heads < 64 ? kv_heads : 64;
   const int G = kv_heads > 0 ? q_heads / kv_heads : 1;
-  if (rows_kernel(T, G, kv_dtype)) return clamp_int(512 * kv, 1024, 2048);
+  if (rows_kernel(T, G, kv_dtype)) return clamp_int(1024 * kv, 2048, 4096);
   return clamp_int(64 * kv, 128, 512);
 #endif
 }

@@ -38,11 +38,11 @@ def test_version_and_default_split():
     assert lib.pa_default_split_tokens(1, 6, 2, 128, pa.PA_BF16) == 128
     assert lib.pa_default_split_tokens(1, 2, 1, 64, pa.PA_F32) == 128
     assert lib.pa_default_split_tokens(1, 96, 16, 128, pa.PA_F32) == 512
-    # matrix-core kernel (verify, int8, bf16 groups of 4+): 512 per KV head within [1024, 2048]
-    assert lib.pa_default_split_tokens(5, 16, 8, 128, pa.PA_BF16) == 2048
-    assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_INT8) == 1024
-    assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_BF16) == 1024
-    assert lib.pa_default_split_tokens(2, 4, 1, 64, pa.PA_BF16) == 1024
+    # matrix-core kernel (verify, int8, bf16 groups of 4+): 1024 per KV head within [2048, 4096]
+    assert lib.pa_default_split_tokens(5, 16, 8, 128, pa.PA_BF16) == 4096
+    assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_INT8) == 2048
+    assert lib.pa_default_split_tokens(1, 12, 2, 128, pa.PA_BF16) == 2048
+    assert lib.pa_default_split_tokens(2, 4, 1, 64, pa.PA_BF16) == 2048
     # it never depends on the batch: the same for any num_seqs / lengths, by signature
 
 
