@@ -97,7 +97,10 @@ const char* pa_last_error(void);
  * key, value    [num_tokens, kv_heads, head_dim], dtype kv_dtype
  * k_cache, v_cache [kv_heads, num_blocks, block_size, head_dim], kv_dtype
  * slot_mapping  [num_tokens] int64
- * kv_dtype      PA_F32 or PA_BF16 (PA_INT8 returns PA_ERR_UNSUPPORTED)
+ * kv_dtype      PA_F32, PA_BF16 or PA_INT8.  For an int8 cache the codes are
+ *               copied as given: quantising them with the block's scale
+ *               (k_scale / v_scale, which this call does not touch) is the
+ *               caller's part.
  * head_dim      64 or 128; block_size 16.  num_tokens == 0 is a no-op.
  */
 int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,

@@ -253,9 +253,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
   if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", block_size);
-  if (kv_dtype == PA_INT8)
-    return fail(PA_ERR_UNSUPPORTED, "int8 cache write is not built");
-  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16)
+  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_INT8)
     return fail(PA_ERR_INVALID_ARG, "unknown kv dtype %d", kv_dtype);
   if (num_tokens == 0) return PA_OK;
   if (long(num_tokens) * kv_heads * head_dim * elem_size(kv_dtype) / 16 > kMaxGrid)

@@ -127,7 +127,6 @@ def test_cache_write_rejects_invalid_arguments():
 
     assert call(D=80) == pa.PA_ERR_UNSUPPORTED
     assert call(bs=8) == pa.PA_ERR_UNSUPPORTED
-    assert call(dt=pa.PA_INT8) == pa.PA_ERR_UNSUPPORTED
     assert call(dt=9) == pa.PA_ERR_INVALID_ARG
     assert call(key=None) == pa.PA_ERR_INVALID_ARG
     assert call(key=FAKE + 4) == pa.PA_ERR_INVALID_ARG

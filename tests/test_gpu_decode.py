@@ -221,15 +221,21 @@ def test_poisoned_tail_and_spare_blocks_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("tag", ["f32", "bf16"])
-def test_cache_write_skips_negative_slots_and_touches_nothing_else(tag):
-    _say("cache write", tag)
+def _stored(rng, shape, tag):
+    if tag == "int8":
+        return rng.integers(-127, 128, size=shape, dtype=np.int8)
+    return wl.encode(rng.standard_normal(shape, dtype=np.float32), tag)
+
+
+@pytest.mark.parametrize("tag,D", [("f32", 64), ("bf16", 128), ("int8", 128), ("int8", 64)])
+def test_cache_write_skips_negative_slots_and_touches_nothing_else(tag, D):
+    _say("cache write", tag, D)
     rng = np.random.default_rng(17)
-    Hkv, nb, D = 3, 9, 128 if tag == "bf16" else 64
-    kc = wl.encode(rng.standard_normal((Hkv, nb, 16, D), dtype=np.float32), tag)
-    vc = wl.encode(rng.standard_normal((Hkv, nb, 16, D), dtype=np.float32), tag)
-    key = wl.encode(rng.standard_normal((7, Hkv, D), dtype=np.float32), tag)
-    val = wl.encode(rng.standard_normal((7, Hkv, D), dtype=np.float32), tag)
+    Hkv, nb = 3, 9
+    kc = _stored(rng, (Hkv, nb, 16, D), tag)
+    vc = _stored(rng, (Hkv, nb, 16, D), tag)
+    key = _stored(rng, (7, Hkv, D), tag)
+    val = _stored(rng, (7, Hkv, D), tag)
     slots = np.array([3, -1, 16 * nb - 1, 40, -7, 0, 77], np.int64)
     dk, dv = dev(kc), dev(vc)
     pa.reshape_and_cache(dev(key), dev(val), dk, dv, dev(slots))
