@@ -1,2 +1,3 @@
 """CPU oracle (test infrastructure only; never imported by the product path)."""
 from .attention import attend, decode, gather_context, reshape_and_cache, verify, widen  # noqa: F401
+from .requant import requantize_block, reshape_and_cache_int8  # noqa: F401
