@@ -140,7 +140,54 @@ def other_workloads(torch, pa, wl, dev, reps=10):
               flush=True)
         del kc, vc, g
         torch.cuda.empty_cache()
+    out["int8_requant_write"] = requant_write_timing(torch, pa, dev, reps)
     return out
+
+
+def requant_write_timing(torch, pa, dev, reps=10, calls=20):
+    """Decode-step cache write into an int8 cache that requantizes each target
+    block (64 tokens, 8 KV heads, head_dim 128, bf16 rows; every token in its
+    own block of a 8192-block cache), beside the plain bf16 row copy at the same
+    shape.  Both launched from a HIP graph of `calls` writes; events on the
+    launch stream."""
+    T, H, D, NB = 64, 8, 128, 8192
+    g_ = torch.Generator(device=dev)
+    g_.manual_seed(11)
+    kc = torch.randint(-127, 128, (H, NB, 16, D), dtype=torch.int8, device=dev, generator=g_)
+    vc = torch.randint(-127, 128, (H, NB, 16, D), dtype=torch.int8, device=dev, generator=g_)
+    ks = torch.rand((H, NB), device=dev, generator=g_) * 0.02 + 0.01
+    vs = torch.rand((H, NB), device=dev, generator=g_) * 0.02 + 0.01
+    key = torch.randn((T, H, D), device=dev, dtype=torch.bfloat16, generator=g_)
+    val = torch.randn((T, H, D), device=dev, dtype=torch.bfloat16, generator=g_)
+    blocks = torch.randperm(NB, device=dev, generator=g_)[:T]
+    slots = (blocks * 16 + torch.randint(0, 16, (T,), device=dev, generator=g_)).to(torch.int64)
+    kb = torch.zeros((H, NB, 16, D), dtype=torch.bfloat16, device=dev)
+    vb = torch.zeros_like(kb)
+    res = {"shape": f"T={T} Hkv={H} D={D} num_blocks={NB} rows=bf16"}
+    for name, fn in (("requant_us_per_call", lambda: pa.reshape_and_cache_quant(key, val, kc, vc, ks, vs, slots)),
+                     ("bf16_copy_us_per_call", lambda: pa.reshape_and_cache(key, val, kb, vb, slots))):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1e3 / (reps * calls), 2)
+    # bytes: read and write the block's codes, read the new rows and scales (K and V)
+    res["algorithmic_bytes"] = T * H * 2 * (2 * 16 * D + 2 * D + 2 * 4) + 8 * T
+    print(f"[bench] int8 requant write: {res['requant_us_per_call']} us/call "
+          f"(bf16 copy {res['bf16_copy_us_per_call']} us)", flush=True)
+    del kc, vc, kb, vb
+    torch.cuda.empty_cache()
+    return res
 
 
 def cache_write_bytes(num_tokens, kv_heads, head_dim, elem=2):

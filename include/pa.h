@@ -109,6 +109,35 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                          void* stream);
 
 /*
+ * pa_reshape_and_cache_quant -- write new tokens into an int8 cache,
+ * requantizing each target block ("A Rust inference server for Qwen2 on Apple
+ * Silicon", "Day 4 measurements -- int8 KV", "Partial blocks").
+ *
+ * For each token i with slot_mapping[i] >= 0, in index order, and every KV
+ * head g, with block p = slot / block_size and offset o = slot % block_size:
+ *   X = k_cache[g, p] * k_scale[g, p]         (fp32, the 16 rows of the block)
+ *   X[o, :] = key[i, g, :]
+ *   k_scale[g, p] = max|X| / 127               (1 when X is all zero)
+ *   k_cache[g, p] = clip(rint(X / k_scale[g, p]), -127, 127)
+ * and the same for value / v_cache / v_scale.  Every step is an fp32
+ * operation (rint rounds half to even), so the codes are exact functions of
+ * the inputs.  Unwritten slots hold code 0 and never raise the maximum; a
+ * value on the grid comes back unchanged while the scale does not change.
+ * Tokens aimed at the same block in one call act as consecutive calls.
+ *
+ * key, value    [num_tokens, kv_heads, head_dim], in_dtype PA_BF16 or PA_F32
+ * k_cache, v_cache [kv_heads, num_blocks, block_size, head_dim] int8
+ * k_scale, v_scale [kv_heads, num_blocks] fp32, read and written
+ * slot_mapping  [num_tokens] int64; negative = skip
+ * head_dim 64 or 128; block_size 16; num_blocks * block_size < 2^31.
+ */
+int pa_reshape_and_cache_quant(const void* key, const void* value, int8_t* k_cache,
+                               int8_t* v_cache, float* k_scale, float* v_scale,
+                               const int64_t* slot_mapping, int num_tokens, int kv_heads,
+                               int head_dim, int num_blocks, int block_size, int in_dtype,
+                               void* stream);
+
+/*
  * Split-K over context.  A sequence's context is cut into consecutive pieces
  * of `split_tokens` positions (a multiple of block_size); each piece is
  * reduced to a partial (normalised output, log-sum-exp) pair in fp32, and a

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
 PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 
-EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_default_split_tokens",
+EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_quant",
+            "pa_default_split_tokens",
             "pa_workspace_size", "pa_decode", "pa_decode_append", "pa_verify"]
 
 _DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_INT8}
@@ -52,6 +53,8 @@ def _load():
     lib.pa_last_error.argtypes = []
     lib.pa_reshape_and_cache.restype = i
     lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.pa_reshape_and_cache_quant.restype = i
+    lib.pa_reshape_and_cache_quant.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.pa_default_split_tokens.restype = i
     lib.pa_default_split_tokens.argtypes = [i, i, i, i, i]
     lib.pa_workspace_size.restype = sz
@@ -139,6 +142,35 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     _check(_load().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(slot_mapping), T, H, D, NB, BS, _DTYPE[key.dtype],
                                         _stream(stream)))
+
+
+def reshape_and_cache_quant(key, value, k_cache, v_cache, k_scale, v_scale, slot_mapping,
+                            stream=None):
+    """Write bf16/fp32 key/value rows into int8 caches, requantizing each target block.
+
+    k_cache/v_cache [kv_heads, num_blocks, 16, head_dim] int8 and k_scale/v_scale
+    [kv_heads, num_blocks] float32 are updated in place.
+    """
+    _need(key, "key", ndim=3)
+    _need(value, "value", dtype=key.dtype, ndim=3)
+    _need(k_cache, "k_cache", dtype=torch.int8, ndim=4)
+    _need(v_cache, "v_cache", dtype=torch.int8, ndim=4)
+    _need(k_scale, "k_scale", dtype=torch.float32, ndim=2)
+    _need(v_scale, "v_scale", dtype=torch.float32, ndim=2)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    if key.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("key/value must be bfloat16 or float32")
+    H, NB, BS, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or key.shape != value.shape:
+        raise ValueError("cache or key/value shapes differ")
+    if k_scale.shape != (H, NB) or v_scale.shape != (H, NB):
+        raise ValueError("scales must be [kv_heads, num_blocks]")
+    T = key.shape[0]
+    if key.shape[1:] != (H, D) or slot_mapping.shape[0] != T:
+        raise ValueError("key [num_tokens, kv_heads, head_dim] does not match the cache")
+    _check(_load().pa_reshape_and_cache_quant(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(slot_mapping), T, H, D, NB, BS, _DTYPE[key.dtype], _stream(stream)))
 
 
 def _attention(fn_verify: bool, out, q, k_cache, v_cache, block_tables, context_lens, scale,

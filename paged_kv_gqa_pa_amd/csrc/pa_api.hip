@@ -270,6 +270,37 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   return PA_OK;
 }
 
+int pa_reshape_and_cache_quant(const void* key, const void* value, int8_t* k_cache,
+                               int8_t* v_cache, float* k_scale, float* v_scale,
+                               const int64_t* slot_mapping, int num_tokens, int kv_heads,
+                               int head_dim, int num_blocks, int block_size, int in_dtype,
+                               void* stream) {
+  if (num_tokens < 0 || kv_heads <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "invalid sizes: num_tokens=%d kv_heads=%d num_blocks=%d",
+                num_tokens, kv_heads, num_blocks);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", block_size);
+  if (in_dtype != PA_F32 && in_dtype != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "key/value dtype %d: PA_F32 or PA_BF16", in_dtype);
+  if (long(num_blocks) * block_size >= 2147483647L)
+    return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size must stay below 2^31");
+  if (2L * num_tokens * kv_heads > kMaxGrid)
+    return fail(PA_ERR_UNSUPPORTED, "num_tokens * kv_heads too large");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !k_scale || !v_scale || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+      !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer argument");
+  pa::QuantCacheArgs a{key, value, k_cache, v_cache, k_scale, v_scale, slot_mapping,
+                       num_tokens, kv_heads, num_blocks, head_dim, in_dtype};
+  hipError_t e = pa::launch_reshape_and_cache_quant(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 int pa_default_split_tokens(int num_query_tokens, int q_heads, int kv_heads, int head_dim,
                             int kv_dtype) {
   return default_split(num_query_tokens, q_heads, kv_heads, head_dim, kv_dtype);

@@ -24,6 +24,21 @@ struct CacheArgs {
   int row_bytes;  // head_dim * element size
 };
 
+struct QuantCacheArgs {
+  const void* key;      // [num_tokens, kv_heads, head_dim], in_dtype
+  const void* value;
+  int8_t* k_cache;      // [kv_heads, num_blocks, 16, head_dim]
+  int8_t* v_cache;
+  float* k_scale;       // [kv_heads, num_blocks]
+  float* v_scale;
+  const int64_t* slot_mapping;
+  int num_tokens;
+  int kv_heads;
+  int num_blocks;
+  int head_dim;
+  int in_dtype;
+};
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -71,6 +86,7 @@ struct MergeArgs {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheArgs& a, hipStream_t stream);
+hipError_t launch_reshape_and_cache_quant(const QuantCacheArgs& a, hipStream_t stream);
 hipError_t launch_decode_pass1(const DecodeArgs& a, bool append, hipStream_t stream);
 // Matrix-core kernel for R = T * G <= 16 query rows per (sequence, KV head):
 // every verify call, and decode over an int8 cache.
