@@ -194,8 +194,33 @@ def cache_write_bytes(num_tokens, kv_heads, head_dim, elem=2):
     return num_tokens * kv_heads * head_dim * elem * 2 * 2 + num_tokens * 8
 
 
+_CPU_CASE = None
+
+
+def _oracle_one_seq(b):
+    """Worker: the oracle's decode of sequence b of the sampled layer (all its heads)."""
+    import oracle
+    c = _CPU_CASE
+    return oracle.decode(c.q[b:b + 1], c.k_cache, c.v_cache, c.block_tables[b:b + 1],
+                         c.context_lens[b:b + 1], c.scale, "bf16", "bf16")
+
+
+def _pool_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
 def cpu_baseline(target_s: float):
-    """The fp64 oracle on a bounded sample of the same workload (single thread)."""
+    """The fp64 oracle on a bounded sample of the same workload: layer 0's decode
+    repeated for about target_s seconds, (i) on one core with one BLAS thread,
+    (ii) on every host core through a process pool over sequences (one BLAS
+    thread per worker, at most 16 workers).  Runs before anything touches the
+    GPU, so the pool's forked workers hold no device state."""
+    global _CPU_CASE
+    import multiprocessing as mp
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
@@ -203,6 +228,8 @@ def cpu_baseline(target_s: float):
     import oracle
     from paged_kv_gqa_pa_amd import workloads as wl
     case = wl.build_case(WORKLOAD, layer=0)
+    spec = case.spec
+    alg = algorithmic_bytes(case.context_lens, spec.q_heads, spec.kv_heads, spec.head_dim)
     ctx = threadpool_limits(1) if threadpool_limits else None
     try:
         n_layers = 0
@@ -218,14 +245,35 @@ def cpu_baseline(target_s: float):
         if ctx is not None:
             ctx.__exit__(None, None, None)
     per_layer = el / n_layers
-    spec = case.spec
     tok_s = spec.num_seqs / (per_layer * spec.layers)
-    gbps = algorithmic_bytes(case.context_lens, spec.q_heads, spec.kv_heads, spec.head_dim) / per_layer / 1e9
-    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_layers} decode passes of layer 0 (64 seqs, 16q/8kv heads, D=128) in "
-                      f"{el:.1f} s; tokens/s = 64 / (28 x time per layer); cache write not timed; "
-                      f"{gbps:.3f} GB/s on the same algorithmic bytes",
-            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+    gbps = alg / per_layer / 1e9
+    res = {"value": round(tok_s, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"{n_layers} decode passes of layer 0 (64 seqs, 16q/8kv heads, D=128) in "
+                     f"{el:.1f} s; tokens/s = 64 / (28 x time per layer); cache write not timed; "
+                     f"{gbps:.3f} GB/s on the same algorithmic bytes",
+           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+    workers = max(1, min(16, os.cpu_count() or 1))
+    _CPU_CASE = case
+    try:
+        with mp.get_context("fork").Pool(workers, initializer=_pool_init) as pool:
+            pool.map(_oracle_one_seq, range(min(workers, spec.num_seqs)))   # start-up
+            n_all = 0
+            t0 = time.perf_counter()
+            while True:
+                pool.map(_oracle_one_seq, range(spec.num_seqs), chunksize=2)
+                n_all += 1
+                el_all = time.perf_counter() - t0
+                if el_all >= target_s:
+                    break
+        per_all = el_all / n_all
+        res["all_cores"] = {
+            "value": round(spec.num_seqs / (per_all * spec.layers), 2), "unit": "tokens/s",
+            "cores": workers, "kind": "oracle",
+            "sample": f"{n_all} decode passes of layer 0 over a {workers}-process pool "
+                      f"(one sequence per task) in {el_all:.1f} s; {alg / per_all / 1e9:.3f} GB/s"}
+    finally:
+        _CPU_CASE = None
+    return res
 
 
 def _cpu_model():
@@ -246,11 +294,21 @@ def main():
               "(multi-GPU sharding is a design note, not a measured path).", file=sys.stderr)
         sys.exit(2)
 
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before the GPU is touched: the all-cores leg forks worker processes
+        print("[bench] cpu baseline ...", flush=True)
+        cpu = cpu_baseline(args.cpu_seconds)
+        print(f"[bench] cpu baseline: {cpu['value']} tokens/s on 1 core, "
+              f"{cpu['all_cores']['value']} on {cpu['all_cores']['cores']}", flush=True)
+
     import torch
     from paged_kv_gqa_pa_amd import _lib as pa
+    from paged_kv_gqa_pa_amd import _probe as probe
     from paged_kv_gqa_pa_amd import workloads as wl
 
     pa.lib()  # fail loudly if the HIP library is missing
+    probe.lib()
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -336,15 +394,18 @@ def main():
         print("[bench] calibration copy: 256 MiB read + 256 MiB written", flush=True)
         del src, dst
 
-    # Whole step: K steps between two events, synchronised on both sides.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Whole step: K steps between events (one before each step and one after the
+    # last), synchronised on both sides; the total gives the mean, the gaps the
+    # per-step median, min and max.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         run_step()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     tok_s = N / (ms_step / 1e3)
     print(f"[bench] step {ms_step * 1e3:.1f} us", flush=True)
 
@@ -364,16 +425,60 @@ def main():
     # Decode kernel alone: back-to-back launches over the 28 layers (distinct caches,
     # 2.8 GB per pass, far beyond the 256 MB last-level cache), events on the launch stream.
     torch.cuda.synchronize()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record()
-    for _ in range(args.decode_reps):
+    dv = [torch.cuda.Event(enable_timing=True) for _ in range(args.decode_reps + 1)]
+    dv[0].record()
+    for i in range(args.decode_reps):
         run_decode()
-    d1.record()
+        dv[i + 1].record()
     torch.cuda.synchronize()
-    us_decode = d0.elapsed_time(d1) * 1e3 / (args.decode_reps * Lyr)
+    us_decode = dv[0].elapsed_time(dv[-1]) * 1e3 / (args.decode_reps * Lyr)
+    per_pass = sorted(dv[i].elapsed_time(dv[i + 1]) * 1e3 / Lyr for i in range(args.decode_reps))
     bytes_launch = algorithmic_bytes(lens, Hq, Hkv, D)
     gbps = bytes_launch / (us_decode * 1e-6) / 1e9
     print(f"[bench] decode {us_decode:.2f} us/launch, {gbps:.0f} GB/s", flush=True)
+
+    # Reference reads: a plain streaming read of four layer caches (4 x 512 MiB,
+    # each launch far beyond the last-level cache), and the decode's own tile
+    # reads without arithmetic over the 28 layers.
+    kv_bytes = 2 * int(lens.sum()) * Hkv * D * 2
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    reads = kc[:4]
+    for r in reads:
+        probe.stream_read(r, sink)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(3):
+        for r in reads:
+            probe.stream_read(r, sink)
+    s1.record()
+    torch.cuda.synchronize()
+    stream_gbps = 3 * sum(r.numel() * 2 for r in reads) / (s0.elapsed_time(s1) * 1e-3) / 1e9
+    split_used = args.split or pa.default_split_tokens(Hq, Hkv, D, torch.bfloat16)
+    tile = {}
+    for waves in (4, 8):
+        def tiles():
+            for l in range(Lyr):
+                probe.tile_read(kc[l], vc[l], bt, cl, max_len, split_used, sink, waves=waves)
+        tiles()
+        torch.cuda.synchronize()
+        gt = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gt):
+            tiles()
+        gt.replay()
+        torch.cuda.synchronize()
+        t0_, t1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0_.record()
+        for _ in range(args.decode_reps):
+            gt.replay()
+        t1_.record()
+        torch.cuda.synchronize()
+        us_t = t0_.elapsed_time(t1_) * 1e3 / (args.decode_reps * Lyr)
+        tile[waves] = {"us_per_launch": round(us_t, 3), "gbps": round(kv_bytes / (us_t * 1e-6) / 1e9, 1)}
+        del gt
+    best_tile = max(t["gbps"] for t in tile.values())
+    print(f"[bench] streaming read {stream_gbps:.0f} GB/s; decode-pattern tile read "
+          f"{tile[4]['gbps']:.0f} GB/s (4 waves), {tile[8]['gbps']:.0f} GB/s (8 waves)", flush=True)
 
     traffic = None
     if os.path.exists(args.traffic_file):
@@ -393,6 +498,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                    "max": round(per_step[-1], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -411,13 +518,22 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_pass1",
-                     "us_per_launch": round(us_decode, 3), "algorithmic_bytes_per_launch": bytes_launch},
+                     "us_per_launch": round(us_decode, 3), "algorithmic_bytes_per_launch": bytes_launch,
+                     "us_per_launch_over_passes": {"median": round(per_pass[len(per_pass) // 2], 3),
+                                                   "min": round(per_pass[0], 3),
+                                                   "max": round(per_pass[-1], 3)}},
+        "achievable": {"stream_read_gbps": round(stream_gbps, 1),
+                       "decode_frac_of_stream_read": round(gbps / stream_gbps, 4),
+                       "tile_read": {f"{w}_waves": t for w, t in tile.items()},
+                       "decode_frac_of_tile_read": round(gbps / best_tile, 4),
+                       "note": "stream read: 4 x 512 MiB layer caches, 16-byte non-temporal loads; "
+                               "tile read: the decode's K/V reads (exact rows, same grid order and "
+                               "pieces) with no arithmetic, over the same 28 layers"},
     }
     if not args.no_other_workloads:
         res["other_workloads"] = other_workloads(torch, pa, wl, dev)
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline ...", flush=True)
-        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Build libpa.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Build libpa.so (the HIP kernels and the C ABI) and libpa_probe.so (bandwidth
+probes used by the benchmark) in-tree for gfx950.
 
 Usage: python -m paged_kv_gqa_pa_amd.build   (or build() from Python)
 """
@@ -13,10 +14,12 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpa.so")
+PROBE_OUT = os.path.join(HERE, "libpa_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 SOURCES = ["pa_api.hip", "pa_cache.hip", "pa_decode.hip", "pa_verify.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -45,21 +48,27 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = True, extra_flags=()) -> str:
-    """Compile every HIP source and link libpa.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     # --no-undefined: a kernel whose host stub was not emitted fails here, not at load time.
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True, extra_flags=()) -> str:
+    """Compile every HIP source, link libpa.so and libpa_probe.so; returns libpa's path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, (os.cpu_count() or 2)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PROBE_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PROBE_OUT}")
     return OUT
 
 

@@ -132,3 +132,24 @@ def test_cache_write_rejects_invalid_arguments():
     assert call(key=FAKE + 4) == pa.PA_ERR_INVALID_ARG
     assert call(T=-1) == pa.PA_ERR_INVALID_ARG
     assert call(T=0, key=None) == pa.PA_OK
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The bandwidth-probe library loads, exports what include/pa_probe.h declares and
+    rejects invalid arguments before launching anything."""
+    from paged_kv_gqa_pa_amd import _probe
+    src = open(os.path.join(ROOT, "include", "pa_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(pa_probe_\w+)\s*\(", src, flags=re.M)))
+    assert names == sorted(_probe.EXPORTED)
+    lib = _probe.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pa_probe_stream_read(None, 1024, 0, None, None) == -1
+    assert lib.pa_probe_stream_read(ctypes.c_void_p(4096), 1000, 0, ctypes.c_void_p(4096), None) == -1
+    assert b"multiple of 16" in lib.pa_probe_last_error()
+    d = ctypes.c_void_p(4096)
+    # row_bytes 64 is not built
+    assert lib.pa_probe_tile_read(d, d, d, d, 1, 1, 4, 4, 64, 16, 64, 4, d, None) == -1
+    # waves 16 is not built
+    assert lib.pa_probe_tile_read(d, d, d, d, 1, 1, 4, 4, 256, 16, 64, 16, d, None) == -1
