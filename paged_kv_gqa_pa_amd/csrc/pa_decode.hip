@@ -515,35 +515,36 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 // weights.  Rows of single-piece sequences were written by pass 1.
 // rows_per_seq is q_heads for decode and T * q_heads for verify.
 // ---------------------------------------------------------------------------
-template <typename O, int D>
+template <typename O, int D, int CH>
 __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.num_rows) return;
-  const int b = row / a.rows_per_seq;
-  const int L = min(a.context_lens[b], a.max_len_clamp);
-  const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
-  if (n_pieces <= 1) return;
   const int lane = threadIdx.x & 63;
   const float* lse = a.part_lse + size_t(row) * a.max_pieces;
   const float* po = a.part_o + size_t(row) * a.max_pieces * D;
   // Pieces are taken CH at a time with every load of the chunk in flight at
   // once: lane u reads piece s0 + u's log2-sum-exp, every lane reads its dims
-  // of all CH partial outputs.  Chunks combine in piece order with a running
-  // maximum.  CH is 8 for calls of up to 8 pieces, else 32.
+  // of all CH partial outputs.  The first chunk is requested together with the
+  // context length (the partial buffers hold max_pieces slots per row, so the
+  // reads stay in bounds whatever the length); slots past the row's piece
+  // count are read but never used.  Chunks combine in piece order with a
+  // running maximum.
   constexpr int PER = D / 64;
+  const int first = min(CH, a.max_pieces);
+  float lse0 = lane < first ? lse[lane] : kNegInf;
+  float ov0[CH][PER];
+#pragma unroll
+  for (int u = 0; u < CH; ++u)
+#pragma unroll
+    for (int j = 0; j < PER; ++j) ov0[u][j] = po[size_t(min(u, first - 1)) * D + j * 64 + lane];
+  const int b = row / a.rows_per_seq;
+  const int L = min(a.context_lens[b], a.max_len_clamp);
+  const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
+  if (n_pieces <= 1) return;
   float M = kNegInf, wsum = 0.0f;
   float o[PER] = {};
-  auto chunk = [&](auto ch_tag, int s0) {
-    constexpr int CH = decltype(ch_tag)::value;
-    const int cnt = min(CH, n_pieces - s0);
-    const float my_lse = lane < cnt ? lse[s0 + lane] : kNegInf;
-    float ov[CH][PER];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int sp = s0 + min(u, cnt - 1);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) ov[u][j] = po[size_t(sp) * D + j * 64 + lane];
-    }
+  auto combine = [&](int cnt, float my_lse, const float (&ov)[CH][PER]) {
+    my_lse = lane < cnt ? my_lse : kNegInf;
     const float cm = fmaxf(M, stride_max<1>(my_lse));
     if (cm == kNegInf) return;
     const float f = M == kNegInf ? 0.0f : fast_exp2(M - cm);
@@ -554,16 +555,24 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
     const float w_lane = my_lse == kNegInf ? 0.0f : fast_exp2(my_lse - M);
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
+      // slots past cnt may hold anything (even NaN): selected away, not weighted by 0
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), u));
-      wsum += w;
+      const bool use = u < cnt;
+      wsum += use ? w : 0.0f;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) o[j] = __builtin_fmaf(w, ov[u][j], o[j]);
+      for (int j = 0; j < PER; ++j) o[j] = use ? __builtin_fmaf(w, ov[u][j], o[j]) : o[j];
     }
   };
-  if (n_pieces <= 8) {
-    chunk(std::integral_constant<int, 8>{}, 0);
-  } else {
-    for (int s0 = 0; s0 < n_pieces; s0 += 32) chunk(std::integral_constant<int, 32>{}, s0);
+  combine(min(CH, n_pieces), lse0, ov0);
+  for (int s0 = CH; s0 < n_pieces; s0 += CH) {
+    const int cnt = min(CH, n_pieces - s0);
+    const float my_lse = lane < cnt ? lse[s0 + lane] : kNegInf;
+    float ov[CH][PER];
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) ov[u][j] = po[size_t(s0 + min(u, cnt - 1)) * D + j * 64 + lane];
+    combine(cnt, my_lse, ov);
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
 #pragma unroll
@@ -629,14 +638,22 @@ extern "C" int pa_debug_wtimes(unsigned long long* host, int n) {
 
 bool decode_group_supported(int G) { return (G >= 1 && G <= 8) || G == 16; }
 
-hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+template <typename O, int D>
+void launch_merge_t(const MergeArgs& a, hipStream_t stream) {
+  // chunks of 8 pieces for calls of up to 8 pieces, 16 up to 16, else 32
   dim3 grid(cdiv(a.num_rows, 4));
+  if (a.max_pieces <= 8) merge_pieces<O, D, 8><<<grid, 256, 0, stream>>>(a);
+  else if (a.max_pieces <= 16) merge_pieces<O, D, 16><<<grid, 256, 0, stream>>>(a);
+  else merge_pieces<O, D, 32><<<grid, 256, 0, stream>>>(a);
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.out_dtype == kF32) {
-    if (a.head_dim == 64) merge_pieces<float, 64><<<grid, 256, 0, stream>>>(a);
-    else merge_pieces<float, 128><<<grid, 256, 0, stream>>>(a);
+    if (a.head_dim == 64) launch_merge_t<float, 64>(a, stream);
+    else launch_merge_t<float, 128>(a, stream);
   } else {
-    if (a.head_dim == 64) merge_pieces<bf16_t, 64><<<grid, 256, 0, stream>>>(a);
-    else merge_pieces<bf16_t, 128><<<grid, 256, 0, stream>>>(a);
+    if (a.head_dim == 64) launch_merge_t<bf16_t, 64>(a, stream);
+    else launch_merge_t<bf16_t, 128>(a, stream);
   }
   return hipGetLastError();
 }
