@@ -30,6 +30,11 @@ What it computes, and where the pages define it:
   triangular mask sliced at the chunk's start), applied to the k+1 tokens of a
   verify step ("From 183 ms to 19 ms", "Then speculative decoding got
   slower").
+* Variable-length verify: sequence b contributes its own number of new
+  tokens T_b (at most k+1; the pages pad every sequence to k+1 -- "From 183
+  ms to 19 ms", "Then speculative decoding got slower"), its query rows packed
+  one sequence after another; each sequence is then the verify above with its
+  own T_b.
 * int8 caches are read as ``code * scale`` with one float scale per
   (kv_head, block) -- the stored values, widened exactly to fp64.
 * The cache write places token i's K/V for every KV head at flat slot
@@ -44,7 +49,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["widen", "gather_context", "attend", "decode", "verify", "reshape_and_cache"]
+__all__ = ["widen", "gather_context", "attend", "decode", "verify", "verify_varlen",
+           "reshape_and_cache"]
 
 
 def widen(stored: np.ndarray, tag: str) -> np.ndarray:
@@ -133,6 +139,27 @@ def verify(q, k_cache, v_cache, block_tables, context_lens, scale, q_tag, kv_tag
             vis = np.arange(L)[None, :] <= np.repeat(last_seen, G)[:, None]
             o = attend(rows, K, V, scale, vis)
             out[b, :, g * G:(g + 1) * G] = o.reshape(T, G, D)
+    return out
+
+
+def verify_varlen(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, q_tag,
+                  kv_tag, k_scale=None, v_scale=None):
+    """Per-sequence query counts over packed query rows.
+
+    q: [total, H_q, D] stored; sequence b's query tokens are rows
+    query_start[b] .. query_start[b+1]-1 (T_b of them, possibly none), and it
+    is the verify of one sequence with T = T_b: its token t sees positions
+    0 .. L_b - T_b + t.  Returns fp64 [total, H_q, D].
+    """
+    qs = np.asarray(query_start, np.int64)
+    q = np.asarray(q)
+    out = np.zeros(q.shape, np.float64)
+    for b in range(len(qs) - 1):
+        lo, hi = int(qs[b]), int(qs[b + 1])
+        if hi <= lo:
+            continue
+        out[lo:hi] = verify(q[None, lo:hi], k_cache, v_cache, block_tables[b:b + 1],
+                            context_lens[b:b + 1], scale, q_tag, kv_tag, k_scale, v_scale)[0]
     return out
 
 

@@ -17,6 +17,9 @@ disagrees with what the pages and the mathematics fix:
   it: an upper-triangular -1e9 matrix sliced at the chunk start;
 * invariants: physical placement of blocks does not matter; verify with one
   query token is decode; an int8 cache reads as code * per-block scale;
+* variable-length verify against pure-Python loops over packed rows (with
+  sequences of no query token and of more tokens than positions), equal
+  counts against fixed-T verify, one token per sequence against decode;
 * the cache write, checked against a flat one-index-per-slot view of the
   cache and for untouched bytes.
 """
@@ -106,6 +109,70 @@ def _brute_decode(q, kc, vc, table, lens, scale, G):
                     acc.append(w[j] * float(vc[g, blk, j % bs, d]))
                 out[b, h, d] = math.fsum(acc) / tot
     return out
+
+
+def _brute_verify_varlen(q, kc, vc, table, lens, qs, scale, G):
+    """Pure-Python loops: packed row r of sequence b (T_b rows from qs[b]) is query
+    token t = r - qs[b], seeing positions j <= L_b - T_b + t."""
+    total, Hq, D = q.shape
+    bs = kc.shape[2]
+    out = np.zeros((total, Hq, D))
+    for b in range(len(qs) - 1):
+        L = int(lens[b])
+        Tb = int(qs[b + 1]) - int(qs[b])
+        for t in range(Tb):
+            r = int(qs[b]) + t
+            last = L - Tb + t
+            for h in range(Hq):
+                g = h // G
+                seen = [j for j in range(L) if j <= last]
+                if not seen:
+                    continue
+                sc = []
+                for j in seen:
+                    blk = int(table[b][j // bs])
+                    sc.append(scale * math.fsum(float(q[r, h, d]) * float(kc[g, blk, j % bs, d])
+                                                for d in range(D)))
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                tot = math.fsum(w)
+                for d in range(D):
+                    out[r, h, d] = math.fsum(w[i] * float(vc[g, int(table[b][j // bs]), j % bs, d])
+                                             for i, j in enumerate(seen)) / tot
+    return out
+
+
+def pin_verify_varlen(oracle):
+    """Per-sequence query counts (none, fewer than the context, more than it) against
+    brute force; equal counts reduce to fixed-T verify; one token per sequence is decode."""
+    rng = np.random.default_rng(77)
+    Hkv, G, D, nb = 2, 3, 4, 20
+    lens = np.array([5, 0, 33, 3, 17, 2], np.int32)
+    counts = np.array([2, 0, 4, 5, 1, 2], np.int64)       # sequence 3: more tokens than positions
+    qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    perm = rng.permutation(nb).astype(np.int32)
+    table = wl.assign_blocks(lens, perm, 3)
+    kc = rng.standard_normal((Hkv, nb, 16, D)).astype(np.float32)
+    vc = rng.standard_normal((Hkv, nb, 16, D)).astype(np.float32)
+    q = rng.standard_normal((int(qs[-1]), Hkv * G, D)).astype(np.float32)
+    got = oracle.verify_varlen(q, kc, vc, table, lens, qs, 0.41, "f32", "f32")
+    want = _brute_verify_varlen(q, kc, vc, table, lens, qs, 0.41, G)
+    assert got.shape == want.shape
+    assert np.abs(got - want).max() <= 1e-12, "varlen verify vs brute force"
+    # equal counts: the fixed-T verify, packed
+    T = 3
+    lens2 = np.array([9, 40, 3], np.int32)
+    table2 = wl.assign_blocks(lens2, rng.permutation(nb).astype(np.int32), 3)
+    q2 = rng.standard_normal((3, T, Hkv * G, D)).astype(np.float32)
+    qs2 = np.arange(4, dtype=np.int32) * T
+    got2 = oracle.verify_varlen(q2.reshape(3 * T, Hkv * G, D), kc, vc, table2, lens2, qs2, 0.5, "f32", "f32")
+    want2 = oracle.verify(q2, kc, vc, table2, lens2, 0.5, "f32", "f32").reshape(3 * T, Hkv * G, D)
+    assert np.abs(got2 - want2).max() <= 1e-12, "equal counts vs fixed-T verify"
+    # one token each: decode
+    got3 = oracle.verify_varlen(q2[:, 0], kc, vc, table2, lens2, np.arange(4, dtype=np.int32), 0.5,
+                                "f32", "f32")
+    want3 = _brute_decode(q2[:, 0], kc, vc, table2, lens2, 0.5, G)
+    assert np.abs(got3 - want3).max() <= 1e-12, "one token per sequence vs decode"
 
 
 def pin_bruteforce_tiny(oracle):
@@ -308,4 +375,5 @@ def pin_cache_write(oracle):
 
 
 PINS = [pin_bruteforce_tiny, pin_closed_forms, pin_golden, pin_gqa_against_library,
-        pin_verify_prefill_mask, pin_placement_invariance, pin_int8_dequant, pin_cache_write]
+        pin_verify_prefill_mask, pin_placement_invariance, pin_int8_dequant, pin_cache_write,
+        pin_verify_varlen]

@@ -48,6 +48,8 @@ MUTATIONS = {
     # cache write offset from the wrong end
     "cache_write_offset": ("blk, off = int(slot) // bs, int(slot) % bs", "blk, off = int(slot) // bs, bs - 1 - int(slot) % bs"),
     # context length off by one
+    "varlen_drop_last_token": ("out[lo:hi] = verify(q[None, lo:hi]", "out[lo:hi - 1] = verify(q[None, lo:hi - 1]"),
+    "varlen_first_seq_length": ("context_lens[b:b + 1], scale, q_tag", "context_lens[0:1], scale, q_tag"),
     "context_short_by_one": ("L = int(context_lens[b])\n        for g in range(Hkv):", "L = max(int(context_lens[b]) - 1, 0)\n        for g in range(Hkv):"),
 }
 
