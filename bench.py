@@ -82,9 +82,16 @@ def other_workloads(torch, pa, wl, dev, reps=10):
     lengths and block tables are the seeded ones."""
     out = {}
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "int8": torch.int8}
-    for name in ("qwen2_1p5b_bf16", "spec_verify_bf16", "long_ctx_int8"):
-        spec = wl.CONFIGS[name]
+    for name in ("qwen2_1p5b_bf16", "spec_verify_bf16", "spec_verify_varlen_bf16", "long_ctx_int8"):
+        varlen = name == "spec_verify_varlen_bf16"
+        spec = wl.CONFIGS["spec_verify_bf16" if varlen else name]
         lens, table = wl.structure(spec)
+        counts = None
+        if varlen:
+            # the speculative workload with 1..5 new tokens per sequence (seeded): the
+            # prior context is kept, so each length becomes prior + T_b
+            counts = np.random.default_rng(spec.seed + 100).integers(1, 6, size=spec.num_seqs)
+            lens = (lens - spec.num_query_tokens + counts).astype(np.int32)
         N, T, Hq, Hkv, D, NB = (spec.num_seqs, spec.num_query_tokens, spec.q_heads,
                                 spec.kv_heads, spec.head_dim, spec.num_blocks)
         kdt = tdt[spec.kv_dtype]
@@ -104,7 +111,13 @@ def other_workloads(torch, pa, wl, dev, reps=10):
             vs = torch.rand((Hkv, NB), device=dev) * 0.02 + 0.01
         bt = torch.from_numpy(table).to(dev)
         cl = torch.from_numpy(lens).to(dev)
-        q = torch.randn((N, T, Hq, D) if T > 1 else (N, Hq, D), device=dev, dtype=torch.bfloat16)
+        if varlen:
+            total = int(counts.sum())
+            q = torch.randn((total, Hq, D), device=dev, dtype=torch.bfloat16)
+            qs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+        else:
+            total = N * T
+            q = torch.randn((N, T, Hq, D) if T > 1 else (N, Hq, D), device=dev, dtype=torch.bfloat16)
         o = torch.empty_like(q)
         split = pa.default_split_tokens(Hq, Hkv, D, kdt, num_query_tokens=T)
         wsb = pa.workspace_size(N, T, Hq, Hkv, D, spec.max_len, kdt, split)
@@ -113,8 +126,12 @@ def other_workloads(torch, pa, wl, dev, reps=10):
 
         def calls():
             for r in range(R):
-                fn(o, q, kc[r], vc[r], bt, cl, 1.0 / float(np.sqrt(D)), spec.max_len, ks, vs,
-                   split_tokens=split, workspace=ws)
+                if varlen:
+                    pa.verify_varlen(o, q, kc[r], vc[r], bt, cl, qs, 1.0 / float(np.sqrt(D)),
+                                     spec.max_len, T, split_tokens=split, workspace=ws)
+                else:
+                    fn(o, q, kc[r], vc[r], bt, cl, 1.0 / float(np.sqrt(D)), spec.max_len, ks, vs,
+                       split_tokens=split, workspace=ws)
         calls()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -129,13 +146,14 @@ def other_workloads(torch, pa, wl, dev, reps=10):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * R)
-        alg = attention_bytes(lens, T, Hq, Hkv, D, elem)
+        alg = attention_bytes(lens, 1, Hq, Hkv, D, elem) + (total - N) * Hq * D * 2 * 2
         gbps = alg / (us * 1e-6) / 1e9
         out[name] = {"us_per_call": round(us, 2), "algorithmic_bytes": alg,
                      "hbm_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "query_tokens_per_s": round(N * T / (us * 1e-6), 1),
+                     "query_tokens_per_s": round(total / (us * 1e-6), 1),
                      "split_tokens": split, "kernel": "rows_pass1" if (T > 1 or elem == 1) else "decode_pass1",
-                     "shape": f"N={N} T={T} Hq={Hq} Hkv={Hkv} D={D} kv={spec.kv_dtype}"}
+                     "shape": f"N={N} T={'1..5 per sequence, ' + str(total) + ' rows' if varlen else T} "
+                              f"Hq={Hq} Hkv={Hkv} D={D} kv={spec.kv_dtype}"}
         print(f"[bench] {name}: {us:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}%)",
               flush=True)
         del kc, vc, g

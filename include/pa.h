@@ -245,9 +245,10 @@ int pa_decode_append(void* out, const void* q, const void* key, const void* valu
  * other arguments as pa_decode.  num_query_tokens * (q_heads / kv_heads)
  * must be <= 16 (the row count of one matrix-core tile), else
  * PA_ERR_UNSUPPORTED.
- * Supported dtypes: PA_BF16 q with a PA_BF16 cache (bf16 output); head_dim
- * 64 or 128.  Scores and the output accumulate in fp32 on the matrix cores;
- * the softmax weights are rounded to bf16 for the weighted sum of V.
+ * Supported dtypes: PA_BF16 q with a PA_BF16 or PA_INT8 cache (bf16 output;
+ * int8 needs k_scale / v_scale); head_dim 64 or 128.  Scores and the output
+ * accumulate in fp32 on the matrix cores; the softmax weights are rounded to
+ * bf16 (bf16 cache) or fp16 (int8 cache) for the weighted sum of V.
  */
 int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
@@ -256,6 +257,39 @@ int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache
               int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
               int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
               void* stream);
+
+/*
+ * pa_verify_varlen -- pa_verify with a number of new tokens per sequence:
+ * T_b = query_start[b + 1] - query_start[b] (0 .. max_query_tokens), where
+ * the pages pad every sequence to k+1 ("From 183 ms to 19 ms per decode
+ * step", "Then speculative decoding got slower").  Each sequence is exactly
+ * the pa_verify of that sequence with T = T_b: query token t attends to
+ * positions 0 .. context_lens[b] - T_b + t.
+ *
+ * out, q        [total_query_tokens, q_heads, head_dim], bf16; sequence b's
+ *               tokens are rows query_start[b] .. query_start[b + 1] - 1.
+ * query_start   [num_seqs + 1] int32, non-decreasing, query_start[0] = 0,
+ *               query_start[num_seqs] = total_query_tokens (device memory,
+ *               not checked by the host; out-of-range offsets are clamped so
+ *               that nothing outside q / out is touched).  Rows of out that
+ *               belong to no sequence are not written.
+ * total_query_tokens  <= num_seqs * max_query_tokens, else PA_ERR_INVALID_ARG.
+ * max_query_tokens    the largest T_b; max_query_tokens * (q_heads /
+ *               kv_heads) <= 16.
+ * split_tokens  0 = the matrix-core default (pa_default_split_tokens with
+ *               num_query_tokens >= 2), so a sequence's result does not depend
+ *               on the other sequences of the call.
+ * workspace     pa_workspace_size(num_seqs, max_query_tokens, ...) bytes
+ *               suffice.
+ * Other arguments, dtypes and limits as pa_verify.
+ */
+int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                     int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+                     int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                     int max_context_len, float scale, int q_dtype, int kv_dtype,
+                     int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -5,5 +5,5 @@ The kernels live in ``libpa.so`` (HIP, gfx950) behind the C ABI declared in
 synthetic workload generators used by the tests and the benchmark.
 """
 from ._lib import (PAError, decode, decode_append, default_split_tokens,  # noqa: F401
-                   reshape_and_cache, reshape_and_cache_quant, verify, version,
-                   workspace_size)
+                   reshape_and_cache, reshape_and_cache_quant, verify, verify_varlen,
+                   version, workspace_size)

@@ -65,8 +65,11 @@ int default_split(int T, int q_heads, int kv_heads, int head_dim, int kv_dtype) 
 }
 
 // Validates sizes shared by decode and verify and fills the split plan.
+// rows_rule: the call runs on the matrix-core kernel whatever T is (variable-
+// length verify), so the default piece length follows that kernel's rule.
 int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
-                int max_context_len, int kv_dtype, int split_tokens, Plan* plan) {
+                int max_context_len, int kv_dtype, int split_tokens, Plan* plan,
+                bool rows_rule = false) {
   if (num_seqs < 0 || T < 1 || q_heads <= 0 || kv_heads <= 0 || max_context_len < 0)
     return fail(PA_ERR_INVALID_ARG,
                 "invalid sizes: num_seqs=%d num_query_tokens=%d q_heads=%d kv_heads=%d "
@@ -79,7 +82,9 @@ int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
   if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_INT8)
     return fail(PA_ERR_INVALID_ARG, "unknown kv dtype %d", kv_dtype);
-  int st = split_tokens == 0 ? default_split(T, q_heads, kv_heads, head_dim, kv_dtype) : split_tokens;
+  int st = split_tokens == 0
+               ? default_split(rows_rule && T < 2 ? 2 : T, q_heads, kv_heads, head_dim, kv_dtype)
+               : split_tokens;
   if (st <= 0 || st % pa::kBlockSizeHost != 0 || st > pa::kMaxSplitTokens)
     return fail(PA_ERR_INVALID_ARG, "split_tokens %d must be a multiple of %d in [%d, %d]",
                 split_tokens, pa::kBlockSizeHost, pa::kBlockSizeHost, pa::kMaxSplitTokens);
@@ -136,16 +141,23 @@ struct Append {
   bool on = false;
 };
 
+// Variable-length verify: packed query rows with per-sequence offsets.
+struct Varlen {
+  const int32_t* query_start = nullptr;
+  int total = 0;
+  bool on = false;
+};
+
 int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
                   const void* v_cache, const float* k_scale, const float* v_scale,
                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int T,
                   int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
                   int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
                   int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
-                  void* stream, const Append& app = Append()) {
+                  void* stream, const Append& app = Append(), const Varlen& vl = Varlen()) {
   Plan plan;
   int st = plan_pieces(num_seqs, T, q_heads, kv_heads, head_dim, max_context_len, kv_dtype,
-                       split_tokens, &plan);
+                       split_tokens, &plan, vl.on);
   if (st != PA_OK) return st;
   st = check_attention_args(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                             context_lens, num_seqs, kv_heads, block_size, num_blocks,
@@ -167,6 +179,15 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
       return fail(PA_ERR_INVALID_ARG, "null key, value or slot_mapping");
     if (!aligned(app.key, 16) || !aligned(app.value, 16) || !aligned(app.slot_mapping, 8))
       return fail(PA_ERR_INVALID_ARG, "misaligned key, value or slot_mapping");
+  }
+  if (vl.on) {
+    if (vl.total < 0 || long(vl.total) > long(num_seqs) * T)
+      return fail(PA_ERR_INVALID_ARG,
+                  "total_query_tokens %d must be in [0, num_seqs * max_query_tokens = %ld]",
+                  vl.total, long(num_seqs) * T);
+    if (num_seqs > 0 && (!vl.query_start || !aligned(vl.query_start, 4)))
+      return fail(PA_ERR_INVALID_ARG, "query_start must be a 4-byte aligned pointer");
+    if (vl.total == 0) return PA_OK;
   }
   if (num_seqs == 0) return PA_OK;
   const size_t need = plan.total();
@@ -202,8 +223,10 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.new_k = app.key;
   a.new_v = app.value;
   a.slot_mapping = app.slot_mapping;
+  a.query_start = vl.on ? vl.query_start : nullptr;
+  a.total_query_tokens = vl.on ? vl.total : num_seqs * T;
   // Verify calls, and decode over an int8 cache, run on the matrix cores.
-  const bool rows = rows_kernel(T, G, kv_dtype);
+  const bool rows = vl.on || rows_kernel(T, G, kv_dtype);
   hipError_t e = hipSuccess;
   if (rows && app.on) {
     // The matrix-core kernel has no fused write: the cache write runs first,
@@ -222,8 +245,11 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
     m.context_lens = context_lens;
+    m.query_start = a.query_start;
+    m.num_seqs = num_seqs;
+    m.q_heads = q_heads;
     m.rows_per_seq = T * q_heads;
-    m.num_rows = num_seqs * m.rows_per_seq;
+    m.num_rows = vl.on ? vl.total * q_heads : num_seqs * m.rows_per_seq;
     m.max_pieces = plan.max_pieces;
     m.split_tokens = plan.split_tokens;
     m.max_len_clamp = max_blocks_per_seq * block_size;
@@ -356,6 +382,24 @@ int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache
                        context_lens, num_seqs, num_query_tokens, q_heads, kv_heads, head_dim,
                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
                        q_dtype, kv_dtype, split_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                     int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+                     int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                     int max_context_len, float scale, int q_dtype, int kv_dtype,
+                     int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  Varlen vl;
+  vl.query_start = query_start;
+  vl.total = total_query_tokens;
+  vl.on = true;
+  return run_attention(true, out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, num_seqs, max_query_tokens, q_heads, kv_heads, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       q_dtype, kv_dtype, split_tokens, workspace, workspace_bytes, stream,
+                       Append(), vl);
 }
 
 }  // extern "C"

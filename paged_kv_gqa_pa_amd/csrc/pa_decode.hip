@@ -537,7 +537,20 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
   for (int u = 0; u < CH; ++u)
 #pragma unroll
     for (int j = 0; j < PER; ++j) ov0[u][j] = po[size_t(min(u, first - 1)) * D + j * 64 + lane];
-  const int b = row / a.rows_per_seq;
+  int b;
+  if (a.query_start) {
+    // packed rows: the sequence holding token tok is the number of sequence
+    // starts 1..num_seqs at or below it
+    const int tok = row / a.q_heads;
+    int cnt = 0;
+    for (int s0 = 1; s0 <= a.num_seqs; s0 += 64) {
+      const int s = s0 + lane;
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(s <= a.num_seqs && a.query_start[s] <= tok));
+    }
+    b = min(cnt, a.num_seqs - 1);
+  } else {
+    b = row / a.rows_per_seq;
+  }
   const int L = min(a.context_lens[b], a.max_len_clamp);
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
   if (n_pieces <= 1) return;

@@ -55,8 +55,13 @@ struct DecodeArgs {
   const void* new_k;
   const void* new_v;
   const int64_t* slot_mapping;
+  // Variable-length verify only: sequence b's query tokens are packed rows
+  // query_start[b] .. query_start[b+1]-1 of q and out ([total, q_heads,
+  // head_dim]); nullptr for a fixed T per sequence.
+  const int32_t* query_start;
+  int total_query_tokens;
   int num_seqs;
-  int num_query_tokens;  // T (1 for decode)
+  int num_query_tokens;  // T (1 for decode); the largest T_b for variable length
   int q_heads;
   int kv_heads;
   int head_dim;
@@ -75,6 +80,9 @@ struct MergeArgs {
   const float* part_o;
   const float* part_lse;
   const int32_t* context_lens;
+  const int32_t* query_start;  // variable-length verify (rows packed by token), else nullptr
+  int num_seqs;
+  int q_heads;
   int num_rows;
   int rows_per_seq;
   int max_pieces;

@@ -115,9 +115,18 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   const int pair = blockIdx.x - piece * pairs;
   const int b = pair / a.kv_heads;
   const int g = pair - b * a.kv_heads;
-  const int T = a.num_query_tokens;
   const int Hq = a.q_heads;
   const int G = Hq / a.kv_heads;
+  // Sequence b's query tokens: T of them from packed token q0 (fixed T: b * T),
+  // or its own count T_b from the offsets (clamped to the buffer and to T).
+  int T = a.num_query_tokens;
+  int q0 = b * T;
+  if (a.query_start) {
+    const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
+    q0 = min(max(s0, 0), a.total_query_tokens);
+    T = min(max(s1 - s0, 0), min(T, a.total_query_tokens - q0));
+    if (T == 0) return;
+  }
   const int R = T * G;
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   float qpart = 0.0f;
   {
     const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) +
-                       ((size_t(b) * T + t_row) * Hq + h_row) * D + 8 * grp;
+                       ((size_t(q0) + t_row) * Hq + h_row) * D + 8 * grp;
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
       const u32x4 w = n < R ? load16(qp + 32 * c) : u32x4{0u, 0u, 0u, 0u};
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
     }
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int tq = row / G;
-    const size_t orow = (size_t(b) * T + tq) * Hq + size_t(g) * G + (row - tq * G);
+    const size_t orow = (size_t(q0) + tq) * Hq + size_t(g) * G + (row - tq * G);
     if (n_pieces == 1) {
       reinterpret_cast<bf16_t*>(a.out)[orow * D + d].bits = f32_to_bf16(ot * inv);
     } else {
