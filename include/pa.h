@@ -291,6 +291,35 @@ int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* 
                      int max_context_len, float scale, int q_dtype, int kv_dtype,
                      int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_prefill -- chunked prefill over the paged cache: many new tokens per
+ * sequence, causal among themselves (the next kernel on the roadmap of "From
+ * 183 ms to 19 ms per decode step", section "Limits").  The result is the one
+ * pa_verify_varlen defines -- sequence b's T_b = query_start[b + 1] -
+ * query_start[b] new tokens are its last T_b positions (their K/V already in
+ * the cache, e.g. by pa_reshape_and_cache), query token t attends to positions
+ * 0 .. context_lens[b] - T_b + t -- without its limit on rows: any
+ * max_query_tokens, any group size.  Each workgroup covers 64 query rows
+ * (token, head) of one (sequence, KV head) over their whole visible context,
+ * so there are no pieces and no workspace.
+ *
+ * out, q        [total_query_tokens, q_heads, head_dim], bf16, packed by
+ *               sequence as in pa_verify_varlen (rows of out belonging to no
+ *               sequence are not written).
+ * query_start   [num_seqs + 1] int32 device offsets (clamped on the device to
+ *               [0, total_query_tokens] and to max_query_tokens per sequence).
+ * max_query_tokens  the largest T_b (sets the grid).
+ * Supported: PA_BF16 q with a PA_BF16 or PA_INT8 cache (k_scale / v_scale
+ * for int8); head_dim 64 or 128; block_size 16.  Other arguments as
+ * pa_decode; max_context_len is only checked against the table width.
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const float* k_scale, const float* v_scale, const int32_t* block_tables,
+               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+               int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+               int max_context_len, float scale, int q_dtype, int kv_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

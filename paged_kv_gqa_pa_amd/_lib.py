@@ -25,7 +25,8 @@ PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 
 EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_quant",
             "pa_default_split_tokens",
-            "pa_workspace_size", "pa_decode", "pa_decode_append", "pa_verify", "pa_verify_varlen"]
+            "pa_workspace_size", "pa_decode", "pa_decode_append", "pa_verify", "pa_verify_varlen",
+            "pa_prefill"]
 
 _DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_INT8}
 
@@ -71,6 +72,10 @@ def _load():
     lib.pa_verify_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i, i, i, i, i, i, i, i, i, i,
                                      f, i, i, i, vp, sz, vp]
+    lib.pa_prefill.restype = i
+    lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                               i, i, i, i, i, i, i, i, i, i,
+                               f, i, i, vp]
     lib.pa_verify.restype = i
     lib.pa_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                               i, i, i, i, i, i, i, i, i,
@@ -289,6 +294,43 @@ def verify_varlen(out, q, k_cache, v_cache, block_tables, context_lens, query_st
         _ptr(block_tables), _ptr(context_lens), _ptr(query_start), N, total, T, Hq, Hkv, D, BS,
         NB, block_tables.shape[1], int(max_context_len), float(scale), _DTYPE[q.dtype], kvd,
         int(split_tokens), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+            max_query_tokens, k_scale=None, v_scale=None, max_context_len=None, stream=None):
+    """Chunked prefill: q/out [total_query_tokens, q_heads, head_dim] packed by sequence,
+    query_start int32 [num_seqs+1]; sequence b's tokens are its last positions."""
+    _need(q, "q", ndim=3)
+    _need(out, "out", dtype=q.dtype, ndim=3)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _need(query_start, "query_start", dtype=torch.int32, ndim=1)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    Hkv, NB, BS, D = k_cache.shape
+    total, Hq, Dq = q.shape
+    N = block_tables.shape[0]
+    if Dq != D or context_lens.shape[0] != N or query_start.shape[0] != N + 1:
+        raise ValueError("q, block_tables, context_lens and query_start disagree")
+    kvd = _DTYPE[k_cache.dtype]
+    if kvd == PA_INT8:
+        for nm, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{nm} is required for an int8 cache")
+            _need(s, nm, dtype=torch.float32, ndim=2)
+    else:
+        k_scale = v_scale = None
+    mcl = block_tables.shape[1] * BS if max_context_len is None else int(max_context_len)
+    _check(_load().pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), _ptr(query_start), N, total,
+        int(max_query_tokens), Hq, Hkv, D, BS, NB, block_tables.shape[1], mcl, float(scale),
+        _DTYPE[q.dtype], kvd, _stream(stream)))
     return out
 
 

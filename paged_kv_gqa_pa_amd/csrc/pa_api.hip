@@ -384,6 +384,67 @@ int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache
                        q_dtype, kv_dtype, split_tokens, workspace, workspace_bytes, stream);
 }
 
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const float* k_scale, const float* v_scale, const int32_t* block_tables,
+               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+               int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+               int max_context_len, float scale, int q_dtype, int kv_dtype, void* stream) {
+  if (num_seqs < 0 || max_query_tokens < 1 || q_heads <= 0 || kv_heads <= 0 ||
+      max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "invalid sizes: num_seqs=%d max_query_tokens=%d q_heads=%d kv_heads=%d "
+                "max_context_len=%d",
+                num_seqs, max_query_tokens, q_heads, kv_heads, max_context_len);
+  if (q_heads % kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "q_heads (%d) is not a multiple of kv_heads (%d)", q_heads,
+                kv_heads);
+  if (!pa::prefill_supported(q_dtype, kv_dtype, head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "prefill not built for q=%d kv=%d head_dim=%d", q_dtype,
+                kv_dtype, head_dim);
+  int st = check_attention_args(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                context_lens, num_seqs, kv_heads, block_size, num_blocks,
+                                max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype);
+  if (st != PA_OK) return st;
+  if (total_query_tokens < 0 || long(total_query_tokens) > long(num_seqs) * max_query_tokens)
+    return fail(PA_ERR_INVALID_ARG,
+                "total_query_tokens %d must be in [0, num_seqs * max_query_tokens = %ld]",
+                total_query_tokens, long(num_seqs) * max_query_tokens);
+  const int G = q_heads / kv_heads;
+  const long rows = long(max_query_tokens) * G;
+  const long tiles = (rows + 16L * pa::prefill_waves() - 1) / (16L * pa::prefill_waves());
+  if (rows > 2147483647L || long(total_query_tokens) * q_heads > 2147483647L ||
+      tiles * num_seqs * kv_heads > kMaxGrid)
+    return fail(PA_ERR_UNSUPPORTED, "too many query rows or workgroups");
+  if (num_seqs == 0 || total_query_tokens == 0) return PA_OK;
+  if (!query_start || !aligned(query_start, 4))
+    return fail(PA_ERR_INVALID_ARG, "query_start must be a 4-byte aligned pointer");
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.total_query_tokens = total_query_tokens;
+  a.num_seqs = num_seqs;
+  a.num_query_tokens = max_query_tokens;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale = scale;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
                      const int32_t* context_lens, const int32_t* query_start, int num_seqs,

@@ -1,0 +1,313 @@
+// Paged chunked prefill on the matrix cores: many new tokens per sequence,
+// causal among themselves, over the paged cache -- the step before decode that
+// "From 183 ms to 19 ms per decode step" names next in its "Limits" section.
+// Sequence b's T_b new tokens are its last T_b positions (their K/V already in
+// the cache); token t sees positions 0 .. L_b - T_b + t, as in verify.
+//
+// Work item: one workgroup of NW waves per (tile of 16 * NW query rows, KV
+// head, sequence).  Row r of a sequence is query token r / G of head
+// g * G + r % G; wave w owns rows 16w .. 16w + 15 of the tile over the whole
+// visible context, so no partial results leave the workgroup.  The cache is
+// walked in stages of KB blocks (64 positions): the workgroup stages a
+// stage's K and V tiles in LDS with direct-to-LDS buffer loads (double
+// buffered, the next stage in flight while this one is used), and every wave
+// reads the shared tiles for its own rows.  A block's buffer resource covers
+// only its rows inside the needed range, so positions past it arrive as zeros
+// (finite: their weights are exactly 0) and cost no memory traffic.
+//
+// Per wave and 16-position tile the products are those of the verify kernel:
+// scores S^T = K Q^T on 16x16x32 products (K from LDS as A, the query rows
+// as B), P as the A operand of 16x16x16 products against V (bf16: transposed
+// LDS reads; int8: codes turned by an identity product), the softmax per row
+// with a reference maximum and delayed rescale.
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_kernels.h"
+#include "pa_mfma.h"
+
+namespace pa {
+namespace {
+
+template <typename KV, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
+  constexpr bool kInt8 = __is_same(KV, i8_t);
+  constexpr int ROWB = D * int(sizeof(KV));      // bytes per key row
+  constexpr int NL = ROWB / 64;                  // 1 KiB loads per 16-row tile
+  constexpr int NQ = D / 32;                     // score products per tile
+  constexpr int NT = D / 16;                     // output blocks of 16 dims
+  constexpr int TILE_BYTES = kBlockSize * ROWB;
+  constexpr int KB = 4;                          // cache blocks per stage
+  constexpr int STAGE = 2 * KB * TILE_BYTES;     // K tiles, then V tiles
+  constexpr int LOADS = 2 * KB * NL;             // 1 KiB loads per stage
+  static_assert(LOADS % NW == 0, "stage loads must split evenly over the waves");
+  constexpr int LPW = LOADS / NW;                // loads per wave per stage
+  constexpr int CPR = ROWB / 16;                 // 16-byte chunks per key row
+  constexpr int RPB = ROWB >= 256 ? 1 : 256 / ROWB;
+  constexpr bool kSwizzleV = kInt8;
+  using M = MOps<KV>;
+
+  // Tiles of later rows see more positions: they are handed out first.
+  const int pairs = a.num_seqs * a.kv_heads;
+  const int tiles = int(gridDim.x) / pairs;
+  const int tile = tiles - 1 - int(blockIdx.x) / pairs;
+  const int pair = int(blockIdx.x) % pairs;
+  const int b = pair / a.kv_heads;
+  const int g = pair - b * a.kv_heads;
+  const int Hq = a.q_heads;
+  const int G = Hq / a.kv_heads;
+  const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
+  const int q0 = min(max(s0, 0), a.total_query_tokens);
+  const int T = min(max(s1 - s0, 0), min(a.num_query_tokens, a.total_query_tokens - q0));
+  const int R = T * G;
+  const int row0 = tile * NW * kRows;
+  if (row0 >= R) return;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;     // key row of an operand read / query row of S, P
+  const int grp = lane >> 4;   // 8-dim group of a score product / key quad of S, P, O
+  const int wrow0 = row0 + wave * kRows;
+  const int row = wrow0 + n;
+  const bool row_ok = row < R;
+  const int t_row = row / G;
+  const int h_row = g * G + (row - t_row * G);
+
+  // Query rows as the B operand of score product c: lane (row n, group grp)
+  // holds q[n][32c + 8grp .. +7] (fp16 for an int8 cache).
+  u32x4 qb[NQ];
+  float qpart = 0.0f;
+  {
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) +
+                       ((size_t(q0) + t_row) * Hq + h_row) * D + 8 * grp;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      const u32x4 w = row_ok ? load16(qp + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kInt8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e]), bf16_hi(w[e]));
+          qb[c][e] = __builtin_bit_cast(uint32_t, hp);
+          qpart += float(hp[0]) + float(hp[1]);
+        }
+      } else {
+        qb[c] = w;
+      }
+    }
+  }
+  const float qsum = kInt8 ? add_xor32(add_xor16(qpart)) : 0.0f;
+
+  const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
+  const int last_vis = row_ok ? L - T + t_row : -1;   // last position row n sees
+  // Positions the workgroup needs (through its last row) and this wave needs.
+  const int t_last = (min(row0 + NW * kRows, R) - 1) / G;
+  const int kend = min(max(L - T + t_last + 1, 0), L);
+  const int w_kend = wrow0 < R ? min(max(L - T + (min(wrow0 + kRows, R) - 1) / G + 1, 0), L) : 0;
+  const int nblk = cdiv(kend, kBlockSize);
+  const int nst = cdiv(nblk, KB);
+
+  const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
+  const size_t head_blocks = size_t(g) * a.num_blocks;
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache);
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache);
+  const float sc = a.scale * kLog2e;
+
+  // The two stages are separate LDS objects, so waiting for one stage's
+  // direct-to-LDS loads does not also wait for the other's.
+  __shared__ __attribute__((aligned(16))) char s_st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char s_st1[STAGE];
+  auto sw = [](int r, int k) { return r * ROWB + 16 * (k ^ ((r / RPB) & (CPR - 1))); };
+  int src_off[NL];
+#pragma unroll
+  for (int c = 0; c < NL; ++c) {
+    const int slot = 64 * c + lane;
+    const int r = slot / CPR, p = slot % CPR;
+    src_off[c] = r * ROWB + 16 * (p ^ ((r / RPB) & (CPR - 1)));
+  }
+  // This wave's share of stage st: loads wave*LPW .. +LPW-1 of the stage's
+  // 2*KB*NL (K tiles, then V tiles; NL loads per tile).  An int8 stage's
+  // block scales are requested first, into ks / vs, so the wait for the
+  // stage's tiles covers them too.
+  auto fetch = [&](int st, char* buf, float (&ks)[KB], float (&vs)[KB]) {
+    if constexpr (kInt8) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int blk = st * KB + kb;
+        const bool need = blk * kBlockSize < kend;
+        const int phys = need ? min(max(bt[blk], 0), a.num_blocks - 1) : 0;
+        ks[kb] = need ? a.k_scale[head_blocks + phys] : 0.0f;
+        vs[kb] = need ? a.v_scale[head_blocks + phys] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int li = wave * LPW + i;
+      const bool isv = li >= KB * NL;
+      const int kb = (li / NL) % KB;
+      const int c = li % NL;
+      const int blk = st * KB + kb;
+      const int valid = min(max(kend - blk * kBlockSize, 0), kBlockSize);
+      const int phys = valid > 0 ? min(max(bt[blk], 0), a.num_blocks - 1) : 0;
+      const size_t tile_off = (head_blocks + size_t(phys)) * TILE_BYTES;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc((isv ? vbase : kbase) + tile_off, valid * ROWB);
+      const int off = (isv && !kSwizzleV) ? 1024 * c + 16 * lane : src_off[c];
+      buffer_load16_to_lds(r, buf + (isv ? KB + kb : kb) * TILE_BYTES + 1024 * c, off);
+    }
+  };
+
+  u32x2 ident;
+  {
+    uint32_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = 4 * grp + j == n ? M::kOne : 0u;
+    ident = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+  }
+  const f32x4 vinit = {M::kVInit, M::kVInit, M::kVInit, M::kVInit};
+
+  constexpr float kSlack = 8.0f;
+  float m = kNegInf;
+  float lsum = 0.0f;
+  f32x4 o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One 16-position tile (block blk, staged at kb of buf) for this wave's rows.
+  auto process = [&](const char* buf, int kb, int blk, float ks, float vs) {
+    const char* const sk = buf + kb * TILE_BYTES;
+    const char* const sv = buf + (KB + kb) * TILE_BYTES;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      u32x4 kop;
+      if constexpr (kInt8) {
+        const int k = (32 * c + 8 * grp) / 16;
+        const uint2 w = *reinterpret_cast<const uint2*>(sk + sw(n, k) + 8 * (grp & 1));
+        kop = codes8_f16(w.x, w.y);
+      } else {
+        kop = *reinterpret_cast<const u32x4*>(sk + sw(n, 4 * c + grp));
+      }
+      s = M::qk(kop, qb[c], s);
+    }
+    const float ssc = sc * ks;
+    float tmax = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pos = blk * kBlockSize + 4 * grp + j;
+      const float x = (kInt8 ? s[j] - kI8Bias * qsum : s[j]) * ssc;
+      s[j] = pos <= last_vis ? x : kNegInf;
+      tmax = fmaxf(tmax, s[j]);
+    }
+    tmax = max_xor32(max_xor16(tmax));
+    if (__builtin_amdgcn_ballot_w64(tmax > m + kSlack) != 0) {
+      const float mnew = fmaxf(m, tmax);
+      const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float ar = __shfl(alpha, 4 * grp + j);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[t][j] *= ar;
+      }
+    }
+    const float mref = m == kNegInf ? 0.0f : m;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[j] - mref);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    const u32x2 pa = {M::pack_round(p[0] * vs, p[1] * vs), M::pack_round(p[2] * vs, p[3] * vs)};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      u32x2 vb;
+      if constexpr (kInt8) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(sv + sw(n, t) + 4 * grp) ^ 0x80808080u;
+        const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
+        vb = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
+      } else {
+        const uint16_t* col = reinterpret_cast<const uint16_t*>(sv) + 4 * grp * D + 16 * t + n;
+        uint32_t e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[j] = col[j * D];
+        vb = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+      }
+      o[t] = M::mm16(pa, vb, o[t]);
+    }
+  };
+
+  // Stage st is used from buffer st % 2 while stage st + 1 loads into the
+  // other; the barrier after a stage frees its buffer for stage st + 2.
+  float ks_cur[KB] = {}, vs_cur[KB] = {}, ks_nxt[KB] = {}, vs_nxt[KB] = {};
+  if (nst > 0) fetch(0, s_st0, ks_cur, vs_cur);
+  for (int st = 0; st < nst; ++st) {
+    char* const cur = (st & 1) ? s_st1 : s_st0;
+    if (st + 1 < nst) {
+      fetch(st + 1, (st & 1) ? s_st0 : s_st1, ks_nxt, vs_nxt);
+      __builtin_amdgcn_s_waitcnt((LPW & 15) | ((LPW >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+    }
+    __asm__ __volatile__("" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int blk = st * KB + kb;
+      if (blk * kBlockSize < w_kend)   // uniform per wave
+        process(cur, kb, blk, kInt8 ? ks_cur[kb] : 1.0f, kInt8 ? vs_cur[kb] : 1.0f);
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      ks_cur[kb] = ks_nxt[kb];
+      vs_cur[kb] = vs_nxt[kb];
+    }
+    __syncthreads();
+  }
+
+  // Row totals, then O / l per row, rounded to bf16.
+  const float lrow = add_xor32(add_xor16(lsum));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wrow0 + 4 * grp + j;
+    const float lr = __shfl(lrow, 4 * grp + j);
+    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+    if (r < R) {
+      const int tq = r / G;
+      const size_t orow = (size_t(q0) + tq) * Hq + size_t(g) * G + (r - tq * G);
+      bf16_t* dst = reinterpret_cast<bf16_t*>(a.out) + orow * D + n;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) dst[16 * t].bits = f32_to_bf16(o[t][j] * inv);
+    }
+  }
+}
+
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+
+template <typename KV>
+hipError_t launch_prefill_t(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int NW = PA_PREFILL_WAVES;
+  const int G = a.q_heads / a.kv_heads;
+  const long tiles = cdiv(a.num_query_tokens * G, NW * kRows);
+  const long wgs = tiles * a.num_seqs * a.kv_heads;
+  if (a.head_dim == 128)
+    prefill_rows<KV, 128, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+  else
+    prefill_rows<KV, 64, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_waves() { return PA_PREFILL_WAVES; }
+
+bool prefill_supported(int q_dtype, int kv_dtype, int head_dim) {
+  return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kI8) &&
+         (head_dim == 64 || head_dim == 128);
+}
+
+hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream) {
+  if (a.kv_dtype == kI8) return launch_prefill_t<i8_t>(a, stream);
+  return launch_prefill_t<bf16_t>(a, stream);
+}
+
+}  // namespace pa

@@ -34,59 +34,10 @@
 
 #include "pa_device.h"
 #include "pa_kernels.h"
+#include "pa_mfma.h"
 
 namespace pa {
 namespace {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
-
-constexpr int kRows = 16;  // query rows of one matrix tile
-
-// Products and conversions per cache element type.
-template <typename KV> struct MOps;
-template <> struct MOps<bf16_t> {
-  static constexpr uint32_t kOne = 0x3F80u;  // bf16 1.0
-  static constexpr float kVInit = 0.0f;
-  __device__ static f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
-                                                  __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
-  }
-  __device__ static f32x4 mm16(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-  }
-  // Two fp32 values that are bf16 numbers: their high halves.
-  __device__ static uint32_t pack_exact(float lo, float hi) {
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-  }
-  __device__ static uint32_t pack_round(float lo, float hi) {
-    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
-  }
-};
-template <> struct MOps<i8_t> {
-  static constexpr uint32_t kOne = 0x3C00u;  // fp16 1.0
-  static constexpr float kVInit = -kI8Bias;
-  __device__ static f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, k),
-                                                 __builtin_bit_cast(h16x8, q), c, 0, 0, 0);
-  }
-  __device__ static f32x4 mm16(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4, a),
-                                                 __builtin_bit_cast(h16x4, b), c, 0, 0, 0);
-  }
-  __device__ static uint32_t pack_exact(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-  }
-  __device__ static uint32_t pack_round(float lo, float hi) { return pack_exact(lo, hi); }
-};
-
-// Eight codes (two words) as the fp16 numbers c + 1152.
-__device__ __forceinline__ u32x4 codes8_f16(uint32_t w0, uint32_t w1) {
-  const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
-  return u32x4{f16pair_lo(u0), f16pair_hi(u0), f16pair_lo(u1), f16pair_hi(u1)};
-}
 
 template <typename KV, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
