@@ -4,9 +4,12 @@ One step = for each of 28 layers: pa_reshape_and_cache of one new K/V token
 per sequence, then pa_decode of one query token per sequence (64 sequences,
 16 query / 8 KV heads, head_dim 128, bf16, block size 16, context = 256-token
 prompt + U{1..256} generated tokens, a shuffled pool of 16384 blocks per
-layer, one shared block table).  The step is captured once in a HIP graph and
-replayed (the pages' change 4: graphs per batch bucket); ``--eager`` launches
-every kernel from Python instead.
+layer, one shared block table).  Each step first makes one work plan
+(pa_plan: the step's (sequence, piece) units ordered longest first, shared by
+the 28 layers); ``--no-plan`` starts the work in the natural order instead.
+The step is captured once in a HIP graph and replayed (the pages' change 4:
+graphs per batch bucket); ``--eager`` launches every kernel from Python
+instead.
 
 Printed: one JSON line with tokens/s for the whole step (``value``), the decode
 kernel's achieved HBM bandwidth on algorithmic bytes against the 8 TB/s peak
@@ -45,6 +48,11 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 256 MiB device-to-device copy (known bytes) so hardware "
                         "byte counters can be scaled")
+    p.add_argument("--no-plan", action="store_true",
+                   help="start the attention work in the natural order instead of a work plan")
+    p.add_argument("--natural", action="store_true",
+                   help="also time the 28 decode launches in the natural order (same kernel "
+                        "symbol as the planned launches: leave off for profiled runs)")
     p.add_argument("--no-other-workloads", action="store_true",
                    help="skip the per-call timings of the other workloads")
     p.add_argument("--traffic-file", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -74,7 +82,7 @@ def attention_bytes(lens, T, q_heads, kv_heads, head_dim, kv_elem, q_elem=2):
     return kv + qo + blocks * 4 + len(lens) * 4 + scales
 
 
-def other_workloads(torch, pa, wl, dev, reps=10):
+def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
     """Per-call timings of the other seeded workloads.  Each call reads its own
     replica of the caches (enough replicas to pass 1 GB per round, far beyond the
     256 MB last-level cache), launched from one HIP graph; events on the launch
@@ -123,6 +131,11 @@ def other_workloads(torch, pa, wl, dev, reps=10):
         wsb = pa.workspace_size(N, T, Hq, Hkv, D, spec.max_len, kdt, split)
         ws = torch.zeros(max(256, wsb), dtype=torch.uint8, device=dev)
         fn = pa.verify if T > 1 else pa.decode
+        # one work plan for the call's tables and lengths (made once, as once per step)
+        plan = None
+        if use_plan and not varlen:
+            plan = pa.make_plan(bt, cl, Hq, Hkv, D, spec.max_len, kdt, num_query_tokens=T,
+                                split_tokens=split)
 
         def calls():
             for r in range(R):
@@ -131,7 +144,7 @@ def other_workloads(torch, pa, wl, dev, reps=10):
                                      spec.max_len, T, split_tokens=split, workspace=ws)
                 else:
                     fn(o, q, kc[r], vc[r], bt, cl, 1.0 / float(np.sqrt(D)), spec.max_len, ks, vs,
-                       split_tokens=split, workspace=ws)
+                       split_tokens=split, workspace=ws, plan=plan)
         calls()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -151,7 +164,8 @@ def other_workloads(torch, pa, wl, dev, reps=10):
         out[name] = {"us_per_call": round(us, 2), "algorithmic_bytes": alg,
                      "hbm_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "query_tokens_per_s": round(total / (us * 1e-6), 1),
-                     "split_tokens": split, "kernel": "rows_pass1" if (T > 1 or elem == 1) else "decode_pass1",
+                     "split_tokens": split, "work_plan": plan is not None,
+                     "kernel": "rows_pass1" if (T > 1 or elem == 1 or Hq // Hkv >= 4) else "decode_pass1",
                      "shape": f"N={N} T={'1..5 per sequence, ' + str(total) + ' rows' if varlen else T} "
                               f"Hq={Hq} Hkv={Hkv} D={D} kv={spec.kv_dtype}"}
         print(f"[bench] {name}: {us:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}%)",
@@ -354,26 +368,38 @@ def main():
     max_len = spec.max_len
     ws_bytes = pa.workspace_size(N, 1, Hq, Hkv, D, max_len, torch.bfloat16, args.split)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    # One work plan per step (the step's tables and lengths serve all 28 layers).
+    plan = None
+    if not args.no_plan:
+        plan = torch.empty(pa.plan_size(N, 1, Hq, Hkv, D, max_len, torch.bfloat16, args.split),
+                           dtype=torch.uint8, device=dev)
+
+    def make_plan():
+        if plan is not None:
+            pa.make_plan(bt, cl, Hq, Hkv, D, max_len, torch.bfloat16, split_tokens=args.split,
+                         plan=plan)
     scale = 1.0 / float(np.sqrt(D))
     torch.cuda.synchronize()
     print(f"[bench] caches ready: {2 * Lyr * kc[0].numel() * 2 / 2**30:.1f} GiB, "
           f"workspace {ws_bytes} B", flush=True)
 
     def step():
+        make_plan()
         for l in range(Lyr):
             pa.reshape_and_cache(nks[l], nvs[l], kc[l], vc[l], sm)
             pa.decode(outs[l], qs[l], kc[l], vc[l], bt, cl, scale, max_len,
-                      split_tokens=args.split, workspace=ws)
+                      split_tokens=args.split, workspace=ws, plan=plan)
 
     def step_fused():
+        make_plan()
         for l in range(Lyr):
             pa.decode_append(outs[l], qs[l], nks[l], nvs[l], kc[l], vc[l], sm, bt, cl, scale,
-                             max_len, split_tokens=args.split, workspace=ws)
+                             max_len, split_tokens=args.split, workspace=ws, plan=plan)
 
-    def decode_only():
+    def decode_only(use_plan=True):
         for l in range(Lyr):
             pa.decode(outs[l], qs[l], kc[l], vc[l], bt, cl, scale, max_len,
-                      split_tokens=args.split, workspace=ws)
+                      split_tokens=args.split, workspace=ws, plan=plan if use_plan else None)
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -383,10 +409,13 @@ def main():
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
 
+    run_natural = None
     if args.eager:
         run_step = step
         run_fused = step_fused
         run_decode = decode_only
+        if args.natural and plan is not None:
+            run_natural = lambda: decode_only(False)
     else:
         g_step = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_step):
@@ -400,6 +429,11 @@ def main():
         run_step = g_step.replay
         run_fused = g_fused.replay
         run_decode = g_dec.replay
+        if args.natural and plan is not None:
+            g_nat = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_nat):
+                decode_only(False)
+            run_natural = g_nat.replay
         for _ in range(max(1, args.warmup)):
             run_step()
         torch.cuda.synchronize()
@@ -453,7 +487,21 @@ def main():
     per_pass = sorted(dv[i].elapsed_time(dv[i + 1]) * 1e3 / Lyr for i in range(args.decode_reps))
     bytes_launch = algorithmic_bytes(lens, Hq, Hkv, D)
     gbps = bytes_launch / (us_decode * 1e-6) / 1e9
-    print(f"[bench] decode {us_decode:.2f} us/launch, {gbps:.0f} GB/s", flush=True)
+    print(f"[bench] decode {us_decode:.2f} us/launch, {gbps:.0f} GB/s"
+          f"{' (work plan)' if plan is not None else ''}", flush=True)
+    natural = None
+    if run_natural is not None:
+        torch.cuda.synchronize()
+        n0, n1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n0.record()
+        for _ in range(args.decode_reps):
+            run_natural()
+        n1.record()
+        torch.cuda.synchronize()
+        us_nat = n0.elapsed_time(n1) * 1e3 / (args.decode_reps * Lyr)
+        natural = {"us_per_launch": round(us_nat, 3),
+                   "gbps": round(bytes_launch / (us_nat * 1e-6) / 1e9, 1)}
+        print(f"[bench] decode, natural order {us_nat:.2f} us/launch", flush=True)
 
     # Reference reads: a plain streaming read of four layer caches (4 x 512 MiB,
     # each launch far beyond the last-level cache), and the decode's own tile
@@ -526,16 +574,20 @@ def main():
         "config": {"workload": WORKLOAD, "num_seqs": N, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "block_size": 16, "layers": Lyr, "num_blocks_per_layer": NB,
                    "context": "256 + U{1..256} (new token included)",
-                   "step": "28 x (reshape_and_cache + decode)",
+                   "step": ("28 x (reshape_and_cache + decode)" if plan is None else
+                            "pa_plan + 28 x (reshape_and_cache + decode with the plan)"),
                    "launch": "eager" if args.eager else "hipgraph",
                    "split_tokens": args.split or pa.default_split_tokens(Hq, Hkv, D, torch.bfloat16)},
         "fused_step": {"ms_per_step": round(ms_fused, 4), "tokens_per_s": round(N / (ms_fused / 1e3), 1),
-                       "entry_point": "pa_decode_append (cache write + decode in one launch)"},
+                       "entry_point": "pa_decode_append (cache write + decode in one launch)" +
+                                      ("" if plan is None else ", after one pa_plan per step")},
         "hbm_gbps": round(gbps, 1),
         "pct_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_pass1",
+                     "work_plan": plan is not None,
+                     "natural_order": natural,
                      "us_per_launch": round(us_decode, 3), "algorithmic_bytes_per_launch": bytes_launch,
                      "us_per_launch_over_passes": {"median": round(per_pass[len(per_pass) // 2], 3),
                                                    "min": round(per_pass[0], 3),
@@ -549,7 +601,7 @@ def main():
                                "pieces) with no arithmetic, over the same 28 layers"},
     }
     if not args.no_other_workloads:
-        res["other_workloads"] = other_workloads(torch, pa, wl, dev)
+        res["other_workloads"] = other_workloads(torch, pa, wl, dev, use_plan=not args.no_plan)
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)

@@ -259,6 +259,80 @@ int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache
               void* stream);
 
 /*
+ * Work plans -- the order in which a call's work is started.
+ *
+ * pa_decode and pa_verify split their work into one unit per (sequence, piece
+ * of context, KV head) and start the units in a fixed natural order.  Each
+ * unit's arithmetic depends on the unit alone, so the order changes no bit of
+ * any result; it changes how evenly the GPU is loaded.  With lengths that
+ * differ, a long unit that happens to start late finishes the launch alone;
+ * started longest first, the long units overlap the short ones.  A plan is
+ * that order, computed on the device from the step's lengths.  The decode
+ * step of "From 183 ms to 19 ms per decode step" ("Four changes, one profile
+ * at a time", change 4) hands every layer the same block tables and lengths,
+ * so one pa_plan per step serves the attention calls of all its layers.
+ *
+ * pa_plan_size -- bytes of a plan for these sizes (arguments as
+ *   pa_workspace_size; num_query_tokens is 1 for decode, T for verify, and
+ *   split_tokens 0 resolves as in the attention calls).  Returns 0 and sets
+ *   pa_last_error on invalid sizes or when num_seqs * ceil(max_context_len /
+ *   split_tokens) exceeds 8192 units.
+ *
+ * pa_plan -- writes the plan: the (sequence, piece) units sorted by their
+ *   tile count, longest first (units of equal length in any order), each with
+ *   its sequence, piece, context length and a COPY of the piece's block-table
+ *   entries.  block_tables and context_lens as for pa_decode (device memory,
+ *   read by the plan kernel on `stream`); plan: device memory of at least
+ *   pa_plan_size(...) bytes, 16-byte aligned, written entirely by this call.
+ *   The other arguments must be those of the attention calls that use it.
+ *
+ * pa_decode_planned, pa_decode_append_planned, pa_verify_planned -- pa_decode,
+ *   pa_decode_append and pa_verify, started in the plan's order, with results
+ *   identical bit for bit to the unplanned calls.  plan / plan_bytes: a plan
+ *   from pa_plan (plan_bytes >= pa_plan_size(...) for the call's sizes, else
+ *   PA_ERR_INVALID_ARG).  The call takes each unit's length and block-table
+ *   entries from the plan, not from block_tables / context_lens: the plan must
+ *   be made again whenever the tables or lengths change (in a decode step:
+ *   once, after the step's tables and lengths are written, before the first
+ *   layer).  A plan made for other sizes (sequences, piece length, table
+ *   width) is detected on the device and ignored: the call then runs in the
+ *   natural order.  Calls that use one plan may run concurrently; pa_plan
+ *   must not overwrite it while they run.
+ */
+size_t pa_plan_size(int num_seqs, int num_query_tokens, int q_heads, int kv_heads,
+                    int head_dim, int max_context_len, int kv_dtype, int split_tokens);
+
+int pa_plan(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+            int num_query_tokens, int q_heads, int kv_heads, int head_dim,
+            int max_blocks_per_seq, int max_context_len, int kv_dtype, int split_tokens,
+            void* plan, size_t plan_bytes, void* stream);
+
+int pa_decode_planned(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int q_heads, int kv_heads,
+                      int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, float scale, int q_dtype, int kv_dtype,
+                      int split_tokens, void* workspace, size_t workspace_bytes,
+                      const void* plan, size_t plan_bytes, void* stream);
+
+int pa_decode_append_planned(void* out, const void* q, const void* key, const void* value,
+                             void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int q_heads, int kv_heads, int head_dim,
+                             int block_size, int num_blocks, int max_blocks_per_seq,
+                             int max_context_len, float scale, int q_dtype, int kv_dtype,
+                             int split_tokens, void* workspace, size_t workspace_bytes,
+                             const void* plan, size_t plan_bytes, void* stream);
+
+int pa_verify_planned(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int num_query_tokens,
+                      int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
+                      int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
+                      int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+                      const void* plan, size_t plan_bytes, void* stream);
+
+/*
  * pa_verify_varlen -- pa_verify with a number of new tokens per sequence:
  * T_b = query_start[b + 1] - query_start[b] (0 .. max_query_tokens), where
  * the pages pad every sequence to k+1 ("From 183 ms to 19 ms per decode

@@ -26,7 +26,8 @@ PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_quant",
             "pa_default_split_tokens",
             "pa_workspace_size", "pa_decode", "pa_decode_append", "pa_verify", "pa_verify_varlen",
-            "pa_prefill"]
+            "pa_prefill", "pa_plan_size", "pa_plan", "pa_decode_planned",
+            "pa_decode_append_planned", "pa_verify_planned"]
 
 _DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_INT8}
 
@@ -80,6 +81,16 @@ def _load():
     lib.pa_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                               i, i, i, i, i, i, i, i, i,
                               f, i, i, i, vp, sz, vp]
+    lib.pa_plan_size.restype = sz
+    lib.pa_plan_size.argtypes = [i, i, i, i, i, i, i, i]
+    lib.pa_plan.restype = i
+    lib.pa_plan.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.pa_decode_planned.restype = i
+    lib.pa_decode_planned.argtypes = lib.pa_decode.argtypes[:-1] + [vp, sz, vp]
+    lib.pa_decode_append_planned.restype = i
+    lib.pa_decode_append_planned.argtypes = lib.pa_decode_append.argtypes[:-1] + [vp, sz, vp]
+    lib.pa_verify_planned.restype = i
+    lib.pa_verify_planned.argtypes = lib.pa_verify.argtypes[:-1] + [vp, sz, vp]
     _lib = lib
     return lib
 
@@ -135,6 +146,44 @@ def workspace_size(num_seqs: int, num_query_tokens: int, q_heads: int, kv_heads:
                                      max_context_len, _DTYPE[kv_dtype], split_tokens)
 
 
+def plan_size(num_seqs: int, num_query_tokens: int, q_heads: int, kv_heads: int, head_dim: int,
+              max_context_len: int, kv_dtype: torch.dtype, split_tokens: int = 0) -> int:
+    """Bytes of a work plan for these sizes (0 with pa_last_error set when none is possible)."""
+    return _load().pa_plan_size(num_seqs, num_query_tokens, q_heads, kv_heads, head_dim,
+                                max_context_len, _DTYPE[kv_dtype], split_tokens)
+
+
+def make_plan(block_tables, context_lens, q_heads, kv_heads, head_dim, max_context_len,
+              kv_dtype: torch.dtype, num_query_tokens=1, split_tokens=0, plan=None, stream=None):
+    """Work plan (longest units first) for the attention calls of one step; returns the plan
+    buffer (a uint8 tensor, allocated when `plan` is None)."""
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    N = block_tables.shape[0]
+    if context_lens.shape[0] != N:
+        raise ValueError("block_tables and context_lens disagree")
+    kvd = _DTYPE[kv_dtype]
+    need = _load().pa_plan_size(N, int(num_query_tokens), q_heads, kv_heads, head_dim,
+                                int(max_context_len), kvd, int(split_tokens))
+    if need == 0:
+        raise PAError(PA_ERR_UNSUPPORTED, _load().pa_last_error().decode())
+    if plan is None:
+        plan = torch.empty(need, dtype=torch.uint8, device=block_tables.device)
+    _need(plan, "plan")
+    _check(_load().pa_plan(_ptr(block_tables), _ptr(context_lens), N, int(num_query_tokens),
+                           q_heads, kv_heads, head_dim, block_tables.shape[1],
+                           int(max_context_len), kvd, int(split_tokens), _ptr(plan),
+                           plan.numel() * plan.element_size(), _stream(stream)))
+    return plan
+
+
+def _plan_args(plan):
+    if plan is None:
+        return None, 0
+    _need(plan, "plan")
+    return _ptr(plan), plan.numel() * plan.element_size()
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     """Write key/value [num_tokens, kv_heads, head_dim] into the caches at slot_mapping."""
     _need(key, "key", ndim=3)
@@ -183,7 +232,7 @@ def reshape_and_cache_quant(key, value, k_cache, v_cache, k_scale, v_scale, slot
 
 
 def _attention(fn_verify: bool, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-               max_context_len, k_scale, v_scale, split_tokens, workspace, stream):
+               max_context_len, k_scale, v_scale, split_tokens, workspace, stream, plan=None):
     _need(q, "q")
     _need(out, "out", dtype=q.dtype)
     if out.shape != q.shape:
@@ -223,34 +272,39 @@ def _attention(fn_verify: bool, out, q, k_cache, v_cache, block_tables, context_
         _need(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib_ = _load()
+    pp = _plan_args(plan)
     if fn_verify:
-        st = lib_.pa_verify(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
-                            _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), N, T, Hq, Hkv,
-                            D, BS, NB, block_tables.shape[1], int(max_context_len), float(scale),
-                            _DTYPE[q.dtype], kvd, int(split_tokens), _ptr(workspace), ws_bytes,
-                            _stream(stream))
+        args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                _ptr(block_tables), _ptr(context_lens), N, T, Hq, Hkv, D, BS, NB,
+                block_tables.shape[1], int(max_context_len), float(scale), _DTYPE[q.dtype], kvd,
+                int(split_tokens), _ptr(workspace), ws_bytes]
+        fn = lib_.pa_verify if plan is None else lib_.pa_verify_planned
     else:
-        st = lib_.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
-                            _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), N, Hq, Hkv, D,
-                            BS, NB, block_tables.shape[1], int(max_context_len), float(scale),
-                            _DTYPE[q.dtype], kvd, int(split_tokens), _ptr(workspace), ws_bytes,
-                            _stream(stream))
-    _check(st)
+        args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                _ptr(block_tables), _ptr(context_lens), N, Hq, Hkv, D, BS, NB,
+                block_tables.shape[1], int(max_context_len), float(scale), _DTYPE[q.dtype], kvd,
+                int(split_tokens), _ptr(workspace), ws_bytes]
+        fn = lib_.pa_decode if plan is None else lib_.pa_decode_planned
+    if plan is not None:
+        args += list(pp)
+    _check(fn(*args, _stream(stream)))
     return out
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-           k_scale=None, v_scale=None, split_tokens=0, workspace=None, stream=None):
-    """Paged GQA decode: q/out [num_seqs, q_heads, head_dim]."""
+           k_scale=None, v_scale=None, split_tokens=0, workspace=None, stream=None, plan=None):
+    """Paged GQA decode: q/out [num_seqs, q_heads, head_dim].  With `plan` (make_plan) the
+    work starts in the plan's order (pa_decode_planned; same bits)."""
     return _attention(False, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                      max_context_len, k_scale, v_scale, split_tokens, workspace, stream)
+                      max_context_len, k_scale, v_scale, split_tokens, workspace, stream, plan)
 
 
 def verify(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-           k_scale=None, v_scale=None, split_tokens=0, workspace=None, stream=None):
-    """Multi-token causal verify: q/out [num_seqs, num_query_tokens, q_heads, head_dim]."""
+           k_scale=None, v_scale=None, split_tokens=0, workspace=None, stream=None, plan=None):
+    """Multi-token causal verify: q/out [num_seqs, num_query_tokens, q_heads, head_dim].
+    With `plan` (make_plan with num_query_tokens = T): pa_verify_planned."""
     return _attention(True, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                      max_context_len, k_scale, v_scale, split_tokens, workspace, stream)
+                      max_context_len, k_scale, v_scale, split_tokens, workspace, stream, plan)
 
 
 def verify_varlen(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
@@ -335,7 +389,7 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, s
 
 
 def decode_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
-                  scale, max_context_len, split_tokens=0, workspace=None, stream=None):
+                  scale, max_context_len, split_tokens=0, workspace=None, stream=None, plan=None):
     """Cache write of one new token per sequence plus decode, in one launch.
 
     key/value [num_seqs, kv_heads, head_dim]; slot_mapping int64 [num_seqs].
@@ -360,10 +414,12 @@ def decode_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tabl
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_load().pa_decode_append(_ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache),
-                                    _ptr(v_cache), _ptr(slot_mapping), _ptr(block_tables),
-                                    _ptr(context_lens), N, Hq, Hkv, D, BS, NB,
-                                    block_tables.shape[1], int(max_context_len), float(scale),
-                                    _DTYPE[q.dtype], kvd, int(split_tokens), _ptr(workspace),
-                                    ws_bytes, _stream(stream)))
+    args = [_ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+            _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), N, Hq, Hkv, D, BS, NB,
+            block_tables.shape[1], int(max_context_len), float(scale), _DTYPE[q.dtype], kvd,
+            int(split_tokens), _ptr(workspace), ws_bytes]
+    if plan is None:
+        _check(_load().pa_decode_append(*args, _stream(stream)))
+    else:
+        _check(_load().pa_decode_append_planned(*args, *_plan_args(plan), _stream(stream)))
     return out

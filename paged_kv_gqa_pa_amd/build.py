@@ -18,7 +18,8 @@ PROBE_OUT = os.path.join(HERE, "libpa_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-SOURCES = ["pa_api.hip", "pa_cache.hip", "pa_decode.hip", "pa_verify.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.hip", "pa_cache.hip", "pa_decode.hip", "pa_verify.hip", "pa_prefill.hip",
+           "pa_plan.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 HIPCC_FLAGS = [

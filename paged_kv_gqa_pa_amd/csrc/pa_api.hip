@@ -29,7 +29,7 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-struct Plan {
+struct SplitPlan {
   int split_tokens = 0;
   int max_pieces = 1;
   size_t o_bytes = 0;
@@ -68,7 +68,7 @@ int default_split(int T, int q_heads, int kv_heads, int head_dim, int kv_dtype) 
 // rows_rule: the call runs on the matrix-core kernel whatever T is (variable-
 // length verify), so the default piece length follows that kernel's rule.
 int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
-                int max_context_len, int kv_dtype, int split_tokens, Plan* plan,
+                int max_context_len, int kv_dtype, int split_tokens, SplitPlan* plan,
                 bool rows_rule = false) {
   if (num_seqs < 0 || T < 1 || q_heads <= 0 || kv_heads <= 0 || max_context_len < 0)
     return fail(PA_ERR_INVALID_ARG,
@@ -97,6 +97,14 @@ int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
     return fail(PA_ERR_UNSUPPORTED, "too many workgroups: pieces * num_seqs * kv_heads > %ld",
                 kMaxGrid);
   return PA_OK;
+}
+
+// Bytes of a work plan for num_seqs sequences cut into max_pieces pieces of
+// split_tokens positions; 0 when the units exceed what one plan orders.
+size_t plan_bytes_for(int num_seqs, const SplitPlan& sp) {
+  const long units = long(num_seqs) * sp.max_pieces;
+  if (units > pa::kMaxPlanUnits) return 0;
+  return size_t(pa::kPlanHeader + units * pa::plan_stride(sp.split_tokens)) * sizeof(int32_t);
 }
 
 int check_attention_args(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -154,8 +162,9 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
                   int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
                   int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
                   int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
-                  void* stream, const Append& app = Append(), const Varlen& vl = Varlen()) {
-  Plan plan;
+                  void* stream, const Append& app = Append(), const Varlen& vl = Varlen(),
+                  const void* work_plan = nullptr, size_t work_plan_bytes = 0) {
+  SplitPlan plan;
   int st = plan_pieces(num_seqs, T, q_heads, kv_heads, head_dim, max_context_len, kv_dtype,
                        split_tokens, &plan, vl.on);
   if (st != PA_OK) return st;
@@ -188,6 +197,16 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
     if (num_seqs > 0 && (!vl.query_start || !aligned(vl.query_start, 4)))
       return fail(PA_ERR_INVALID_ARG, "query_start must be a 4-byte aligned pointer");
     if (vl.total == 0) return PA_OK;
+  }
+  if (work_plan) {
+    const size_t pb = plan_bytes_for(num_seqs, plan);
+    if (pb == 0)
+      return fail(PA_ERR_UNSUPPORTED, "a work plan orders at most %d (sequence, piece) units",
+                  pa::kMaxPlanUnits);
+    if (work_plan_bytes < pb || !aligned(work_plan, 16))
+      return fail(PA_ERR_INVALID_ARG,
+                  "work plan of %zu bytes (16-byte aligned) needed for these sizes, got %zu", pb,
+                  work_plan_bytes);
   }
   if (num_seqs == 0) return PA_OK;
   const size_t need = plan.total();
@@ -224,6 +243,7 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.new_v = app.value;
   a.slot_mapping = app.slot_mapping;
   a.query_start = vl.on ? vl.query_start : nullptr;
+  a.plan = static_cast<const int32_t*>(work_plan);
   a.total_query_tokens = vl.on ? vl.total : num_seqs * T;
   // Verify calls, and decode over an int8 cache, run on the matrix cores.
   const bool rows = vl.on || rows_kernel(T, G, kv_dtype);
@@ -334,7 +354,7 @@ int pa_default_split_tokens(int num_query_tokens, int q_heads, int kv_heads, int
 
 size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv_heads,
                          int head_dim, int max_context_len, int kv_dtype, int split_tokens) {
-  Plan plan;
+  SplitPlan plan;
   if (plan_pieces(num_seqs, num_query_tokens, q_heads, kv_heads, head_dim, max_context_len,
                   kv_dtype, split_tokens, &plan) != PA_OK)
     return 0;
@@ -382,6 +402,101 @@ int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache
                        context_lens, num_seqs, num_query_tokens, q_heads, kv_heads, head_dim,
                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
                        q_dtype, kv_dtype, split_tokens, workspace, workspace_bytes, stream);
+}
+
+size_t pa_plan_size(int num_seqs, int num_query_tokens, int q_heads, int kv_heads,
+                    int head_dim, int max_context_len, int kv_dtype, int split_tokens) {
+  SplitPlan sp;
+  if (plan_pieces(num_seqs, num_query_tokens, q_heads, kv_heads, head_dim, max_context_len,
+                  kv_dtype, split_tokens, &sp) != PA_OK)
+    return 0;
+  const size_t pb = plan_bytes_for(num_seqs, sp);
+  if (pb == 0)
+    fail(PA_ERR_UNSUPPORTED, "a work plan orders at most %d (sequence, piece) units",
+         pa::kMaxPlanUnits);
+  return pb;
+}
+
+int pa_plan(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+            int num_query_tokens, int q_heads, int kv_heads, int head_dim,
+            int max_blocks_per_seq, int max_context_len, int kv_dtype, int split_tokens,
+            void* plan, size_t plan_bytes, void* stream) {
+  SplitPlan sp;
+  int st = plan_pieces(num_seqs, num_query_tokens, q_heads, kv_heads, head_dim,
+                       max_context_len, kv_dtype, split_tokens, &sp);
+  if (st != PA_OK) return st;
+  if (max_blocks_per_seq <= 0 || long(max_context_len) > long(max_blocks_per_seq) * 16)
+    return fail(PA_ERR_INVALID_ARG,
+                "max_blocks_per_seq %d must be > 0 and cover max_context_len %d",
+                max_blocks_per_seq, max_context_len);
+  const size_t pb = plan_bytes_for(num_seqs, sp);
+  if (pb == 0)
+    return fail(PA_ERR_UNSUPPORTED, "a work plan orders at most %d (sequence, piece) units",
+                pa::kMaxPlanUnits);
+  if (!plan || plan_bytes < pb || !aligned(plan, 16))
+    return fail(PA_ERR_INVALID_ARG,
+                "work plan of %zu bytes (16-byte aligned) needed for these sizes, got %zu", pb,
+                plan ? plan_bytes : size_t(0));
+  if (num_seqs > 0 && (!block_tables || !context_lens))
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned table or length pointer");
+  pa::PlanArgs a{block_tables, context_lens, static_cast<int32_t*>(plan), num_seqs,
+                 max_blocks_per_seq, sp.max_pieces, sp.split_tokens};
+  hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "plan launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_decode_planned(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int q_heads, int kv_heads,
+                      int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, float scale, int q_dtype, int kv_dtype,
+                      int split_tokens, void* workspace, size_t workspace_bytes,
+                      const void* plan, size_t plan_bytes, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID_ARG, "null work plan");
+  return run_attention(false, out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
+                       split_tokens, workspace, workspace_bytes, stream, Append(), Varlen(),
+                       plan, plan_bytes);
+}
+
+int pa_decode_append_planned(void* out, const void* q, const void* key, const void* value,
+                             void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int q_heads, int kv_heads, int head_dim,
+                             int block_size, int num_blocks, int max_blocks_per_seq,
+                             int max_context_len, float scale, int q_dtype, int kv_dtype,
+                             int split_tokens, void* workspace, size_t workspace_bytes,
+                             const void* plan, size_t plan_bytes, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID_ARG, "null work plan");
+  Append app;
+  app.key = key;
+  app.value = value;
+  app.slot_mapping = slot_mapping;
+  app.on = true;
+  return run_attention(false, out, q, k_cache, v_cache, nullptr, nullptr, block_tables,
+                       context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
+                       split_tokens, workspace, workspace_bytes, stream, app, Varlen(), plan,
+                       plan_bytes);
+}
+
+int pa_verify_planned(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int num_query_tokens,
+                      int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
+                      int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
+                      int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+                      const void* plan, size_t plan_bytes, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID_ARG, "null work plan");
+  return run_attention(true, out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, num_seqs, num_query_tokens, q_heads, kv_heads, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       q_dtype, kv_dtype, split_tokens, workspace, workspace_bytes, stream,
+                       Append(), Varlen(), plan, plan_bytes);
 }
 
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

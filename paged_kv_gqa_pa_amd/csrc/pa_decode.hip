@@ -177,25 +177,20 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // always-present first pieces spread evenly over the chip, and all pieces of
   // one (sequence, head) land on the same XCD whenever N*Hkv is a multiple of 8.
   PA_STAMP(0);
-  const int pairs = a.num_seqs * a.kv_heads;
-  const int piece = blockIdx.x / pairs;
-  const int pair = blockIdx.x - piece * pairs;
-  const int b = pair / a.kv_heads;
-  const int g = pair - b * a.kv_heads;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPK;   // key row inside a load
   const int c = lane % LPK;   // which 16-byte column of each piece
+
+  // The work unit (natural order or a work plan) and the piece's table
+  // entries (spread over the lanes; a tile's physical block is then read
+  // with readlane), then this group's query rows: in the natural order the
+  // length, the table row and q arrive in one round trip.
+  PieceTable<kTabRegs> tab;
+  const WorkItem it = work_item(a, tab, lane);
+  const int b = it.b, piece = it.piece, g = it.g;
   const int split_blocks = a.split_tokens / kBlockSize;
   const int blk_begin = piece * split_blocks;
-
-  // Issue the loads that do not depend on the context length first, so the
-  // length, the block-table row and q arrive in one round trip: the piece's
-  // table entries (spread over the lanes; a tile's physical block is then
-  // read with readlane) and this group's query rows.
-  const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
-  PieceTable<kTabRegs> tab;
-  tab.load(bt, blk_begin, min(a.max_blocks_per_seq, blk_begin + split_blocks), lane);
   const Q* qrow = reinterpret_cast<const Q*>(a.q) + (size_t(b) * a.q_heads + size_t(g) * G) * D;
   QRegs<Q, KV, D, G> qr;
   qr.load(qrow, c);
@@ -217,9 +212,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 
   // Lengths beyond the table are clamped so that no access leaves the
   // buffers (the result of such a call is unspecified).
-  const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
+  const int L = it.L;
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
-  if (piece >= n_pieces) return;
+  if (piece < 0 || piece >= n_pieces) return;
   PA_STAMP(1);
   if constexpr (APPEND) {
     // The last piece writes the new row into the cache (one key row: the

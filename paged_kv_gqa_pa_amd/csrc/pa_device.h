@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_kernels.h"
+
 namespace pa {
 
 constexpr int kWave = 64;
@@ -163,6 +165,51 @@ __device__ __forceinline__ u32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 __device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, int offset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds, 16, offset, 0, 0, 2);
+}
+
+
+// The work unit of this workgroup: sequence b, piece, KV head g, the
+// sequence's context length L (clamped to the table), and the piece's
+// block-table entries in `tab` (entry i = logical block piece * sb + i).
+// With a work plan whose header matches the call, unit blockIdx / kv_heads of
+// the plan is taken and its entries come from the plan row: one round trip,
+// as the natural order's table-row load.  Otherwise (no plan, or a plan made
+// for other sizes) the natural order: piece-major, then sequence, then head.
+// Either way the unit's arithmetic is the same, so the order changes no bit
+// of the result.  piece < 0 means no work.
+struct WorkItem {
+  int b, piece, g, L;
+};
+template <int NREG>
+__device__ __forceinline__ WorkItem work_item(const DecodeArgs& a, PieceTable<NREG>& tab, int lane) {
+  const int sb = a.split_tokens / kBlockSize;
+  const int max_len = a.max_blocks_per_seq * kBlockSize;
+  WorkItem it;
+  if (a.plan) {
+    const int unit = blockIdx.x / a.kv_heads;
+    const int32_t* row = a.plan + kPlanHeader + size_t(unit) * plan_stride(a.split_tokens);
+    tab.load(row + kPlanRowHead, 0, sb, lane);
+    const int32_t* h = a.plan;
+    if (h[0] == kPlanMagic && h[1] == a.num_seqs && h[2] == a.max_pieces &&
+        h[3] == a.split_tokens && h[4] == a.max_blocks_per_seq) {
+      // Clamped so that a corrupt row cannot address outside the buffers.
+      it.b = min(max(row[0], 0), a.num_seqs - 1);
+      it.piece = row[3] < 0 ? -1 : min(row[1], a.max_pieces - 1);
+      it.g = blockIdx.x - unit * a.kv_heads;
+      it.L = min(max(row[2], 0), max_len);
+      return it;
+    }
+  }
+  const int pairs = a.num_seqs * a.kv_heads;
+  it.piece = blockIdx.x / pairs;
+  const int pair = blockIdx.x - it.piece * pairs;
+  it.b = pair / a.kv_heads;
+  it.g = pair - it.b * a.kv_heads;
+  const int begin = it.piece * sb;
+  tab.load(a.block_tables + size_t(it.b) * a.max_blocks_per_seq, begin,
+           min(a.max_blocks_per_seq, begin + sb), lane);
+  it.L = min(a.context_lens[it.b], max_len);
+  return it;
 }
 
 }  // namespace pa

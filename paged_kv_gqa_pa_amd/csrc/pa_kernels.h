@@ -59,6 +59,10 @@ struct DecodeArgs {
   // query_start[b] .. query_start[b+1]-1 of q and out ([total, q_heads,
   // head_dim]); nullptr for a fixed T per sequence.
   const int32_t* query_start;
+  // Work plan (pa_plan): the order in which the (sequence, piece) units are
+  // started, with copies of their lengths and block-table entries; nullptr =
+  // natural order.
+  const int32_t* plan;
   int total_query_tokens;
   int num_seqs;
   int num_query_tokens;  // T (1 for decode); the largest T_b for variable length
@@ -92,6 +96,31 @@ struct MergeArgs {
   int out_dtype;
 };
 
+// Work plans.  A plan is kPlanHeader ints (kPlanMagic, num_seqs, max_pieces,
+// split_tokens, max_blocks_per_seq, the rest 0) and then one row per unit
+// (sequence, piece) in the order the units are to be started: sequence,
+// piece, context length, the piece's tile count (-1: the piece does not
+// exist), then the piece's split_tokens / 16 block-table entries (0 past its
+// tiles), padded to a multiple of 4 ints.
+constexpr int kPlanHeader = 16;
+constexpr int kPlanRowHead = 4;
+constexpr int kPlanMagic = 0x50414E31;
+constexpr int kMaxPlanUnits = 8192;  // units (num_seqs * max_pieces) one plan orders
+__host__ __device__ inline int plan_stride(int split_tokens) {
+  return kPlanRowHead + ((split_tokens / kBlockSizeHost + 3) & ~3);
+}
+
+struct PlanArgs {
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t* plan;
+  int num_seqs;
+  int max_blocks_per_seq;
+  int max_pieces;
+  int split_tokens;
+};
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 // Chunked prefill (matrix cores): DecodeArgs with query_start set, no pieces.
 hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);

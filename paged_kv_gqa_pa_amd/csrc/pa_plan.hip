@@ -1,0 +1,103 @@
+// Work plan: the order in which an attention call's (sequence, piece) units
+// are started, longest first.
+//
+// Every unit's arithmetic is fixed by the unit alone (its sequence, its piece
+// of a fixed length), so the order changes no bit of any result; it only
+// changes how evenly the chip is loaded.  In the natural order a long unit
+// started late ends the launch alone; started first, it overlaps the short
+// ones.  The decode step of "From 183 ms to 19 ms per decode step" (section
+// "Four changes, one profile at a time", change 4) hands every layer of a step
+// the same block tables and lengths, so one plan serves all of a step's
+// layers.
+//
+// One workgroup orders the units with a counting sort on their tile counts
+// (at most split_tokens / 16 + 2 distinct keys): a histogram, offsets in
+// descending key order, then each unit takes the next place of its key
+// (units of equal length land in any order).  Each unit's row receives its
+// sequence, piece, length, tile count and a copy of the piece's block-table
+// entries, so that an attention workgroup learns its unit and the piece's
+// physical blocks in one round trip.
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int s_key[kMaxPlanUnits];
+  __shared__ int s_pos[kMaxPlanUnits];
+  __shared__ int s_cnt[kMaxSplitTokens / kBlockSize + 2];
+  const int N = a.num_seqs;
+  const int U = a.max_pieces * N;
+  const int sb = a.split_tokens / kBlockSize;
+  const int max_len = a.max_blocks_per_seq * kBlockSize;
+  const int tid = threadIdx.x;
+
+  for (int i = tid; i < sb + 2; i += kPlanThreads) s_cnt[i] = 0;
+  __syncthreads();
+  // Key of unit v = (piece v / N, sequence v % N): its tile count, 0 for the
+  // single piece of an empty context (it still writes a zero row), -1 for a
+  // piece past the sequence's context (no work).
+  for (int v = tid; v < U; v += kPlanThreads) {
+    const int piece = v / N, b = v - piece * N;
+    const int L = min(max(a.context_lens[b], 0), max_len);
+    const int np = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
+    const int key = piece < np ? min(max(cdiv(L, kBlockSize) - piece * sb, 0), sb) : -1;
+    s_key[v] = key;
+    atomicAdd(&s_cnt[key + 1], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int k = sb + 1; k >= 0; --k) {
+      const int c = s_cnt[k];
+      s_cnt[k] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int v = tid; v < U; v += kPlanThreads) s_pos[v] = atomicAdd(&s_cnt[s_key[v] + 1], 1);
+  __syncthreads();
+
+  const int stride = plan_stride(a.split_tokens);
+  int32_t* rows = a.plan + kPlanHeader;
+  for (int v = tid; v < U; v += kPlanThreads) {
+    const int piece = v / N, b = v - piece * N;
+    int32_t* row = rows + size_t(s_pos[v]) * stride;
+    row[0] = b;
+    row[1] = piece;
+    row[2] = min(max(a.context_lens[b], 0), max_len);
+    row[3] = s_key[v];
+  }
+  // The piece's table entries, one per thread: entry i of unit v.
+  const long entries = long(U) * sb;
+  for (long idx = tid; idx < entries; idx += kPlanThreads) {
+    const int v = int(idx / sb), i = int(idx - long(v) * sb);
+    const int piece = v / N, b = v - piece * N;
+    const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
+    rows[size_t(s_pos[v]) * stride + kPlanRowHead + i] = i < s_key[v] ? bt[piece * sb + i] : 0;
+  }
+  if (tid < kPlanHeader) {
+    int h = 0;
+    switch (tid) {
+      case 0: h = kPlanMagic; break;
+      case 1: h = N; break;
+      case 2: h = a.max_pieces; break;
+      case 3: h = a.split_tokens; break;
+      case 4: h = a.max_blocks_per_seq; break;
+      default: h = 0;
+    }
+    a.plan[tid] = h;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
+  plan_kernel<<<1, kPlanThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -61,11 +61,12 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   constexpr int WBYTES = SLOT > OHALF ? SLOT : OHALF;
   using M = MOps<KV>;
 
-  const int pairs = a.num_seqs * a.kv_heads;
-  const int piece = blockIdx.x / pairs;
-  const int pair = blockIdx.x - piece * pairs;
-  const int b = pair / a.kv_heads;
-  const int g = pair - b * a.kv_heads;
+  const int lane = threadIdx.x & (kWave - 1);
+  // The work unit (natural order or a work plan) and the piece's table
+  // entries, requested before anything that depends on them.
+  PieceTable<kTabRegs> tab;
+  const WorkItem it = work_item(a, tab, lane);
+  const int b = it.b, piece = it.piece, g = it.g;
   const int Hq = a.q_heads;
   const int G = Hq / a.kv_heads;
   // Sequence b's query tokens: T of them from packed token q0 (fixed T: b * T),
@@ -80,17 +81,12 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   }
   const int R = T * G;
 
-  const int lane = threadIdx.x & (kWave - 1);
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;     // key row of an operand read / query row of S, P
   const int grp = lane >> 4;   // 8-dim group of a score product / key quad of S, P, O
   const int split_blocks = a.split_tokens / kBlockSize;
   const int blk_begin = piece * split_blocks;
 
-  // Length-independent loads first: the piece's table entries and the query rows.
-  const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
-  PieceTable<kTabRegs> tab;
-  tab.load(bt, blk_begin, min(a.max_blocks_per_seq, blk_begin + split_blocks), lane);
   const int t_row = n / G;
   const int h_row = g * G + (n - t_row * G);
   // Query rows as the B operand of score product c: lane (row n, group grp)
@@ -118,9 +114,9 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   // Row n's sum of (fp16) q over all dims: the four groups of row n.
   const float qsum = kInt8 ? add_xor32(add_xor16(qpart)) : 0.0f;
 
-  const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
+  const int L = it.L;
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
-  if (piece >= n_pieces) return;
+  if (piece < 0 || piece >= n_pieces) return;
   const int blk_end = min(cdiv(L, kBlockSize), blk_begin + split_blocks);
   // Last position row n may see (rows past R see nothing).
   const int last_vis = n < R ? L - T + t_row : -1;

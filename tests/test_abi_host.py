@@ -153,3 +153,36 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.pa_probe_tile_read(d, d, d, d, 1, 1, 4, 4, 64, 16, 64, 4, d, None) == -1
     # waves 16 is not built
     assert lib.pa_probe_tile_read(d, d, d, d, 1, 1, 4, 4, 256, 16, 64, 16, d, None) == -1
+
+
+def test_plan_size_and_invalid_arguments():
+    """Plan sizes follow the layout (16 header ints, one row per (sequence, piece) unit of
+    4 + split/16 rounded up to 4 ints); invalid calls are refused before any launch."""
+    lib = pa.lib()
+    # batch-64 decode: one 512-token piece per sequence -> 64 rows of 4 + 32 ints
+    assert lib.pa_plan_size(64, 1, 16, 8, 128, 512, pa.PA_BF16, 0) == 4 * (16 + 64 * 36)
+    # 8 sequences of 32768 in 2048-token pieces (int8 default) -> 128 rows of 4 + 128 ints
+    assert lib.pa_plan_size(8, 1, 12, 2, 128, 32768, pa.PA_INT8, 0) == 4 * (16 + 128 * 132)
+    # split 48 -> 3 entries, padded to 4
+    assert lib.pa_plan_size(2, 1, 2, 1, 64, 100, pa.PA_F32, 48) == 4 * (16 + 2 * 3 * 8)
+    # more than 8192 units, or invalid sizes: 0
+    assert lib.pa_plan_size(9000, 1, 2, 1, 64, 16, pa.PA_F32, 0) == 0
+    assert lib.pa_plan_size(4, 1, 3, 2, 64, 16, pa.PA_F32, 0) == 0
+    d = ctypes.c_void_p(FAKE)
+    need = lib.pa_plan_size(4, 1, 2, 1, 64, 64, pa.PA_F32, 16)
+    # plan buffer too small / missing
+    assert lib.pa_plan(d, d, 4, 1, 2, 1, 64, 4, 64, pa.PA_F32, 16, d, need - 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_plan(d, d, 4, 1, 2, 1, 64, 4, 64, pa.PA_F32, 16, None, need, None) == pa.PA_ERR_INVALID_ARG
+    # table too narrow for max_context_len
+    assert lib.pa_plan(d, d, 4, 1, 2, 1, 64, 3, 64, pa.PA_F32, 16, d, need, None) == pa.PA_ERR_INVALID_ARG
+    # null tables
+    assert lib.pa_plan(None, d, 4, 1, 2, 1, 64, 4, 64, pa.PA_F32, 16, d, need, None) == pa.PA_ERR_INVALID_ARG
+    # planned decode with a null plan
+    ptrs = [d] * 8
+    st = lib.pa_decode_planned(*ptrs, 4, 2, 1, 64, 16, 16, 4, 64, ctypes.c_float(0.125),
+                               pa.PA_F32, pa.PA_F32, 16, d, 1 << 20, None, need, None)
+    assert st == pa.PA_ERR_INVALID_ARG
+    # planned decode with a plan smaller than the call's sizes need
+    st = lib.pa_decode_planned(*ptrs, 4, 2, 1, 64, 16, 16, 4, 64, ctypes.c_float(0.125),
+                               pa.PA_F32, pa.PA_F32, 16, d, 1 << 20, d, need - 16, None)
+    assert st == pa.PA_ERR_INVALID_ARG and b"work plan" in lib.pa_last_error()
