@@ -441,8 +441,21 @@ int pa_plan(const int32_t* block_tables, const int32_t* context_lens, int num_se
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PA_ERR_INVALID_ARG, "misaligned table or length pointer");
+  // Snake rounds where the kernel that will read the plan keeps several
+  // workgroups per CU: one round is one workgroup per CU, i.e. CUs / kv_heads
+  // units (a unit's kv_heads workgroups are consecutive).
+  const int G = q_heads / kv_heads;
+  const int resident = rows_kernel(num_query_tokens, G, kv_dtype)
+                           ? pa::rows_pass1_resident(kv_dtype, head_dim)
+                           : pa::decode_pass1_resident(kv_dtype == PA_F32 ? PA_F32 : PA_BF16,
+                                                       kv_dtype, head_dim, G);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const int snake_units = resident >= 2 && cus > 0 ? (cus + kv_heads - 1) / kv_heads : 0;
   pa::PlanArgs a{block_tables, context_lens, static_cast<int32_t*>(plan), num_seqs,
-                 max_blocks_per_seq, sp.max_pieces, sp.split_tokens};
+                 max_blocks_per_seq, sp.max_pieces, sp.split_tokens, snake_units, resident};
   hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "plan launch failed: %s", hipGetErrorString(e));
   return PA_OK;

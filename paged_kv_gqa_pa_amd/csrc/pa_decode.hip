@@ -646,6 +646,42 @@ extern "C" int pa_debug_wtimes(unsigned long long* host, int n) {
 
 bool decode_group_supported(int G) { return (G >= 1 && G <= 8) || G == 16; }
 
+namespace {
+template <typename Q, typename KV, int D, int G>
+int resident_t() {
+  int n = 0;
+  constexpr int NW = PA_DECODE_WAVES;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, decode_pass1<Q, KV, D, G, NW, PA_RING, false>, NW * kWave, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+template <typename Q, typename KV, int D>
+int resident_group(int G) {
+  switch (G) {
+    case 1: return resident_t<Q, KV, D, 1>();
+    case 2: return resident_t<Q, KV, D, 2>();
+    case 3: return resident_t<Q, KV, D, 3>();
+    case 4: return resident_t<Q, KV, D, 4>();
+    case 5: return resident_t<Q, KV, D, 5>();
+    case 6: return resident_t<Q, KV, D, 6>();
+    case 7: return resident_t<Q, KV, D, 7>();
+    case 8: return resident_t<Q, KV, D, 8>();
+    case 16: return resident_t<Q, KV, D, 16>();
+    default: return 1;
+  }
+}
+}  // namespace
+
+int decode_pass1_resident(int q_dtype, int kv_dtype, int head_dim, int G) {
+  if (q_dtype == kF32 && kv_dtype == kF32)
+    return head_dim == 64 ? resident_group<float, float, 64>(G) : resident_group<float, float, 128>(G);
+  if (q_dtype == kBF16 && kv_dtype == kBF16)
+    return head_dim == 64 ? resident_group<bf16_t, bf16_t, 64>(G)
+                          : resident_group<bf16_t, bf16_t, 128>(G);
+  return 1;
+}
+
 template <typename O, int D>
 void launch_merge_t(const MergeArgs& a, hipStream_t stream) {
   // chunks of 8 pieces for calls of up to 8 pieces, 16 up to 16, else 32

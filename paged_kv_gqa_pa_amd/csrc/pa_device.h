@@ -189,14 +189,19 @@ __device__ __forceinline__ WorkItem work_item(const DecodeArgs& a, PieceTable<NR
     const int unit = blockIdx.x / a.kv_heads;
     const int32_t* row = a.plan + kPlanHeader + size_t(unit) * plan_stride(a.split_tokens);
     tab.load(row + kPlanRowHead, 0, sb, lane);
-    const int32_t* h = a.plan;
-    if (h[0] == kPlanMagic && h[1] == a.num_seqs && h[2] == a.max_pieces &&
-        h[3] == a.split_tokens && h[4] == a.max_blocks_per_seq) {
+    // Header and row head as two 16-byte loads issued together (a short-
+    // circuit test would wait for each header word before asking for the next).
+    const int4 h = *reinterpret_cast<const int4*>(a.plan);
+    const int h4 = a.plan[4];
+    const int4 r = *reinterpret_cast<const int4*>(row);
+    const bool ok = (h.x == kPlanMagic) & (h.y == a.num_seqs) & (h.z == a.max_pieces) &
+                    (h.w == a.split_tokens) & (h4 == a.max_blocks_per_seq);
+    if (ok) {
       // Clamped so that a corrupt row cannot address outside the buffers.
-      it.b = min(max(row[0], 0), a.num_seqs - 1);
-      it.piece = row[3] < 0 ? -1 : min(row[1], a.max_pieces - 1);
+      it.b = min(max(r.x, 0), a.num_seqs - 1);
+      it.piece = r.w < 0 ? -1 : min(r.y, a.max_pieces - 1);
       it.g = blockIdx.x - unit * a.kv_heads;
-      it.L = min(max(row[2], 0), max_len);
+      it.L = min(max(r.z, 0), max_len);
       return it;
     }
   }

@@ -97,7 +97,8 @@ struct MergeArgs {
 };
 
 // Work plans.  A plan is kPlanHeader ints (kPlanMagic, num_seqs, max_pieces,
-// split_tokens, max_blocks_per_seq, the rest 0) and then one row per unit
+// split_tokens, max_blocks_per_seq, snake_units, snake_rounds, the rest 0)
+// and then one row per unit
 // (sequence, piece) in the order the units are to be started: sequence,
 // piece, context length, the piece's tile count (-1: the piece does not
 // exist), then the piece's split_tokens / 16 block-table entries (0 past its
@@ -118,7 +119,17 @@ struct PlanArgs {
   int max_blocks_per_seq;
   int max_pieces;
   int split_tokens;
+  // The first snake_rounds rounds of snake_units units each (the workgroups
+  // resident at once, one per CU per round) alternate longest-first and
+  // shortest-first, so each CU holds a long and a short unit; 0 = plain
+  // longest-first order.
+  int snake_units;
+  int snake_rounds;
 };
+
+// Workgroups of one attention kernel resident per CU (occupancy query).
+int decode_pass1_resident(int q_dtype, int kv_dtype, int head_dim, int G);
+int rows_pass1_resident(int kv_dtype, int head_dim);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

@@ -13,10 +13,14 @@
 // One workgroup orders the units with a counting sort on their tile counts
 // (at most split_tokens / 16 + 2 distinct keys): a histogram, offsets in
 // descending key order, then each unit takes the next place of its key
-// (units of equal length land in any order).  Each unit's row receives its
-// sequence, piece, length, tile count and a copy of the piece's block-table
-// entries, so that an attention workgroup learns its unit and the piece's
-// physical blocks in one round trip.
+// (units of equal length land in any order).  Where the attention kernel
+// keeps several workgroups per CU, all of them started at once, the first
+// rounds snake: a CU's second workgroup gets a short unit opposite its first
+// workgroup's long one, which evens the work per CU (a plain longest-first
+// order pairs the c-th longest with the (c + CUs)-th longest).  Each unit's
+// row receives its sequence, piece, length, tile count and a copy of the
+// piece's block-table entries, so that an attention workgroup learns its unit
+// and the piece's physical blocks in one round trip.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -58,7 +62,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
   }
   __syncthreads();
-  for (int v = tid; v < U; v += kPlanThreads) s_pos[v] = atomicAdd(&s_cnt[s_key[v] + 1], 1);
+  // Rounds of resident workgroups: round r of snake_units units lands one
+  // workgroup per CU, and round r + 1 the second workgroup of the same CUs in
+  // the same CU order, so odd rounds are reversed (shortest first) to pair
+  // each CU's long unit with a short one.
+  const int S = a.snake_units;
+  for (int v = tid; v < U; v += kPlanThreads) {
+    int p = atomicAdd(&s_cnt[s_key[v] + 1], 1);
+    if (S > 0) {
+      const int r = p / S;
+      if (r < a.snake_rounds && (r & 1)) {
+        const int lo = r * S, n = min(S, U - lo);
+        p = lo + (n - 1 - (p - lo));
+      }
+    }
+    s_pos[v] = p;
+  }
   __syncthreads();
 
   const int stride = plan_stride(a.split_tokens);
@@ -87,6 +106,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       case 2: h = a.max_pieces; break;
       case 3: h = a.split_tokens; break;
       case 4: h = a.max_blocks_per_seq; break;
+      case 5: h = a.snake_units; break;
+      case 6: h = a.snake_rounds; break;
       default: h = 0;
     }
     a.plan[tid] = h;

@@ -383,6 +383,19 @@ bool rows_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T) {
          (head_dim == 64 || head_dim == 128) && G >= 1 && T >= 1 && long(G) * T <= kRows;
 }
 
+int rows_pass1_resident(int kv_dtype, int head_dim) {
+  int n = 0;
+  constexpr int NW = PA_ROWS_WAVES;
+  hipError_t e;
+  if (kv_dtype == kI8)
+    e = head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<i8_t, 64, NW>, NW * kWave, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<i8_t, 128, NW>, NW * kWave, 0);
+  else
+    e = head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<bf16_t, 64, NW>, NW * kWave, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<bf16_t, 128, NW>, NW * kWave, 0);
+  return e == hipSuccess && n > 0 ? n : 1;
+}
+
 hipError_t launch_rows_pass1(const DecodeArgs& a, hipStream_t stream) {
   return a.kv_dtype == kI8 ? launch_rows_t<i8_t>(a, stream) : launch_rows_t<bf16_t>(a, stream);
 }

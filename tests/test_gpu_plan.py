@@ -67,7 +67,8 @@ def test_plan_contents_exact():
     stride = ROW_HEAD + (sb + 3) // 4 * 4
     maxb = case.block_tables.shape[1]
     assert list(p[:5]) == [MAGIC, N, max_pieces, split, maxb]
-    assert (p[5:HEADER] == 0).all()
+    snake_units, snake_rounds = int(p[5]), int(p[6])
+    assert (p[7:HEADER] == 0).all()
     rows = p[HEADER:HEADER + N * max_pieces * stride].reshape(N * max_pieces, stride)
     seen = set()
     for row in rows:
@@ -84,8 +85,54 @@ def test_plan_contents_exact():
             want = case.block_tables[b, piece * sb + i] if i < tiles else 0
             assert ids[i] == want, (b, piece, i)
     assert len(seen) == N * max_pieces
-    keys = rows[:, 3]
-    assert (np.diff(keys) <= 0).all(), "units must be ordered longest first"
+    _check_order(rows[:, 3], snake_units, snake_rounds)
+
+
+def _check_order(keys, snake_units, snake_rounds):
+    """Longest first, except that the first snake_rounds rounds of snake_units units
+    alternate: even rounds longest first, odd rounds shortest first; every unit of a round
+    is at least as long as every unit of the next."""
+    U = len(keys)
+    S = snake_units if snake_units > 0 else U
+    bounds = list(range(0, U, S)) + [U]
+    for r in range(len(bounds) - 1):
+        part = keys[bounds[r]:bounds[r + 1]]
+        if snake_units > 0 and r < snake_rounds and r % 2 == 1:
+            assert (np.diff(part) >= 0).all(), r
+        else:
+            assert (np.diff(part) <= 0).all(), r
+        if r + 2 < len(bounds):
+            assert part.min() >= keys[bounds[r + 1]:bounds[r + 2]].max(), r
+
+
+@pytest.mark.parametrize("kv,G,T", [("bf16", 2, 1), ("f32", 1, 1), ("bf16", 6, 1), ("int8", 6, 1),
+                                    ("bf16", 2, 5)])
+def test_plan_order_for_each_kernel(kv, G, T):
+    """The vector-ALU decode keeps two workgroups per CU (snaked rounds of CUs / kv_heads
+    units); the matrix-core kernel one (plain longest-first)."""
+    _say("plan order", kv, "G", G, "T", T)
+    rng = np.random.default_rng(42 + G + T)
+    lens = rng.integers(1, 513, size=200).astype(np.int32)
+    case = (_random_case(rng, lens, Hkv=8, G=G, D=128, tag=kv) if T == 1 else
+            _random_verify_case(rng, lens, Hkv=8, G=G, D=128, T=T, kv=kv))
+    dc = DevCase(case)
+    plan = _plan(dc, kv, 0, T=T)
+    torch.cuda.synchronize()
+    p = plan.cpu().numpy().view(np.int32)
+    split, max_pieces = int(p[3]), int(p[2])
+    stride = ROW_HEAD + (split // 16 + 3) // 4 * 4
+    U = len(lens) * max_pieces
+    rows = p[HEADER:HEADER + U * stride].reshape(U, stride)
+    snake_units, snake_rounds = int(p[5]), int(p[6])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    vector_kernel = T == 1 and kv != "int8" and G < 4
+    if vector_kernel:                       # two or more workgroups per CU
+        assert snake_units == -(-cus // 8) and snake_rounds >= 2
+    elif kv == "bf16":                      # 128 KiB of LDS: one workgroup per CU
+        assert snake_units == 0
+    if snake_units:
+        assert snake_units == -(-cus // 8) and snake_rounds >= 2
+    _check_order(rows[:, 3], snake_units, snake_rounds)
 
 
 @pytest.mark.parametrize("tag", ["f32", "bf16", "int8"])
