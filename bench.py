@@ -173,7 +173,70 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
         del kc, vc, g
         torch.cuda.empty_cache()
     out["int8_requant_write"] = requant_write_timing(torch, pa, dev, reps)
+    out["chunked_prefill_bf16"] = prefill_timing(torch, pa, dev, reps)
     return out
+
+
+def prefill_timing(torch, pa, dev, reps=10, calls=8):
+    """Chunked prefill (pa_prefill): 16 sequences, each a 512-token chunk on top of a
+    seeded prior context U{0..1536}, 16 query / 8 KV heads, head_dim 128, bf16 cache of
+    8192 blocks.  Reported against the bf16 matrix-core peak (the causal products are the
+    work: 4 * head_dim flops per (query row, visible position)) and as HBM bytes (K/V of
+    each sequence once, q, out, tables)."""
+    N, T, Hq, Hkv, D, NB = 16, 512, 16, 8, 128, 8192
+    rng = np.random.default_rng(12)
+    prior = rng.integers(0, 1537, size=N)
+    lens = (prior + T).astype(np.int32)
+    maxb = int(-(-lens.max() // 16))
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.full((N, maxb), -1, np.int32)
+    pos = 0
+    for b, L in enumerate(lens):
+        nb = -(-int(L) // 16)
+        table[b, :nb] = perm[pos:pos + nb]
+        pos += nb
+    g_ = torch.Generator(device=dev)
+    g_.manual_seed(13)
+    kc = torch.randn((Hkv, NB, 16, D), device=dev, dtype=torch.bfloat16, generator=g_)
+    vc = torch.randn((Hkv, NB, 16, D), device=dev, dtype=torch.bfloat16, generator=g_)
+    q = torch.randn((N * T, Hq, D), device=dev, dtype=torch.bfloat16, generator=g_)
+    o = torch.empty_like(q)
+    bt = torch.from_numpy(table).to(dev)
+    cl = torch.from_numpy(lens).to(dev)
+    qs = torch.from_numpy(np.arange(0, N * T + 1, T).astype(np.int32)).to(dev)
+
+    def run():
+        for _ in range(calls):
+            pa.prefill(o, q, kc, vc, bt, cl, qs, 1.0 / float(np.sqrt(D)), T)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+    visible = int(sum(int(p) * T + T * (T + 1) // 2 for p in prior))   # per head
+    flops = 4 * D * Hq * visible
+    alg = (int(lens.sum()) * Hkv * D * 2 * 2 + 2 * N * T * Hq * D * 2 +
+           int(((lens + 15) // 16).sum()) * 4 + N * 8)
+    tflops = flops / (us * 1e-6) / 1e12
+    res = {"shape": f"N={N} chunk={T} prior=U{{0..1536}} Hq={Hq} Hkv={Hkv} D={D} kv=bf16",
+           "us_per_call": round(us, 2), "flops": flops, "tflops": round(tflops, 1),
+           "mfma_frac": round(tflops / 2500.0, 4), "algorithmic_bytes": alg,
+           "hbm_gbps": round(alg / (us * 1e-6) / 1e9, 1), "query_tokens_per_s": round(N * T / (us * 1e-6), 1),
+           "kernel": "prefill_rows"}
+    print(f"[bench] chunked prefill: {us:.2f} us/call, {tflops:.1f} TFLOP/s "
+          f"({100 * tflops / 2500.0:.1f}% of bf16 matrix peak)", flush=True)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
 
 
 def requant_write_timing(torch, pa, dev, reps=10, calls=20):

@@ -50,6 +50,31 @@ template <> struct MOps<i8_t> {
   __device__ static uint32_t pack_round(float lo, float hi) { return pack_exact(lo, hi); }
 };
 
+// bf16 V tiles staged in LDS for transposed reads.  16-byte chunk k of key
+// row r sits at chunk position k ^ vswz(r): the rows an output block's read
+// touches in one LDS pass (two chunks each) then fall on distinct banks.
+template <int ROWB>
+__device__ __forceinline__ int vswz(int r) {
+  constexpr int CPR = ROWB / 16, RPB = ROWB >= 256 ? 1 : 256 / ROWB;
+  return ((r / RPB) & (CPR / 2 - 1)) << 1;
+}
+
+// B operand of the P.V product for output dims 16t .. 16t+15 from a staged
+// bf16 V tile (16 key rows): lane (n = lane % 16, grp = lane / 16) receives
+// V[4grp + j][16t + n], j = 0..3.  One LDS transpose read: lane l addresses
+// dims 16t + 4(l % 4) .. +3 of key row l / 4, and the hardware hands lane i
+// of each 16-lane group element i % 4 of the chunks addressed by lanes
+// i / 4 + 4j of that group, which are key rows 4grp + j.
+template <int ROWB>
+__device__ __forceinline__ u32x2 v_operand_tr(const char* sv, int t, int lane) {
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+  const int r = lane >> 2;
+  const int k = 2 * t + ((lane & 3) >> 1);
+  const char* p = sv + r * ROWB + 16 * (k ^ vswz<ROWB>(r)) + 8 * (lane & 1);
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Eight codes (two words) as the fp16 numbers c + 1152.
 __device__ __forceinline__ u32x4 codes8_f16(uint32_t w0, uint32_t w1) {
   const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;

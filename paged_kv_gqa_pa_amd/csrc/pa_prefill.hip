@@ -117,12 +117,15 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char s_st0[STAGE];
   __shared__ __attribute__((aligned(16))) char s_st1[STAGE];
   auto sw = [](int r, int k) { return r * ROWB + 16 * (k ^ ((r / RPB) & (CPR - 1))); };
-  int src_off[NL];
+  // Source offsets of this lane's 16-byte LDS slots: K rows (and int8 V rows)
+  // swizzled for the score operand reads, bf16 V rows for the transposed reads.
+  int src_off[NL], src_off_v[NL];
 #pragma unroll
   for (int c = 0; c < NL; ++c) {
     const int slot = 64 * c + lane;
     const int r = slot / CPR, p = slot % CPR;
     src_off[c] = r * ROWB + 16 * (p ^ ((r / RPB) & (CPR - 1)));
+    src_off_v[c] = kSwizzleV ? src_off[c] : r * ROWB + 16 * (p ^ vswz<ROWB>(r));
   }
   // This wave's share of stage st: loads wave*LPW .. +LPW-1 of the stage's
   // 2*KB*NL (K tiles, then V tiles; NL loads per tile).  An int8 stage's
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       const int phys = valid > 0 ? min(max(bt[blk], 0), a.num_blocks - 1) : 0;
       const size_t tile_off = (head_blocks + size_t(phys)) * TILE_BYTES;
       const __amdgpu_buffer_rsrc_t r = make_rsrc((isv ? vbase : kbase) + tile_off, valid * ROWB);
-      const int off = (isv && !kSwizzleV) ? 1024 * c + 16 * lane : src_off[c];
+      const int off = isv ? src_off_v[c] : src_off[c];
       buffer_load16_to_lds(r, buf + (isv ? KB + kb : kb) * TILE_BYTES + 1024 * c, off);
     }
   };
@@ -224,11 +227,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
         const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
         vb = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
       } else {
-        const uint16_t* col = reinterpret_cast<const uint16_t*>(sv) + 4 * grp * D + 16 * t + n;
-        uint32_t e[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) e[j] = col[j * D];
-        vb = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+        vb = v_operand_tr<ROWB>(sv, t, lane);
       }
       o[t] = M::mm16(pa, vb, o[t]);
     }
@@ -279,8 +278,12 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   }
 }
 
+// Eight waves (128 query rows) share each staged K/V stage: measured on 16
+// sequences x 512-token chunks, 16/8 heads, D = 128 against four waves,
+// 296 us instead of 523 us per call (a stage's loads are then covered by
+// twice the products); larger stages or 16 waves were slower.
 #ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 4
+#define PA_PREFILL_WAVES 8
 #endif
 
 template <typename KV>

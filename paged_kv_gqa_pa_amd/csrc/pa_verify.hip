@@ -52,8 +52,8 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   // loop.  Within a staged K tile (and an int8 V tile), 16-byte chunk k of key
   // row r sits at position k ^ ((r / RPB) mod CPR) of its row (RPB rows share
   // one 256-byte bank period), so that the operand reads below hit distinct
-  // banks.  A bf16 V tile stays in row order: its transposed reads then take
-  // one base address and immediate offsets (at a 4-way bank conflict).
+  // banks.  A bf16 V tile is swizzled for the LDS transpose reads that hand
+  // out its B operand (vswz, pa_mfma.h).
   constexpr int CPR = ROWB / 16;             // 16-byte chunks per key row
   constexpr int RPB = ROWB >= 256 ? 1 : 256 / ROWB;
   constexpr int SLOT = 2 * TILE_BYTES;       // one (K, V) tile pair
@@ -166,14 +166,16 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   // whole 128-byte lines of the tile.  A fetch with live == false reads
   // nothing (zero-record buffer resource), so the loop keeps one instruction
   // stream and one set of wait counts.
-  int src_off[NL];
+  int src_off[NL], src_off_v[NL];
+  constexpr bool kSwizzleV = kInt8;
 #pragma unroll
   for (int c = 0; c < NL; ++c) {
     const int slot = 64 * c + lane;          // destination 16-byte slot
     const int r = slot / CPR, p = slot % CPR;
     src_off[c] = r * ROWB + 16 * (p ^ ((r / RPB) & (CPR - 1)));
+    // bf16 V rows: the layout of the transposed operand reads
+    src_off_v[c] = kSwizzleV ? src_off[c] : r * ROWB + 16 * (p ^ vswz<ROWB>(r));
   }
-  constexpr bool kSwizzleV = kInt8;
   auto fetch = [&](int blk, bool live, int slot, float& ks, float& vs) {
     const int phys = min(max(tab.at(blk - blk_begin), 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * TILE_BYTES;
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
       buffer_load16_to_lds(kr, kbuf(slot) + 1024 * c, src_off[c]);
 #pragma unroll
     for (int c = 0; c < NL; ++c)
-      buffer_load16_to_lds(vr, vbuf(slot) + 1024 * c, kSwizzleV ? src_off[c] : 1024 * c + 16 * lane);
+      buffer_load16_to_lds(vr, vbuf(slot) + 1024 * c, src_off_v[c]);
     if constexpr (kInt8) {
       ks = a.k_scale[head_blocks + phys];
       vs = a.v_scale[head_blocks + phys];
@@ -279,12 +281,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
         vb = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
       } else {
-        // transposed reads: four keys of one dim
-        const uint16_t* col = reinterpret_cast<const uint16_t*>(sv) + 4 * grp * D + 16 * t + n;
-        uint32_t e[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) e[j] = col[j * D];
-        vb = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+        vb = v_operand_tr<ROWB>(sv, t, lane);   // four keys of one dim
       }
       o[t] = M::mm16(pa, vb, o[t]);
     }
