@@ -540,7 +540,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                 total_query_tokens, long(num_seqs) * max_query_tokens);
   const int G = q_heads / kv_heads;
   const long rows = long(max_query_tokens) * G;
-  const long tiles = (rows + 16L * pa::prefill_waves() - 1) / (16L * pa::prefill_waves());
+  const long per_wg = pa::prefill_rows_per_workgroup();
+  const long tiles = (rows + per_wg - 1) / per_wg;
   if (rows > 2147483647L || long(total_query_tokens) * q_heads > 2147483647L ||
       tiles * num_seqs * kv_heads > kMaxGrid)
     return fail(PA_ERR_UNSUPPORTED, "too many query rows or workgroups");

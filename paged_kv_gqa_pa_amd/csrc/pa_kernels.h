@@ -136,7 +136,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 // Chunked prefill (matrix cores): DecodeArgs with query_start set, no pieces.
 hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim);
-int prefill_waves();
+int prefill_rows_per_workgroup();
 hipError_t launch_reshape_and_cache(const CacheArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache_quant(const QuantCacheArgs& a, hipStream_t stream);
 hipError_t launch_decode_pass1(const DecodeArgs& a, bool append, hipStream_t stream);

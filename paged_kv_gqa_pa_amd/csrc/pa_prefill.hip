@@ -4,10 +4,11 @@
 // Sequence b's T_b new tokens are its last T_b positions (their K/V already in
 // the cache); token t sees positions 0 .. L_b - T_b + t, as in verify.
 //
-// Work item: one workgroup of NW waves per (tile of 16 * NW query rows, KV
-// head, sequence).  Row r of a sequence is query token r / G of head
-// g * G + r % G; wave w owns rows 16w .. 16w + 15 of the tile over the whole
-// visible context, so no partial results leave the workgroup.  The cache is
+// Work item: one workgroup of NW waves per (tile of 16 * RT * NW query rows,
+// KV head, sequence).  Row r of a sequence is query token r / G of head
+// g * G + r % G; wave w owns RT consecutive 16-row tiles (rows 16 RT w ..
+// 16 RT (w + 1) - 1) over the whole visible context, so no partial results
+// leave the workgroup.  The cache is
 // walked in stages of KB blocks (64 positions): the workgroup stages a
 // stage's K and V tiles in LDS with direct-to-LDS buffer loads (double
 // buffered, the next stage in flight while this one is used), and every wave
@@ -26,10 +27,26 @@
 #include "pa_kernels.h"
 #include "pa_mfma.h"
 
+#ifndef PA_PREFILL_STAGE_BLOCKS
+#define PA_PREFILL_STAGE_BLOCKS 4
+#endif
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 2
+#endif
+
 namespace pa {
 namespace {
 
-template <typename KV, int D, int NW>
+// f(integral_constant<int, i>) for i = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+template <typename KV, int D, int NW, int RT>
 __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   constexpr bool kInt8 = __is_same(KV, i8_t);
   constexpr int ROWB = D * int(sizeof(KV));      // bytes per key row
@@ -37,7 +54,9 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   constexpr int NQ = D / 32;                     // score products per tile
   constexpr int NT = D / 16;                     // output blocks of 16 dims
   constexpr int TILE_BYTES = kBlockSize * ROWB;
-  constexpr int KB = 4;                          // cache blocks per stage
+  // Cache blocks per stage: at least enough for one load per wave.
+  constexpr int KB = PA_PREFILL_STAGE_BLOCKS * 2 * NL >= NW ? PA_PREFILL_STAGE_BLOCKS : NW / (2 * NL);
+  constexpr int NBUF = PA_PREFILL_STAGES;        // stage buffers in the ring
   constexpr int STAGE = 2 * KB * TILE_BYTES;     // K tiles, then V tiles
   constexpr int LOADS = 2 * KB * NL;             // 1 KiB loads per stage
   static_assert(LOADS % NW == 0, "stage loads must split evenly over the waves");
@@ -60,26 +79,33 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   const int q0 = min(max(s0, 0), a.total_query_tokens);
   const int T = min(max(s1 - s0, 0), min(a.num_query_tokens, a.total_query_tokens - q0));
   const int R = T * G;
-  const int row0 = tile * NW * kRows;
+  constexpr int WROWS = RT * kRows;              // query rows per wave
+  const int row0 = tile * NW * WROWS;
   if (row0 >= R) return;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;     // key row of an operand read / query row of S, P
   const int grp = lane >> 4;   // 8-dim group of a score product / key quad of S, P, O
-  const int wrow0 = row0 + wave * kRows;
-  const int row = wrow0 + n;
-  const bool row_ok = row < R;
-  const int t_row = row / G;
-  const int h_row = g * G + (row - t_row * G);
+  const int wrow0 = row0 + wave * WROWS;
 
-  // Query rows as the B operand of score product c: lane (row n, group grp)
-  // holds q[n][32c + 8grp .. +7] (fp16 for an int8 cache).
-  u32x4 qb[NQ];
-  float qpart = 0.0f;
-  {
+  const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
+  // Row tile i of this wave: rows wrow0 + 16i .. +15.  Query rows as the B
+  // operand of score product c: lane (row n, group grp) holds
+  // q[n][32c + 8grp .. +7] (fp16 for an int8 cache).
+  u32x4 qb[RT][NQ];
+  float qsum[RT];
+  int last_vis[RT];   // last position row n of tile i sees
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int row = wrow0 + i * kRows + n;
+    const bool row_ok = row < R;
+    const int t_row = row / G;
+    const int h_row = g * G + (row - t_row * G);
+    last_vis[i] = row_ok ? L - T + t_row : -1;
     const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) +
                        ((size_t(q0) + t_row) * Hq + h_row) * D + 8 * grp;
+    float qpart = 0.0f;
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
       const u32x4 w = row_ok ? load16(qp + 32 * c) : u32x4{0u, 0u, 0u, 0u};
@@ -87,35 +113,46 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e]), bf16_hi(w[e]));
-          qb[c][e] = __builtin_bit_cast(uint32_t, hp);
+          qb[i][c][e] = __builtin_bit_cast(uint32_t, hp);
           qpart += float(hp[0]) + float(hp[1]);
         }
       } else {
-        qb[c] = w;
+        qb[i][c] = w;
       }
     }
+    qsum[i] = kInt8 ? add_xor32(add_xor16(qpart)) : 0.0f;
   }
-  const float qsum = kInt8 ? add_xor32(add_xor16(qpart)) : 0.0f;
 
-  const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
-  const int last_vis = row_ok ? L - T + t_row : -1;   // last position row n sees
   // Positions the workgroup needs (through its last row) and this wave needs.
-  const int t_last = (min(row0 + NW * kRows, R) - 1) / G;
+  const int t_last = (min(row0 + NW * WROWS, R) - 1) / G;
   const int kend = min(max(L - T + t_last + 1, 0), L);
-  const int w_kend = wrow0 < R ? min(max(L - T + (min(wrow0 + kRows, R) - 1) / G + 1, 0), L) : 0;
+  const int w_kend = wrow0 < R ? min(max(L - T + (min(wrow0 + WROWS, R) - 1) / G + 1, 0), L) : 0;
   const int nblk = cdiv(kend, kBlockSize);
   const int nst = cdiv(nblk, KB);
 
-  const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks_per_seq;
+  // The table row is read-only for this kernel: read through the constant
+  // address space, its (uniform) entries come through scalar loads, which the
+  // stage waits below (vector-memory counts) do not see.
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr bt = (const_i32_ptr)(a.block_tables + size_t(b) * a.max_blocks_per_seq);
   const size_t head_blocks = size_t(g) * a.num_blocks;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
   const float sc = a.scale * kLog2e;
 
-  // The two stages are separate LDS objects, so waiting for one stage's
-  // direct-to-LDS loads does not also wait for the other's.
+  // A ring of NBUF stage buffers, each its own LDS object, so that waiting
+  // for one stage's direct-to-LDS loads does not also wait for the others'.
   __shared__ __attribute__((aligned(16))) char s_st0[STAGE];
   __shared__ __attribute__((aligned(16))) char s_st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char s_st2[NBUF > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char s_st3[NBUF > 3 ? STAGE : 16];
+  auto ring = [&](auto u_tag) -> char* {
+    constexpr int u = decltype(u_tag)::value;
+    if constexpr (u == 0) return s_st0;
+    else if constexpr (u == 1) return s_st1;
+    else if constexpr (u == 2) return s_st2;
+    else return s_st3;
+  };
   auto sw = [](int r, int k) { return r * ROWB + 16 * (k ^ ((r / RPB) & (CPR - 1))); };
   // Source offsets of this lane's 16-byte LDS slots: K rows (and int8 V rows)
   // swizzled for the score operand reads, bf16 V rows for the transposed reads.
@@ -137,9 +174,12 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       for (int kb = 0; kb < KB; ++kb) {
         const int blk = st * KB + kb;
         const bool need = blk * kBlockSize < kend;
-        const int phys = need ? min(max(bt[blk], 0), a.num_blocks - 1) : 0;
-        ks[kb] = need ? a.k_scale[head_blocks + phys] : 0.0f;
-        vs[kb] = need ? a.v_scale[head_blocks + phys] : 0.0f;
+        // uniform addresses in the constant address space: scalar loads,
+        // outside the vector-memory count the stage waits below rely on
+        const int phys = need ? min(max(bt[readfirstlane(blk)], 0), a.num_blocks - 1) : 0;
+        typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+        ks[kb] = need ? ((const_f32_ptr)a.k_scale)[head_blocks + phys] : 0.0f;
+        vs[kb] = need ? ((const_f32_ptr)a.v_scale)[head_blocks + phys] : 0.0f;
       }
     }
 #pragma unroll
@@ -150,7 +190,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       const int c = li % NL;
       const int blk = st * KB + kb;
       const int valid = min(max(kend - blk * kBlockSize, 0), kBlockSize);
-      const int phys = valid > 0 ? min(max(bt[blk], 0), a.num_blocks - 1) : 0;
+      const int phys = valid > 0 ? min(max(bt[readfirstlane(blk)], 0), a.num_blocks - 1) : 0;
       const size_t tile_off = (head_blocks + size_t(phys)) * TILE_BYTES;
       const __amdgpu_buffer_rsrc_t r = make_rsrc((isv ? vbase : kbase) + tile_off, valid * ROWB);
       const int off = isv ? src_off_v[c] : src_off[c];
@@ -168,17 +208,24 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   const f32x4 vinit = {M::kVInit, M::kVInit, M::kVInit, M::kVInit};
 
   constexpr float kSlack = 8.0f;
-  float m = kNegInf;
-  float lsum = 0.0f;
-  f32x4 o[NT];
+  float m[RT], lsum[RT];
+  f32x4 o[RT][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RT; ++i) {
+    m[i] = kNegInf;
+    lsum[i] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // One 16-position tile (block blk, staged at kb of buf) for this wave's rows.
+  // One 16-position tile (block blk, staged at kb of buf) for this wave's
+  // RT row tiles: every K and V operand read from LDS feeds RT products.
   auto process = [&](const char* buf, int kb, int blk, float ks, float vs) {
     const char* const sk = buf + kb * TILE_BYTES;
     const char* const sv = buf + (KB + kb) * TILE_BYTES;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
       u32x4 kop;
@@ -189,36 +236,41 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       } else {
         kop = *reinterpret_cast<const u32x4*>(sk + sw(n, 4 * c + grp));
       }
-      s = M::qk(kop, qb[c], s);
+#pragma unroll
+      for (int i = 0; i < RT; ++i) s[i] = M::qk(kop, qb[i][c], s[i]);
     }
     const float ssc = sc * ks;
-    float tmax = kNegInf;
+    u32x2 pa[RT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int pos = blk * kBlockSize + 4 * grp + j;
-      const float x = (kInt8 ? s[j] - kI8Bias * qsum : s[j]) * ssc;
-      s[j] = pos <= last_vis ? x : kNegInf;
-      tmax = fmaxf(tmax, s[j]);
-    }
-    tmax = max_xor32(max_xor16(tmax));
-    if (__builtin_amdgcn_ballot_w64(tmax > m + kSlack) != 0) {
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
-      m = mnew;
-      lsum *= alpha;
+    for (int i = 0; i < RT; ++i) {
+      float tmax = kNegInf;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float ar = __shfl(alpha, 4 * grp + j);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) o[t][j] *= ar;
+        const int pos = blk * kBlockSize + 4 * grp + j;
+        const float x = (kInt8 ? s[i][j] - kI8Bias * qsum[i] : s[i][j]) * ssc;
+        s[i][j] = pos <= last_vis[i] ? x : kNegInf;
+        tmax = fmaxf(tmax, s[i][j]);
       }
-    }
-    const float mref = m == kNegInf ? 0.0f : m;
-    float p[4];
+      tmax = max_xor32(max_xor16(tmax));
+      if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
+        const float mnew = fmaxf(m[i], tmax);
+        const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
+        m[i] = mnew;
+        lsum[i] *= alpha;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[j] - mref);
-    lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    const u32x2 pa = {M::pack_round(p[0] * vs, p[1] * vs), M::pack_round(p[2] * vs, p[3] * vs)};
+        for (int j = 0; j < 4; ++j) {
+          const float ar = __shfl(alpha, 4 * grp + j);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) o[i][t][j] *= ar;
+        }
+      }
+      const float mref = m[i] == kNegInf ? 0.0f : m[i];
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[i][j] - mref);
+      lsum[i] += (p[0] + p[1]) + (p[2] + p[3]);
+      pa[i] = u32x2{M::pack_round(p[0] * vs, p[1] * vs), M::pack_round(p[2] * vs, p[3] * vs)};
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       u32x2 vb;
@@ -229,51 +281,66 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       } else {
         vb = v_operand_tr<ROWB>(sv, t, lane);
       }
-      o[t] = M::mm16(pa, vb, o[t]);
+#pragma unroll
+      for (int i = 0; i < RT; ++i) o[i][t] = M::mm16(pa[i], vb, o[i][t]);
     }
   };
 
-  // Stage st is used from buffer st % 2 while stage st + 1 loads into the
-  // other; the barrier after a stage frees its buffer for stage st + 2.
-  float ks_cur[KB] = {}, vs_cur[KB] = {}, ks_nxt[KB] = {}, vs_nxt[KB] = {};
-  if (nst > 0) fetch(0, s_st0, ks_cur, vs_cur);
-  for (int st = 0; st < nst; ++st) {
-    char* const cur = (st & 1) ? s_st1 : s_st0;
-    if (st + 1 < nst) {
-      fetch(st + 1, (st & 1) ? s_st0 : s_st1, ks_nxt, vs_nxt);
-      __builtin_amdgcn_s_waitcnt((LPW & 15) | ((LPW >> 4) << 14) | (7 << 4) | (15 << 8));
-    } else {
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
-    }
+  // Stage st lives in ring buffer st % NBUF; stages up to st + NBUF - 1 are
+  // requested while stage st is used.  One barrier per stage both publishes
+  // stage st (every wave has waited for its own share of its loads) and
+  // frees buffer (st - 1) % NBUF, which the stage st + NBUF - 1 loads issued
+  // right after it overwrite.  The loop is unrolled by NBUF so that buffers
+  // and each stage's int8 scales are compile-time choices.
+  float ks[NBUF][KB] = {}, vs[NBUF][KB] = {};
+  auto wait_tiles = [&](int later) {   // stage st done; `later` stages may still load
+    static_assert(NBUF - 2 <= 3 && (NBUF - 2) * LPW <= 63, "vmcnt range");
+    if (later <= 0) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(((LPW) & 15) | (((LPW) >> 4) << 14) | (7 << 4) | (15 << 8));
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(((2 * LPW) & 15) | (((2 * LPW) >> 4) << 14) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt(((3 * LPW) & 15) | (((3 * LPW) >> 4) << 14) | (7 << 4) | (15 << 8));
     __asm__ __volatile__("" ::: "memory");
-    __syncthreads();
+  };
+  static_for<0, NBUF - 1>([&](auto u_tag) {
+    constexpr int u = decltype(u_tag)::value;
+    if (u < nst) fetch(u, ring(u_tag), ks[u], vs[u]);
+  });
+  for (int st0 = 0; st0 < nst; st0 += NBUF) {
+    static_for<0, NBUF>([&](auto u_tag) {
+      constexpr int u = decltype(u_tag)::value;
+      constexpr int nu = (u + NBUF - 1) % NBUF;   // ring slot of stage st + NBUF - 1
+      const int st = st0 + u;
+      if (st < nst) {
+        wait_tiles(min(NBUF - 2, nst - 1 - st));
+        __syncthreads();
+        if (st + NBUF - 1 < nst)
+          fetch(st + NBUF - 1, ring(std::integral_constant<int, nu>{}), ks[nu], vs[nu]);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int blk = st * KB + kb;
-      if (blk * kBlockSize < w_kend)   // uniform per wave
-        process(cur, kb, blk, kInt8 ? ks_cur[kb] : 1.0f, kInt8 ? vs_cur[kb] : 1.0f);
-    }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      ks_cur[kb] = ks_nxt[kb];
-      vs_cur[kb] = vs_nxt[kb];
-    }
-    __syncthreads();
+        for (int kb = 0; kb < KB; ++kb) {
+          const int blk = st * KB + kb;
+          if (blk * kBlockSize < w_kend)   // uniform per wave
+            process(ring(u_tag), kb, blk, kInt8 ? ks[u][kb] : 1.0f, kInt8 ? vs[u][kb] : 1.0f);
+        }
+      }
+    });
   }
 
   // Row totals, then O / l per row, rounded to bf16.
-  const float lrow = add_xor32(add_xor16(lsum));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = wrow0 + 4 * grp + j;
-    const float lr = __shfl(lrow, 4 * grp + j);
-    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-    if (r < R) {
-      const int tq = r / G;
-      const size_t orow = (size_t(q0) + tq) * Hq + size_t(g) * G + (r - tq * G);
-      bf16_t* dst = reinterpret_cast<bf16_t*>(a.out) + orow * D + n;
+  for (int i = 0; i < RT; ++i) {
+    const float lrow = add_xor32(add_xor16(lsum[i]));
 #pragma unroll
-      for (int t = 0; t < NT; ++t) dst[16 * t].bits = f32_to_bf16(o[t][j] * inv);
+    for (int j = 0; j < 4; ++j) {
+      const int r = wrow0 + i * kRows + 4 * grp + j;
+      const float lr = __shfl(lrow, 4 * grp + j);
+      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+      if (r < R) {
+        const int tq = r / G;
+        const size_t orow = (size_t(q0) + tq) * Hq + size_t(g) * G + (r - tq * G);
+        bf16_t* dst = reinterpret_cast<bf16_t*>(a.out) + orow * D + n;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) dst[16 * t].bits = f32_to_bf16(o[i][t][j] * inv);
+      }
     }
   }
 }
@@ -285,23 +352,29 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
 #ifndef PA_PREFILL_WAVES
 #define PA_PREFILL_WAVES 8
 #endif
+// 16-row tiles per wave: each K / V operand read from LDS serves this many
+// products.  Two tiles (measured 265 us against 238 us for one on the
+// 16 x 512-token workload) need 152 VGPRs, which halves the workgroups per CU.
+#ifndef PA_PREFILL_ROW_TILES
+#define PA_PREFILL_ROW_TILES 1
+#endif
 
 template <typename KV>
 hipError_t launch_prefill_t(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int NW = PA_PREFILL_WAVES;
+  constexpr int NW = PA_PREFILL_WAVES, RT = PA_PREFILL_ROW_TILES;
   const int G = a.q_heads / a.kv_heads;
-  const long tiles = cdiv(a.num_query_tokens * G, NW * kRows);
+  const long tiles = cdiv(a.num_query_tokens * G, NW * RT * kRows);
   const long wgs = tiles * a.num_seqs * a.kv_heads;
   if (a.head_dim == 128)
-    prefill_rows<KV, 128, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    prefill_rows<KV, 128, NW, RT><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   else
-    prefill_rows<KV, 64, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    prefill_rows<KV, 64, NW, RT><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_waves() { return PA_PREFILL_WAVES; }
+int prefill_rows_per_workgroup() { return PA_PREFILL_WAVES * PA_PREFILL_ROW_TILES * kRows; }
 
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim) {
   return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kI8) &&
