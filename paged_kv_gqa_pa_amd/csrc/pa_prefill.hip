@@ -54,8 +54,10 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   constexpr int NQ = D / 32;                     // score products per tile
   constexpr int NT = D / 16;                     // output blocks of 16 dims
   constexpr int TILE_BYTES = kBlockSize * ROWB;
-  // Cache blocks per stage: at least enough for one load per wave.
+  // Cache blocks per stage (an even number: they are used in pairs), at least
+  // enough for one load per wave.
   constexpr int KB = PA_PREFILL_STAGE_BLOCKS * 2 * NL >= NW ? PA_PREFILL_STAGE_BLOCKS : NW / (2 * NL);
+  static_assert(KB % 2 == 0, "stages hold pairs of blocks");
   constexpr int NBUF = PA_PREFILL_STAGES;        // stage buffers in the ring
   constexpr int STAGE = 2 * KB * TILE_BYTES;     // K tiles, then V tiles
   constexpr int LOADS = 2 * KB * NL;             // 1 KiB loads per stage
@@ -127,6 +129,8 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   const int t_last = (min(row0 + NW * WROWS, R) - 1) / G;
   const int kend = min(max(L - T + t_last + 1, 0), L);
   const int w_kend = wrow0 < R ? min(max(L - T + (min(wrow0 + WROWS, R) - 1) / G + 1, 0), L) : 0;
+  // Last position the wave's first row sees: every row sees at least this far.
+  const int w_minvis = wrow0 < R ? L - T + wrow0 / G : -1;
   const int nblk = cdiv(kend, kBlockSize);
   const int nst = cdiv(nblk, KB);
 
@@ -218,39 +222,57 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
     for (int t = 0; t < NT; ++t) o[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One 16-position tile (block blk, staged at kb of buf) for this wave's
-  // RT row tiles: every K and V operand read from LDS feeds RT products.
-  auto process = [&](const char* buf, int kb, int blk, float ks, float vs) {
-    const char* const sk = buf + kb * TILE_BYTES;
-    const char* const sv = buf + (KB + kb) * TILE_BYTES;
-    f32x4 s[RT];
+  // Two 16-position tiles (blocks blk, blk + 1, staged at kb, kb + 1 of buf)
+  // for this wave's RT row tiles.  Lane (n, grp) holds row n's scores of keys
+  // 4grp .. 4grp+3 of both blocks; read as keys 8grp .. 8grp+7 of one 32-key
+  // product, with V's rows in the same order (the two blocks' transposed
+  // reads side by side), P.V runs on 16x16x32 products.  Positions are masked
+  // only where the pair crosses the wave's causal edge.
+  auto process2 = [&](const char* buf, int kb, int blk, float ks0, float vs0, float ks1,
+                      float vs1) {
+    const char* const sk0 = buf + kb * TILE_BYTES;
+    const char* const sv0 = buf + (KB + kb) * TILE_BYTES;
+    f32x4 s[RT][2];
 #pragma unroll
-    for (int i = 0; i < RT; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < RT; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-      u32x4 kop;
-      if constexpr (kInt8) {
-        const int k = (32 * c + 8 * grp) / 16;
-        const uint2 w = *reinterpret_cast<const uint2*>(sk + sw(n, k) + 8 * (grp & 1));
-        kop = codes8_f16(w.x, w.y);
-      } else {
-        kop = *reinterpret_cast<const u32x4*>(sk + sw(n, 4 * c + grp));
-      }
 #pragma unroll
-      for (int i = 0; i < RT; ++i) s[i] = M::qk(kop, qb[i][c], s[i]);
+      for (int h = 0; h < 2; ++h) {
+        const char* const sk = sk0 + h * TILE_BYTES;
+        u32x4 kop;
+        if constexpr (kInt8) {
+          const int k = (32 * c + 8 * grp) / 16;
+          const uint2 w = *reinterpret_cast<const uint2*>(sk + sw(n, k) + 8 * (grp & 1));
+          kop = codes8_f16(w.x, w.y);
+        } else {
+          kop = *reinterpret_cast<const u32x4*>(sk + sw(n, 4 * c + grp));
+        }
+#pragma unroll
+        for (int i = 0; i < RT; ++i) s[i][h] = M::qk(kop, qb[i][c], s[i][h]);
+      }
     }
-    const float ssc = sc * ks;
-    u32x2 pa[RT];
+    const bool edge = (blk + 2) * kBlockSize - 1 > w_minvis;   // uniform per wave
+    const float ssc[2] = {sc * ks0, sc * ks1};
+    const float vsc[2] = {vs0, vs1};
+    u32x4 pa[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      float tmax = kNegInf;
+      float x[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pos = blk * kBlockSize + 4 * grp + j;
-        const float x = (kInt8 ? s[i][j] - kI8Bias * qsum[i] : s[i][j]) * ssc;
-        s[i][j] = pos <= last_vis[i] ? x : kNegInf;
-        tmax = fmaxf(tmax, s[i][j]);
+      for (int e = 0; e < 8; ++e) {
+        const float v = s[i][e >> 2][e & 3];
+        x[e] = (kInt8 ? v - kI8Bias * qsum[i] : v) * ssc[e >> 2];
       }
+      if (edge) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pos = (blk + (e >> 2)) * kBlockSize + 4 * grp + (e & 3);
+          x[e] = pos <= last_vis[i] ? x[e] : kNegInf;
+        }
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       tmax = max_xor32(max_xor16(tmax));
       if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
         const float mnew = fmaxf(m[i], tmax);
@@ -265,24 +287,30 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
         }
       }
       const float mref = m[i] == kNegInf ? 0.0f : m[i];
-      float p[4];
+      float p[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[i][j] - mref);
-      lsum[i] += (p[0] + p[1]) + (p[2] + p[3]);
-      pa[i] = u32x2{M::pack_round(p[0] * vs, p[1] * vs), M::pack_round(p[2] * vs, p[3] * vs)};
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] - mref);
+      lsum[i] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pa[i] = u32x4{M::pack_round(p[0] * vsc[0], p[1] * vsc[0]), M::pack_round(p[2] * vsc[0], p[3] * vsc[0]),
+                    M::pack_round(p[4] * vsc[1], p[5] * vsc[1]), M::pack_round(p[6] * vsc[1], p[7] * vsc[1])};
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      u32x2 vb;
-      if constexpr (kInt8) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(sv + sw(n, t) + 4 * grp) ^ 0x80808080u;
-        const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
-        vb = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
-      } else {
-        vb = v_operand_tr<ROWB>(sv, t, lane);
-      }
+      u32x2 vb[2];
 #pragma unroll
-      for (int i = 0; i < RT; ++i) o[i][t] = M::mm16(pa[i], vb, o[i][t]);
+      for (int h = 0; h < 2; ++h) {
+        const char* const sv = sv0 + h * TILE_BYTES;
+        if constexpr (kInt8) {
+          const uint32_t u = *reinterpret_cast<const uint32_t*>(sv + sw(n, t) + 4 * grp) ^ 0x80808080u;
+          const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
+          vb[h] = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
+        } else {
+          vb[h] = v_operand_tr<ROWB>(sv, t, lane);
+        }
+      }
+      const u32x4 v8 = {vb[0][0], vb[0][1], vb[1][0], vb[1][1]};
+#pragma unroll
+      for (int i = 0; i < RT; ++i) o[i][t] = M::qk(pa[i], v8, o[i][t]);
     }
   };
 
@@ -316,10 +344,11 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
         if (st + NBUF - 1 < nst)
           fetch(st + NBUF - 1, ring(std::integral_constant<int, nu>{}), ks[nu], vs[nu]);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; kb += 2) {
           const int blk = st * KB + kb;
           if (blk * kBlockSize < w_kend)   // uniform per wave
-            process(ring(u_tag), kb, blk, kInt8 ? ks[u][kb] : 1.0f, kInt8 ? vs[u][kb] : 1.0f);
+            process2(ring(u_tag), kb, blk, kInt8 ? ks[u][kb] : 1.0f, kInt8 ? vs[u][kb] : 1.0f,
+                     kInt8 ? ks[u][kb + 1] : 1.0f, kInt8 ? vs[u][kb + 1] : 1.0f);
         }
       }
     });
