@@ -29,8 +29,10 @@ template <> struct MOps<bf16_t> {
   __device__ static uint32_t pack_exact(float lo, float hi) {
     return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   }
+  // Two fp32 values rounded to nearest even, in one packed conversion.
   __device__ static uint32_t pack_round(float lo, float hi) {
-    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
   }
 };
 template <> struct MOps<i8_t> {
