@@ -168,24 +168,27 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
     src_off[c] = r * ROWB + 16 * (p ^ ((r / RPB) & (CPR - 1)));
     src_off_v[c] = kSwizzleV ? src_off[c] : r * ROWB + 16 * (p ^ vswz<ROWB>(r));
   }
-  // This wave's share of stage st: loads wave*LPW .. +LPW-1 of the stage's
-  // 2*KB*NL (K tiles, then V tiles; NL loads per tile).  An int8 stage's
-  // block scales are requested first, into ks / vs, so the wait for the
-  // stage's tiles covers them too.
-  auto fetch = [&](int st, char* buf, float (&ks)[KB], float (&vs)[KB]) {
-    if constexpr (kInt8) {
+  // The physical blocks of stage st (and for int8 their scales), through
+  // scalar loads: uniform addresses in the constant address space, outside
+  // the vector-memory count the stage waits below rely on.  A stage's lookup
+  // is issued one stage before its tile loads, so their latency overlaps the
+  // previous stage's wait.
+  auto lookup = [&](int st, int (&phys)[KB], float (&ks)[KB], float (&vs)[KB]) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int blk = st * KB + kb;
-        const bool need = blk * kBlockSize < kend;
-        // uniform addresses in the constant address space: scalar loads,
-        // outside the vector-memory count the stage waits below rely on
-        const int phys = need ? min(max(bt[readfirstlane(blk)], 0), a.num_blocks - 1) : 0;
+    for (int kb = 0; kb < KB; ++kb) {
+      const int blk = st * KB + kb;
+      const bool need = blk * kBlockSize < kend;
+      phys[kb] = need ? min(max(bt[readfirstlane(blk)], 0), a.num_blocks - 1) : 0;
+      if constexpr (kInt8) {
         typedef const __attribute__((address_space(4))) float* const_f32_ptr;
-        ks[kb] = need ? ((const_f32_ptr)a.k_scale)[head_blocks + phys] : 0.0f;
-        vs[kb] = need ? ((const_f32_ptr)a.v_scale)[head_blocks + phys] : 0.0f;
+        ks[kb] = need ? ((const_f32_ptr)a.k_scale)[head_blocks + phys[kb]] : 0.0f;
+        vs[kb] = need ? ((const_f32_ptr)a.v_scale)[head_blocks + phys[kb]] : 0.0f;
       }
     }
+  };
+  // This wave's share of stage st's tile loads: loads wave*LPW .. +LPW-1 of
+  // the stage's 2*KB*NL (K tiles, then V tiles; NL loads per tile).
+  auto fetch = [&](int st, char* buf, const int (&phys)[KB]) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int li = wave * LPW + i;
@@ -194,8 +197,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       const int c = li % NL;
       const int blk = st * KB + kb;
       const int valid = min(max(kend - blk * kBlockSize, 0), kBlockSize);
-      const int phys = valid > 0 ? min(max(bt[readfirstlane(blk)], 0), a.num_blocks - 1) : 0;
-      const size_t tile_off = (head_blocks + size_t(phys)) * TILE_BYTES;
+      const size_t tile_off = (head_blocks + size_t(valid > 0 ? phys[kb] : 0)) * TILE_BYTES;
       const __amdgpu_buffer_rsrc_t r = make_rsrc((isv ? vbase : kbase) + tile_off, valid * ROWB);
       const int off = isv ? src_off_v[c] : src_off[c];
       buffer_load16_to_lds(r, buf + (isv ? KB + kb : kb) * TILE_BYTES + 1024 * c, off);
@@ -228,11 +230,11 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   // product, with V's rows in the same order (the two blocks' transposed
   // reads side by side), P.V runs on 16x16x32 products.  Positions are masked
   // only where the pair crosses the wave's causal edge.
-  auto process2 = [&](const char* buf, int kb, int blk, float ks0, float vs0, float ks1,
-                      float vs1) {
+  // Scores of a pair (the products only; issued for every pair of a stage
+  // before any softmax, so the matrix cores work on the next pair's scores
+  // while the vector ALUs take the softmax of this one).
+  auto scores2 = [&](const char* buf, int kb, f32x4 (&s)[RT][2]) {
     const char* const sk0 = buf + kb * TILE_BYTES;
-    const char* const sv0 = buf + (KB + kb) * TILE_BYTES;
-    f32x4 s[RT][2];
 #pragma unroll
     for (int i = 0; i < RT; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -252,6 +254,10 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
         for (int i = 0; i < RT; ++i) s[i][h] = M::qk(kop, qb[i][c], s[i][h]);
       }
     }
+  };
+  auto softmax_pv2 = [&](const char* buf, int kb, int blk, f32x4 (&s)[RT][2], float ks0,
+                         float vs0, float ks1, float vs1) {
+    const char* const sv0 = buf + (KB + kb) * TILE_BYTES;
     const bool edge = (blk + 2) * kBlockSize - 1 > w_minvis;   // uniform per wave
     const float ssc[2] = {sc * ks0, sc * ks1};
     const float vsc[2] = {vs0, vs1};
@@ -321,6 +327,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   // right after it overwrite.  The loop is unrolled by NBUF so that buffers
   // and each stage's int8 scales are compile-time choices.
   float ks[NBUF][KB] = {}, vs[NBUF][KB] = {};
+  int phys_next[KB] = {};
   auto wait_tiles = [&](int later) {   // stage st done; `later` stages may still load
     static_assert(NBUF - 2 <= 3 && (NBUF - 2) * LPW <= 63, "vmcnt range");
     if (later <= 0) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
@@ -331,8 +338,13 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   };
   static_for<0, NBUF - 1>([&](auto u_tag) {
     constexpr int u = decltype(u_tag)::value;
-    if (u < nst) fetch(u, ring(u_tag), ks[u], vs[u]);
+    if (u < nst) {
+      int phys[KB];
+      lookup(u, phys, ks[u], vs[u]);
+      fetch(u, ring(u_tag), phys);
+    }
   });
+  if (NBUF - 1 < nst) lookup(NBUF - 1, phys_next, ks[NBUF - 1], vs[NBUF - 1]);
   for (int st0 = 0; st0 < nst; st0 += NBUF) {
     static_for<0, NBUF>([&](auto u_tag) {
       constexpr int u = decltype(u_tag)::value;
@@ -341,15 +353,23 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       if (st < nst) {
         wait_tiles(min(NBUF - 2, nst - 1 - st));
         __syncthreads();
-        if (st + NBUF - 1 < nst)
-          fetch(st + NBUF - 1, ring(std::integral_constant<int, nu>{}), ks[nu], vs[nu]);
+        if (st + NBUF - 1 < nst) fetch(st + NBUF - 1, ring(std::integral_constant<int, nu>{}), phys_next);
+        f32x4 sc2[KB / 2][RT][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; kb += 2)
+          if ((st * KB + kb) * kBlockSize < w_kend)   // uniform per wave
+            scores2(ring(u_tag), kb, sc2[kb / 2]);
 #pragma unroll
         for (int kb = 0; kb < KB; kb += 2) {
           const int blk = st * KB + kb;
-          if (blk * kBlockSize < w_kend)   // uniform per wave
-            process2(ring(u_tag), kb, blk, kInt8 ? ks[u][kb] : 1.0f, kInt8 ? vs[u][kb] : 1.0f,
-                     kInt8 ? ks[u][kb + 1] : 1.0f, kInt8 ? vs[u][kb + 1] : 1.0f);
+          if (blk * kBlockSize < w_kend)
+            softmax_pv2(ring(u_tag), kb, blk, sc2[kb / 2], kInt8 ? ks[u][kb] : 1.0f,
+                        kInt8 ? vs[u][kb] : 1.0f, kInt8 ? ks[u][kb + 1] : 1.0f,
+                        kInt8 ? vs[u][kb + 1] : 1.0f);
         }
+        // the table entries (and scales) of the stage after next, into the
+        // slot just used
+        if (st + NBUF < nst) lookup(st + NBUF, phys_next, ks[u], vs[u]);
       }
     });
   }
