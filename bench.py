@@ -670,14 +670,18 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+# The sources the batch-64 decode kernel (decode_pass1) is built from: stored
+# hardware byte counts stay valid while these are unchanged.
+DECODE_KERNEL_SOURCES = ("pa_decode.hip", "pa_device.h", "pa_kernels.h")
+
+
 def _kernel_hash():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_gqa_pa_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
-        if n.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, n), "rb") as f:
-                h.update(f.read())
+    for n in DECODE_KERNEL_SOURCES:
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
