@@ -131,9 +131,12 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
         wsb = pa.workspace_size(N, T, Hq, Hkv, D, spec.max_len, kdt, split)
         ws = torch.zeros(max(256, wsb), dtype=torch.uint8, device=dev)
         fn = pa.verify if T > 1 else pa.decode
-        # one work plan for the call's tables and lengths (made once, as once per step)
+        # One work plan for the call's tables and lengths (made once, as once per step),
+        # where it pays: lengths that vary on a bandwidth-bound launch.  The Qwen2-shaped
+        # decode is latency-bound (64 workgroups; the plan row's read delays the query
+        # load by ~0.2 us) and the long-context lengths are all equal.
         plan = None
-        if use_plan and not varlen:
+        if use_plan and name == "spec_verify_bf16":
             plan = pa.make_plan(bt, cl, Hq, Hkv, D, spec.max_len, kdt, num_query_tokens=T,
                                 split_tokens=split)
 

@@ -41,8 +41,11 @@ struct SplitPlan {
 // every int8 cache; a bf16 decode call goes there too from groups of 4 query
 // heads up (measured: at G = 2 the vector-ALU kernel is ~5 % faster, at G = 6
 // the matrix-core one ~15 %).  fp32 decode stays on the vector ALUs.
+#ifndef PA_ROWS_MIN_GROUP
+#define PA_ROWS_MIN_GROUP 4
+#endif
 bool rows_kernel(int T, int G, int kv_dtype) {
-  return T > 1 || kv_dtype == PA_INT8 || (kv_dtype == PA_BF16 && G >= 4);
+  return T > 1 || kv_dtype == PA_INT8 || (kv_dtype == PA_BF16 && G >= PA_ROWS_MIN_GROUP);
 }
 
 // Piece length for split_tokens = 0.  It depends on the shape only, never on
