@@ -181,9 +181,9 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
 
 
 def prefill_timing(torch, pa, dev, reps=10, calls=8):
-    """Chunked prefill (pa_prefill): 16 sequences, each a 512-token chunk on top of a
-    seeded prior context U{0..1536}, 16 query / 8 KV heads, head_dim 128, bf16 cache of
-    8192 blocks.  Reported against the bf16 matrix-core peak (the causal products are the
+    """Chunked prefill (pa_prefill, started from a prefill work plan; the natural order
+    is timed beside it): 16 sequences, each a 512-token chunk on top of a seeded prior
+    context U{0..1536}, 16 query / 8 KV heads, head_dim 128, bf16 cache of 8192 blocks.  Reported against the bf16 matrix-core peak (the causal products are the
     work: 4 * head_dim flops per (query row, visible position)) and as HBM bytes (K/V of
     each sequence once, q, out, tables)."""
     N, T, Hq, Hkv, D, NB = 16, 512, 16, 8, 128, 8192
@@ -208,23 +208,30 @@ def prefill_timing(torch, pa, dev, reps=10, calls=8):
     cl = torch.from_numpy(lens).to(dev)
     qs = torch.from_numpy(np.arange(0, N * T + 1, T).astype(np.int32)).to(dev)
 
-    def run():
-        for _ in range(calls):
-            pa.prefill(o, q, kc, vc, bt, cl, qs, 1.0 / float(np.sqrt(D)), T)
-    run()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    # one prefill work plan (tiles longest first), made once for the call's offsets and lengths
+    plan = pa.make_prefill_plan(cl, qs, N * T, T, Hq, Hkv, maxb)
+
+    def timed(use_plan):
+        def run():
+            for _ in range(calls):
+                pa.prefill(o, q, kc, vc, bt, cl, qs, 1.0 / float(np.sqrt(D)), T,
+                           plan=plan if use_plan else None)
         run()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
         g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * calls)
+    us_natural = timed(False)
+    us = timed(True)
     visible = int(sum(int(p) * T + T * (T + 1) // 2 for p in prior))   # per head
     flops = 4 * D * Hq * visible
     alg = (int(lens.sum()) * Hkv * D * 2 * 2 + 2 * N * T * Hq * D * 2 +
@@ -234,9 +241,11 @@ def prefill_timing(torch, pa, dev, reps=10, calls=8):
            "us_per_call": round(us, 2), "flops": flops, "tflops": round(tflops, 1),
            "mfma_frac": round(tflops / 2500.0, 4), "algorithmic_bytes": alg,
            "hbm_gbps": round(alg / (us * 1e-6) / 1e9, 1), "query_tokens_per_s": round(N * T / (us * 1e-6), 1),
-           "kernel": "prefill_rows"}
+           "kernel": "prefill_rows", "work_plan": True,
+           "natural_order_us_per_call": round(us_natural, 2)}
     print(f"[bench] chunked prefill: {us:.2f} us/call, {tflops:.1f} TFLOP/s "
-          f"({100 * tflops / 2500.0:.1f}% of bf16 matrix peak)", flush=True)
+          f"({100 * tflops / 2500.0:.1f}% of bf16 matrix peak; natural order {us_natural:.2f} us)",
+          flush=True)
     del kc, vc
     torch.cuda.empty_cache()
     return res

@@ -394,6 +394,43 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                int max_context_len, float scale, int q_dtype, int kv_dtype, void* stream);
 
+/*
+ * Prefill work plans -- pa_prefill's (sequence, tile of query rows) units in
+ * the order they are started, longest first.
+ *
+ * A prefill tile's work is the number of cached positions its last query row
+ * sees (causal); with chunks on top of prior contexts of different lengths the
+ * tiles differ many times over, and in the natural order (later tiles of every
+ * sequence first) the longest can end the launch alone.  A plan orders the
+ * tiles by that length (in 256 buckets of equal width).  Each tile's
+ * arithmetic does not depend on the order: pa_prefill_planned gives the bits
+ * pa_prefill gives.
+ *
+ * pa_prefill_plan_size -- bytes of a plan (0 and pa_last_error on invalid
+ *   sizes or more than 8192 units; units = num_seqs * ceil(max_query_tokens *
+ *   (q_heads / kv_heads) / rows per workgroup)).
+ * pa_prefill_plan -- writes the plan from context_lens and query_start (the
+ *   pa_prefill arguments; device memory read on `stream`).  It holds copies of
+ *   the offsets and lengths: make it again whenever they change.
+ * pa_prefill_planned -- pa_prefill started in the plan's order.  plan_bytes
+ *   must be at least pa_prefill_plan_size(...) for the call's sizes, else
+ *   PA_ERR_INVALID_ARG; a plan made for other sizes is detected on the device
+ *   and ignored (natural order).
+ */
+size_t pa_prefill_plan_size(int num_seqs, int max_query_tokens, int q_heads, int kv_heads);
+
+int pa_prefill_plan(const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                    int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+                    int max_blocks_per_seq, void* plan, size_t plan_bytes, void* stream);
+
+int pa_prefill_planned(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                       int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+                       int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                       int max_context_len, float scale, int q_dtype, int kv_dtype,
+                       const void* plan, size_t plan_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_a
             "pa_default_split_tokens",
             "pa_workspace_size", "pa_decode", "pa_decode_append", "pa_verify", "pa_verify_varlen",
             "pa_prefill", "pa_plan_size", "pa_plan", "pa_decode_planned",
-            "pa_decode_append_planned", "pa_verify_planned"]
+            "pa_decode_append_planned", "pa_verify_planned", "pa_prefill_plan_size",
+            "pa_prefill_plan", "pa_prefill_planned"]
 
 _DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_INT8}
 
@@ -91,6 +92,12 @@ def _load():
     lib.pa_decode_append_planned.argtypes = lib.pa_decode_append.argtypes[:-1] + [vp, sz, vp]
     lib.pa_verify_planned.restype = i
     lib.pa_verify_planned.argtypes = lib.pa_verify.argtypes[:-1] + [vp, sz, vp]
+    lib.pa_prefill_plan_size.restype = sz
+    lib.pa_prefill_plan_size.argtypes = [i, i, i, i]
+    lib.pa_prefill_plan.restype = i
+    lib.pa_prefill_plan.argtypes = [vp, vp, i, i, i, i, i, i, vp, sz, vp]
+    lib.pa_prefill_planned.restype = i
+    lib.pa_prefill_planned.argtypes = lib.pa_prefill.argtypes[:-1] + [vp, sz, vp]
     _lib = lib
     return lib
 
@@ -351,10 +358,38 @@ def verify_varlen(out, q, k_cache, v_cache, block_tables, context_lens, query_st
     return out
 
 
+def prefill_plan_size(num_seqs: int, max_query_tokens: int, q_heads: int, kv_heads: int) -> int:
+    return _load().pa_prefill_plan_size(num_seqs, max_query_tokens, q_heads, kv_heads)
+
+
+def make_prefill_plan(context_lens, query_start, total_query_tokens, max_query_tokens, q_heads,
+                      kv_heads, max_blocks_per_seq, plan=None, stream=None):
+    """Prefill work plan (row tiles longest first) for pa_prefill calls with these offsets and
+    lengths; returns the plan buffer (a uint8 tensor, allocated when `plan` is None)."""
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _need(query_start, "query_start", dtype=torch.int32, ndim=1)
+    N = context_lens.shape[0]
+    if query_start.shape[0] != N + 1:
+        raise ValueError("query_start must have num_seqs + 1 entries")
+    need = _load().pa_prefill_plan_size(N, int(max_query_tokens), q_heads, kv_heads)
+    if need == 0:
+        raise PAError(PA_ERR_UNSUPPORTED, _load().pa_last_error().decode())
+    if plan is None:
+        plan = torch.empty(need, dtype=torch.uint8, device=context_lens.device)
+    _need(plan, "plan")
+    _check(_load().pa_prefill_plan(_ptr(context_lens), _ptr(query_start), N,
+                                   int(total_query_tokens), int(max_query_tokens), q_heads,
+                                   kv_heads, int(max_blocks_per_seq), _ptr(plan),
+                                   plan.numel() * plan.element_size(), _stream(stream)))
+    return plan
+
+
 def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
-            max_query_tokens, k_scale=None, v_scale=None, max_context_len=None, stream=None):
+            max_query_tokens, k_scale=None, v_scale=None, max_context_len=None, stream=None,
+            plan=None):
     """Chunked prefill: q/out [total_query_tokens, q_heads, head_dim] packed by sequence,
-    query_start int32 [num_seqs+1]; sequence b's tokens are its last positions."""
+    query_start int32 [num_seqs+1]; sequence b's tokens are its last positions.  With `plan`
+    (make_prefill_plan): pa_prefill_planned, same bits."""
     _need(q, "q", ndim=3)
     _need(out, "out", dtype=q.dtype, ndim=3)
     if out.shape != q.shape:
@@ -380,11 +415,14 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, s
     else:
         k_scale = v_scale = None
     mcl = block_tables.shape[1] * BS if max_context_len is None else int(max_context_len)
-    _check(_load().pa_prefill(
-        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-        _ptr(block_tables), _ptr(context_lens), _ptr(query_start), N, total,
-        int(max_query_tokens), Hq, Hkv, D, BS, NB, block_tables.shape[1], mcl, float(scale),
-        _DTYPE[q.dtype], kvd, _stream(stream)))
+    args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_tables), _ptr(context_lens), _ptr(query_start), N, total,
+            int(max_query_tokens), Hq, Hkv, D, BS, NB, block_tables.shape[1], mcl, float(scale),
+            _DTYPE[q.dtype], kvd]
+    if plan is None:
+        _check(_load().pa_prefill(*args, _stream(stream)))
+    else:
+        _check(_load().pa_prefill_planned(*args, *_plan_args(plan), _stream(stream)))
     return out
 
 

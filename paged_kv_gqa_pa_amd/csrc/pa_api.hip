@@ -515,12 +515,29 @@ int pa_verify_planned(void* out, const void* q, const void* k_cache, const void*
                        Append(), Varlen(), plan, plan_bytes);
 }
 
-int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
-               const float* k_scale, const float* v_scale, const int32_t* block_tables,
-               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
-               int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
-               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
-               int max_context_len, float scale, int q_dtype, int kv_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Prefill plan bytes for these sizes (0 past kMaxPlanUnits units).
+size_t prefill_plan_bytes(int num_seqs, int max_query_tokens, int q_heads, int kv_heads) {
+  if (num_seqs < 0 || max_query_tokens < 1 || q_heads <= 0 || kv_heads <= 0 ||
+      q_heads % kv_heads != 0)
+    return 0;
+  const long rows = long(max_query_tokens) * (q_heads / kv_heads);
+  const long per_wg = pa::prefill_rows_per_workgroup();
+  const long units = long(num_seqs) * ((rows + per_wg - 1) / per_wg);
+  if (units > pa::kMaxPlanUnits) return 0;
+  return size_t(pa::kPlanHeader + units * pa::kPrefillPlanRow) * sizeof(int32_t);
+}
+
+int run_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+                int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                int max_context_len, float scale, int q_dtype, int kv_dtype, void* stream,
+                const void* plan, size_t plan_bytes) {
   if (num_seqs < 0 || max_query_tokens < 1 || q_heads <= 0 || kv_heads <= 0 ||
       max_context_len < 0)
     return fail(PA_ERR_INVALID_ARG,
@@ -548,6 +565,16 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   if (rows > 2147483647L || long(total_query_tokens) * q_heads > 2147483647L ||
       tiles * num_seqs * kv_heads > kMaxGrid)
     return fail(PA_ERR_UNSUPPORTED, "too many query rows or workgroups");
+  if (plan) {
+    const size_t pb = prefill_plan_bytes(num_seqs, max_query_tokens, q_heads, kv_heads);
+    if (pb == 0)
+      return fail(PA_ERR_UNSUPPORTED, "a prefill plan orders at most %d (sequence, row tile) units",
+                  pa::kMaxPlanUnits);
+    if (plan_bytes < pb || !aligned(plan, 16))
+      return fail(PA_ERR_INVALID_ARG,
+                  "prefill plan of %zu bytes (16-byte aligned) needed for these sizes, got %zu", pb,
+                  plan_bytes);
+  }
   if (num_seqs == 0 || total_query_tokens == 0) return PA_OK;
   if (!query_start || !aligned(query_start, 4))
     return fail(PA_ERR_INVALID_ARG, "query_start must be a 4-byte aligned pointer");
@@ -572,9 +599,82 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   a.scale = scale;
   a.q_dtype = q_dtype;
   a.kv_dtype = kv_dtype;
+  a.plan = static_cast<const int32_t*>(plan);
   hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const float* k_scale, const float* v_scale, const int32_t* block_tables,
+               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+               int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+               int max_context_len, float scale, int q_dtype, int kv_dtype, void* stream) {
+  return run_prefill(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                     query_start, num_seqs, total_query_tokens, max_query_tokens, q_heads,
+                     kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_context_len, scale, q_dtype, kv_dtype, stream, nullptr, 0);
+}
+
+size_t pa_prefill_plan_size(int num_seqs, int max_query_tokens, int q_heads, int kv_heads) {
+  const size_t pb = prefill_plan_bytes(num_seqs, max_query_tokens, q_heads, kv_heads);
+  if (pb == 0) fail(PA_ERR_INVALID_ARG, "invalid sizes or more than %d units", pa::kMaxPlanUnits);
+  return pb;
+}
+
+int pa_prefill_plan(const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                    int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+                    int max_blocks_per_seq, void* plan, size_t plan_bytes, void* stream) {
+  if (num_seqs < 0 || max_query_tokens < 1 || q_heads <= 0 || kv_heads <= 0 ||
+      max_blocks_per_seq <= 0 || total_query_tokens < 0 ||
+      long(total_query_tokens) > long(num_seqs) * max_query_tokens)
+    return fail(PA_ERR_INVALID_ARG,
+                "invalid sizes: num_seqs=%d total_query_tokens=%d max_query_tokens=%d q_heads=%d "
+                "kv_heads=%d max_blocks_per_seq=%d",
+                num_seqs, total_query_tokens, max_query_tokens, q_heads, kv_heads,
+                max_blocks_per_seq);
+  if (q_heads % kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "q_heads (%d) is not a multiple of kv_heads (%d)", q_heads,
+                kv_heads);
+  const size_t pb = prefill_plan_bytes(num_seqs, max_query_tokens, q_heads, kv_heads);
+  if (pb == 0)
+    return fail(PA_ERR_UNSUPPORTED, "a prefill plan orders at most %d (sequence, row tile) units",
+                pa::kMaxPlanUnits);
+  if (!plan || plan_bytes < pb || !aligned(plan, 16))
+    return fail(PA_ERR_INVALID_ARG,
+                "prefill plan of %zu bytes (16-byte aligned) needed for these sizes, got %zu", pb,
+                plan ? plan_bytes : size_t(0));
+  if (num_seqs > 0 && (!context_lens || !query_start))
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(context_lens, 4) || !aligned(query_start, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned length or offset pointer");
+  const int G = q_heads / kv_heads;
+  const int per_wg = pa::prefill_rows_per_workgroup();
+  pa::PrefillPlanArgs a{context_lens, query_start, static_cast<int32_t*>(plan), num_seqs,
+                        int((long(max_query_tokens) * G + per_wg - 1) / per_wg), per_wg, G,
+                        total_query_tokens, max_query_tokens, max_blocks_per_seq};
+  hipError_t e = pa::launch_prefill_plan(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "plan launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_prefill_planned(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                       int total_query_tokens, int max_query_tokens, int q_heads, int kv_heads,
+                       int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                       int max_context_len, float scale, int q_dtype, int kv_dtype,
+                       const void* plan, size_t plan_bytes, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID_ARG, "null prefill plan");
+  return run_prefill(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                     query_start, num_seqs, total_query_tokens, max_query_tokens, q_heads,
+                     kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_context_len, scale, q_dtype, kv_dtype, stream, plan, plan_bytes);
 }
 
 int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -132,6 +132,30 @@ int decode_pass1_resident(int q_dtype, int kv_dtype, int head_dim, int G);
 int rows_pass1_resident(int kv_dtype, int head_dim);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
+
+// Prefill work plans.  kPlanHeader ints (kPrefillPlanMagic, num_seqs, row
+// tiles per sequence, query rows per tile, total_query_tokens,
+// max_query_tokens, max_blocks_per_seq, group size, the rest 0), then one row
+// of kPrefillPlanRow ints per (sequence, row tile) unit, longest first:
+// sequence, tile, first packed query token, query count, context length, the
+// positions the tile's last row sees (-1: no rows), 0, 0.
+constexpr int kPrefillPlanMagic = 0x50414E32;
+constexpr int kPrefillPlanRow = 8;
+constexpr int kPrefillBuckets = 256;
+
+struct PrefillPlanArgs {
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int32_t* plan;
+  int num_seqs;
+  int tiles;
+  int rows_per_tile;
+  int group;
+  int total_query_tokens;
+  int max_query_tokens;
+  int max_blocks_per_seq;
+};
+hipError_t launch_prefill_plan(const PrefillPlanArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 // Chunked prefill (matrix cores): DecodeArgs with query_start set, no pieces.
 hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);

@@ -114,7 +114,96 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
 }
 
+// The prefill work plan: the (sequence, row tile) units of a pa_prefill call
+// sorted by the positions each tile's last row sees (the length of its loop
+// over the cache), longest first, in kPrefillBuckets buckets of equal width.
+// Causal chunks on top of prior contexts of different lengths give tiles
+// that differ many times over in work; started in the natural order, the
+// longest end the launch alone.
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillPlanArgs a) {
+  __shared__ int s_key[kMaxPlanUnits];
+  __shared__ int s_pos[kMaxPlanUnits];
+  __shared__ int s_cnt[kPrefillBuckets];
+  const int N = a.num_seqs;
+  const int U = N * a.tiles;
+  const int max_len = a.max_blocks_per_seq * kBlockSize;
+  const int width = max(1, cdiv(max_len + 1, kPrefillBuckets - 1));
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPrefillBuckets; i += kPlanThreads) s_cnt[i] = 0;
+  __syncthreads();
+  for (int u = tid; u < U; u += kPlanThreads) {
+    const int b = u / a.tiles, t = u - b * a.tiles;
+    const int L = min(a.context_lens[b], max_len);
+    const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
+    const int q0 = min(max(s0, 0), a.total_query_tokens);
+    const int T = min(max(s1 - s0, 0), min(a.max_query_tokens, a.total_query_tokens - q0));
+    const int R = T * a.group, row0 = t * a.rows_per_tile;
+    int key = -1;
+    if (row0 < R) {
+      const int tl = (min(row0 + a.rows_per_tile, R) - 1) / a.group;
+      key = min(max(L - T + tl + 1, 0), max(L, 0));
+    }
+    const int bucket = key < 0 ? 0 : 1 + min(key / width, kPrefillBuckets - 2);
+    s_key[u] = bucket;
+    atomicAdd(&s_cnt[bucket], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int k = kPrefillBuckets - 1; k >= 0; --k) {
+      const int c = s_cnt[k];
+      s_cnt[k] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int u = tid; u < U; u += kPlanThreads) s_pos[u] = atomicAdd(&s_cnt[s_key[u]], 1);
+  __syncthreads();
+  for (int u = tid; u < U; u += kPlanThreads) {
+    const int b = u / a.tiles, t = u - b * a.tiles;
+    const int L = min(a.context_lens[b], max_len);
+    const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
+    const int q0 = min(max(s0, 0), a.total_query_tokens);
+    const int T = min(max(s1 - s0, 0), min(a.max_query_tokens, a.total_query_tokens - q0));
+    const int R = T * a.group, row0 = t * a.rows_per_tile;
+    int key = -1;
+    if (row0 < R) {
+      const int tl = (min(row0 + a.rows_per_tile, R) - 1) / a.group;
+      key = min(max(L - T + tl + 1, 0), max(L, 0));
+    }
+    int32_t* row = a.plan + kPlanHeader + size_t(s_pos[u]) * kPrefillPlanRow;
+    row[0] = b;
+    row[1] = t;
+    row[2] = q0;
+    row[3] = T;
+    row[4] = L;
+    row[5] = key;
+    row[6] = 0;
+    row[7] = 0;
+  }
+  if (tid < kPlanHeader) {
+    int h = 0;
+    switch (tid) {
+      case 0: h = kPrefillPlanMagic; break;
+      case 1: h = N; break;
+      case 2: h = a.tiles; break;
+      case 3: h = a.rows_per_tile; break;
+      case 4: h = a.total_query_tokens; break;
+      case 5: h = a.max_query_tokens; break;
+      case 6: h = a.max_blocks_per_seq; break;
+      case 7: h = a.group; break;
+      default: h = 0;
+    }
+    a.plan[tid] = h;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prefill_plan(const PrefillPlanArgs& a, hipStream_t stream) {
+  prefill_plan_kernel<<<1, kPlanThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
   plan_kernel<<<1, kPlanThreads, 0, stream>>>(a);

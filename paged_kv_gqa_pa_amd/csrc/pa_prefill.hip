@@ -68,20 +68,50 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   constexpr bool kSwizzleV = kInt8;
   using M = MOps<KV>;
 
-  // Tiles of later rows see more positions: they are handed out first.
+  // Unit of this workgroup: rank r = blockIdx / kv_heads (the kv_heads
+  // workgroups of a unit are consecutive, so they spread over the XCDs).
+  // With a prefill work plan whose header matches the call, unit r of the
+  // plan (longest first) and its offsets and lengths, in the round trip the
+  // natural order spends on them; otherwise tiles of later rows (which see
+  // more positions) first.  The order changes no bit of any result.
+  constexpr int WROWS = RT * kRows;              // query rows per wave
   const int pairs = a.num_seqs * a.kv_heads;
   const int tiles = int(gridDim.x) / pairs;
-  const int tile = tiles - 1 - int(blockIdx.x) / pairs;
-  const int pair = int(blockIdx.x) % pairs;
-  const int b = pair / a.kv_heads;
-  const int g = pair - b * a.kv_heads;
   const int Hq = a.q_heads;
   const int G = Hq / a.kv_heads;
-  const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
-  const int q0 = min(max(s0, 0), a.total_query_tokens);
-  const int T = min(max(s1 - s0, 0), min(a.num_query_tokens, a.total_query_tokens - q0));
+  const int g = int(blockIdx.x) % a.kv_heads;
+  const int rank = int(blockIdx.x) / a.kv_heads;
+  const int max_len = a.max_blocks_per_seq * kBlockSize;
+  int b, tile, q0, T, L;
+  bool planned = false;
+  if (a.plan) {
+    const int4 h0 = *reinterpret_cast<const int4*>(a.plan);
+    const int4 h1 = *reinterpret_cast<const int4*>(a.plan + 4);
+    const int32_t* row = a.plan + kPlanHeader + size_t(rank) * kPrefillPlanRow;
+    const int4 r0 = *reinterpret_cast<const int4*>(row);
+    const int r4 = row[4];
+    planned = (h0.x == kPrefillPlanMagic) & (h0.y == a.num_seqs) & (h0.z == tiles) &
+              (h0.w == NW * WROWS) & (h1.x == a.total_query_tokens) &
+              (h1.y == a.num_query_tokens) & (h1.z == a.max_blocks_per_seq) & (h1.w == G);
+    if (planned) {
+      // clamped like the natural order's values: a corrupt row cannot address
+      // outside the buffers
+      b = min(max(r0.x, 0), a.num_seqs - 1);
+      tile = min(max(r0.y, 0), tiles - 1);
+      q0 = min(max(r0.z, 0), a.total_query_tokens);
+      T = min(max(r0.w, 0), min(a.num_query_tokens, a.total_query_tokens - q0));
+      L = min(r4, max_len);
+    }
+  }
+  if (!planned) {
+    tile = tiles - 1 - rank / a.num_seqs;
+    b = rank % a.num_seqs;
+    const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
+    q0 = min(max(s0, 0), a.total_query_tokens);
+    T = min(max(s1 - s0, 0), min(a.num_query_tokens, a.total_query_tokens - q0));
+    L = min(a.context_lens[b], max_len);
+  }
   const int R = T * G;
-  constexpr int WROWS = RT * kRows;              // query rows per wave
   const int row0 = tile * NW * WROWS;
   if (row0 >= R) return;
 
@@ -91,7 +121,6 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   const int grp = lane >> 4;   // 8-dim group of a score product / key quad of S, P, O
   const int wrow0 = row0 + wave * WROWS;
 
-  const int L = min(a.context_lens[b], a.max_blocks_per_seq * kBlockSize);
   // Row tile i of this wave: rows wrow0 + 16i .. +15.  Query rows as the B
   // operand of score product c: lane (row n, group grp) holds
   // q[n][32c + 8grp .. +7] (fp16 for an int8 cache).

@@ -186,3 +186,18 @@ def test_plan_size_and_invalid_arguments():
     st = lib.pa_decode_planned(*ptrs, 4, 2, 1, 64, 16, 16, 4, 64, ctypes.c_float(0.125),
                                pa.PA_F32, pa.PA_F32, 16, d, 1 << 20, d, need - 16, None)
     assert st == pa.PA_ERR_INVALID_ARG and b"work plan" in lib.pa_last_error()
+
+
+def test_prefill_plan_size_and_invalid_arguments():
+    lib = pa.lib()
+    # 16 sequences x 512 tokens, 16/8 heads: 1024 rows per sequence in tiles of the workgroup's rows
+    n = lib.pa_prefill_plan_size(16, 512, 16, 8)
+    assert n > 0 and (n // 4 - 16) % 8 == 0
+    units = (n // 4 - 16) // 8
+    assert units % 16 == 0 and 1024 % (units // 16) == 0
+    assert lib.pa_prefill_plan_size(16, 512, 15, 8) == 0        # q_heads not a multiple
+    assert lib.pa_prefill_plan_size(100000, 512, 16, 8) == 0    # too many units
+    d = ctypes.c_void_p(FAKE)
+    assert lib.pa_prefill_plan(d, d, 16, 8192, 512, 16, 8, 64, d, n - 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_prefill_plan(d, d, 16, 9000, 512, 16, 8, 64, d, n, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_prefill_plan(None, d, 16, 8192, 512, 16, 8, 64, d, n, None) == pa.PA_ERR_INVALID_ARG

@@ -121,3 +121,100 @@ def test_prefill_untouched_rows_and_invalid_arguments():
         pa.prefill(q32.clone(), q32, dc.k_cache.float(), dc.v_cache.float(), dc.block_tables,
                    dev(lens), dev(qs), case.scale, T)
     assert ei.value.status == pa.PA_ERR_UNSUPPORTED
+
+
+def _prefill_plan(case, dc, qs, lens, T):
+    sp = case.spec
+    return pa.make_prefill_plan(dev(lens), dev(qs), int(qs[-1]), T, sp.q_heads, sp.kv_heads,
+                                case.block_tables.shape[1])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("G", [1, 2, 6])
+def test_planned_prefill_equals_unplanned_bitwise(G, kv):
+    """The prefill plan only reorders the start of row tiles: same bits, and the oracle."""
+    _say("planned prefill", kv, "G", G)
+    rng = np.random.default_rng(4000 + G)
+    T = 90
+    case = _random_verify_case(rng, LENS, Hkv=2, G=G, D=128, T=T, poison=True, kv=kv)
+    dc = DevCase(case)
+    counts = [0, 3, 15, 16, 17, 64, 65, 90, 33, 90]
+    qp, qs, lens = _pack(case, counts, LENS)
+    base = _prefill(case, dc, qp, qs, lens, T)
+    plan = _prefill_plan(case, dc, qs, lens, T)
+    got = torch.empty_like(base)
+    pa.prefill(got, dev(qp), dc.k_cache, dc.v_cache, dc.block_tables, dev(lens), dev(qs),
+               case.scale, T, dc.k_scale, dc.v_scale, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), base.view(torch.int16))
+    assert max_abs_err(got, _want(case, qp, qs, lens)) < TOL[kv]
+
+
+def test_prefill_plan_contents_exact():
+    """One row per (sequence, row tile) unit with its offsets and lengths, ordered by the
+    positions the tile's last row sees (256 buckets), longest first."""
+    _say("prefill plan contents")
+    rng = np.random.default_rng(77)
+    T, G = 300, 2
+    prior = np.array([0, 700, 5, 1500, 64, 333])
+    case = _random_verify_case(rng, prior + T, Hkv=2, G=G, D=64, T=T)
+    dc = DevCase(case)
+    counts = [300, 1, 0, 299, 128, 77]
+    qp, qs, lens = _packed(case, counts)
+    plan = _prefill_plan(case, dc, qs, lens, T)
+    torch.cuda.synchronize()
+    p = plan.cpu().numpy().view(np.int32)
+    N = len(counts)
+    maxb = case.block_tables.shape[1]
+    rows_per_tile = int(p[3])
+    tiles = -(-T * G // rows_per_tile)
+    assert list(p[:8]) == [0x50414E32, N, tiles, rows_per_tile, int(qs[-1]), T, maxb, G]
+    rows = p[16:16 + N * tiles * 8].reshape(N * tiles, 8)
+    seen = set()
+    width = max(1, -(-(maxb * 16 + 1) // 255))
+    buckets = []
+    for r in rows:
+        b, t, q0, Tb, L, key = (int(x) for x in r[:6])
+        assert (b, t) not in seen
+        seen.add((b, t))
+        assert q0 == int(qs[b]) and Tb == counts[b] and L == int(lens[b])
+        R = Tb * G
+        if t * rows_per_tile >= R:
+            want = -1
+        else:
+            tl = (min(t * rows_per_tile + rows_per_tile, R) - 1) // G
+            want = min(max(L - Tb + tl + 1, 0), L)
+        assert key == want, (b, t)
+        buckets.append(0 if key < 0 else 1 + min(key // width, 254))
+    assert len(seen) == N * tiles
+    assert (np.diff(buckets) <= 0).all(), "tiles must be ordered longest first"
+
+
+def test_prefill_plan_for_other_sizes_is_ignored():
+    _say("prefill plan for other sizes")
+    rng = np.random.default_rng(78)
+    T = 40
+    case = _random_verify_case(rng, [50, 130, 200], Hkv=2, G=3, D=128, T=T)
+    dc = DevCase(case)
+    qp, qs, lens = _packed(case, [40, 7, 33])
+    base = _prefill(case, dc, qp, qs, lens, T)
+    big = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    sp = case.spec
+    # a plan for a larger query count (another tile count)
+    pa.make_prefill_plan(dev(lens), dev(qs), int(qs[-1]), 300, sp.q_heads, sp.kv_heads,
+                         case.block_tables.shape[1], plan=big)
+    got = torch.empty_like(base)
+    pa.prefill(got, dev(qp), dc.k_cache, dc.v_cache, dc.block_tables, dev(lens), dev(qs),
+               case.scale, T, plan=big)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), base.view(torch.int16))
+    big.fill_(0x33)
+    pa.prefill(got, dev(qp), dc.k_cache, dc.v_cache, dc.block_tables, dev(lens), dev(qs),
+               case.scale, T, plan=big)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), base.view(torch.int16))
+    small = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pa.PAError) as ei:
+        pa.prefill(got, dev(qp), dc.k_cache, dc.v_cache, dc.block_tables, dev(lens), dev(qs),
+                   case.scale, T, plan=small)
+    assert ei.value.status == pa.PA_ERR_INVALID_ARG
