@@ -39,7 +39,7 @@
 namespace pa {
 namespace {
 
-template <typename KV, int D, int NW>
+template <typename KV, int D, int NW, int NS>
 __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   constexpr bool kInt8 = __is_same(KV, i8_t);
   constexpr int ROWB = D * int(sizeof(KV));  // bytes per key row
@@ -130,6 +130,8 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   // slot's direct-to-LDS loads does not also wait for the other slot's.
   __shared__ __attribute__((aligned(16))) char s_ring0[NW * WBYTES];
   __shared__ __attribute__((aligned(16))) char s_ring1[NW * WBYTES];
+  __shared__ __attribute__((aligned(16))) char s_ring2[NS > 2 ? NW * WBYTES : 16];
+  __shared__ __attribute__((aligned(16))) char s_ring3[NS > 3 ? NW * WBYTES : 16];
   // Each wave's row maxima and sums: in its slot-1 region behind its O rows
   // when there is room (keeps a bf16, D = 128 workgroup within 64 KiB).
   constexpr bool kMLInRing = WBYTES - OHALF >= 2 * kRows * 4;
@@ -139,8 +141,13 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   };
   char* const s_w0 = s_ring0 + wave * WBYTES;
   char* const s_w1 = s_ring1 + wave * WBYTES;
-  auto kbuf = [&](int slot) { return slot ? s_w1 : s_w0; };
-  auto vbuf = [&](int slot) { return (slot ? s_w1 : s_w0) + TILE_BYTES; };
+  // slot is a compile-time constant at every call (the tile loop is unrolled
+  // over the ring)
+  auto kbuf = [&](int slot) {
+    return slot == 0 ? s_w0 : slot == 1 ? s_w1 : slot == 2 ? s_ring2 + wave * WBYTES
+                                                            : s_ring3 + wave * WBYTES;
+  };
+  auto vbuf = [&](int slot) { return kbuf(slot) + TILE_BYTES; };
   // Byte offset inside a staged tile of chunk k of key row r.
   auto sw = [](int r, int k) { return r * ROWB + 16 * (k ^ ((r / RPB) & (CPR - 1))); };
 
@@ -289,22 +296,28 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
   };
 
-  using Pend = std::integral_constant<int, kFetchLoads>;
-  using Pend0 = std::integral_constant<int, 0>;
+  // Each wave takes every NW-th tile of the piece through a ring of NS LDS
+  // slots: tile j is used from slot j % NS while tiles j+1 .. j+NS-1 load.
+  // Every step issues exactly one fetch (past the wave's last tile it reads
+  // nothing), so the loads issued after a tile's own are always NS - 1
+  // fetches' worth and one wait count serves every step.
+  using Pend = std::integral_constant<int, (NS - 1) * kFetchLoads>;
   const int first = blk_begin + wave;
   const int n_my = first < blk_end ? cdiv(blk_end - first, NW) : 0;
   if (n_my > 0) {
     const int last = n_my - 1;
-    float ks0, vs0, ks1, vs1;
-    fetch(first, true, 0, ks0, vs0);
-    int j = 0;
-    for (; j + 1 <= last; j += 2) {
-      fetch(first + (j + 1) * NW, true, 1, ks1, vs1);
-      process(Pend{}, first + j * NW, 0, ks0, vs0);
-      fetch(first + min(j + 2, last) * NW, j + 2 <= last, 0, ks0, vs0);
-      process(Pend{}, first + (j + 1) * NW, 1, ks1, vs1);
+    auto tile = [&](int j) { return first + min(j, last) * NW; };
+    float ks[NS], vs[NS];
+#pragma unroll
+    for (int v = 0; v < NS - 1; ++v) fetch(tile(v), v <= last, v, ks[v], vs[v]);
+    for (int j = 0; j <= last; j += NS) {
+#pragma unroll
+      for (int v = 0; v < NS; ++v) {
+        const int nf = (v + NS - 1) % NS;   // slot of tile j + v + NS - 1 (constant once unrolled)
+        fetch(tile(j + v + NS - 1), j + v + NS - 1 <= last, nf, ks[nf], vs[nf]);
+        if (j + v <= last) process(Pend{}, first + (j + v) * NW, v, ks[v], vs[v]);
+      }
     }
-    if (j == last) process(Pend0{}, first + j * NW, 0, ks0, vs0);
   }
   // The last prefetch (reading nothing) may still be writing its LDS slot:
   // wait for it before the slots are reused below.
@@ -354,6 +367,16 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   }
 }
 
+// LDS ring slots per wave: two (with eight waves a bf16 ring fills 128 KiB).
+// int8 tiles are half the size, but four slots were measured slower on the
+// long-context workload (30.7 us against 29.4 us per call): as in the
+// vector-ALU decode, more tiles in flight per wave only add contention.
+#ifndef PA_ROWS_SLOTS_INT8
+#define PA_ROWS_SLOTS_INT8 2
+#endif
+template <typename KV> struct RowsSlots : std::integral_constant<int, 2> {};
+template <> struct RowsSlots<i8_t> : std::integral_constant<int, PA_ROWS_SLOTS_INT8> {};
+
 template <typename KV>
 hipError_t launch_rows_t(const DecodeArgs& a, hipStream_t stream) {
   // Eight waves per (piece, sequence, KV head): a long piece's tiles spread
@@ -367,9 +390,9 @@ hipError_t launch_rows_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = PA_ROWS_WAVES;
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
   if (a.head_dim == 128)
-    rows_pass1<KV, 128, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    rows_pass1<KV, 128, NW, RowsSlots<KV>::value><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   else
-    rows_pass1<KV, 64, NW><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    rows_pass1<KV, 64, NW, RowsSlots<KV>::value><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -385,11 +408,11 @@ int rows_pass1_resident(int kv_dtype, int head_dim) {
   constexpr int NW = PA_ROWS_WAVES;
   hipError_t e;
   if (kv_dtype == kI8)
-    e = head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<i8_t, 64, NW>, NW * kWave, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<i8_t, 128, NW>, NW * kWave, 0);
+    e = head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<i8_t, 64, NW, RowsSlots<i8_t>::value>, NW * kWave, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<i8_t, 128, NW, RowsSlots<i8_t>::value>, NW * kWave, 0);
   else
-    e = head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<bf16_t, 64, NW>, NW * kWave, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<bf16_t, 128, NW>, NW * kWave, 0);
+    e = head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<bf16_t, 64, NW, RowsSlots<bf16_t>::value>, NW * kWave, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<bf16_t, 128, NW, RowsSlots<bf16_t>::value>, NW * kWave, 0);
   return e == hipSuccess && n > 0 ? n : 1;
 }
 
