@@ -170,6 +170,8 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   using GE = Geo<KV, D, G>;
   constexpr int EPL = GE::EPL, PPL = GE::PPL, E = GE::E, LPK = GE::LPK, KPL = GE::KPL;
   constexpr int LPB = GE::LPB, KR = GE::KR;
+  // bf16 V: products over key pairs (below); needs an even count of key rows per lane.
+  constexpr bool kPairPV = __is_same(KV, bf16_t) && KR % 2 == 0;
   using P = u32x4;
 
   // 1-D grid, piece-major: ids 0 .. N*Hkv-1 are piece 0 of every (sequence,
@@ -333,6 +335,48 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
       }
+    }
+    if constexpr (kPairPV) {
+      // bf16 cache: the lane's key rows in pairs, each dimension's two values
+      // in one word, so that one packed product adds both rows' terms.  The
+      // weights are rounded to bf16 for this product (as on the matrix
+      // cores); the running sum keeps them in fp32.
+      uint32_t vp[KR / 2][E];
+#pragma unroll
+      for (int k2 = 0; k2 < KR / 2; ++k2)
+#pragma unroll
+        for (int p = 0; p < PPL; ++p)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = vt[(2 * k2) * PPL + p][w], hi = vt[(2 * k2 + 1) * PPL + p][w];
+            vp[k2][p * EPL + 2 * w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            vp[k2][p * EPL + 2 * w + 1] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+          }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mref = m[h] == kNegInf ? 0.0f : m[h];
+        float pw[KR];
+        float psum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KR; ++k) {
+          pw[k] = fast_exp2(s[h][k] - mref);
+          psum += pw[k];
+        }
+        l[h] += psum;
+        bf16x2 pp[KR / 2];
+#pragma unroll
+        for (int k2 = 0; k2 < KR / 2; ++k2) pp[k2] = pack_bf16x2(pw[2 * k2], pw[2 * k2 + 1]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float x = acc[h][e];
+#pragma unroll
+          for (int k2 = 0; k2 < KR / 2; ++k2)
+            x = __builtin_amdgcn_fdot2_f32_bf16(pp[k2], __builtin_bit_cast(bf16x2, vp[k2][e]), x,
+                                                false);
+          acc[h][e] = x;
+        }
+      }
+      return;
     }
     float vf[KR][E];
 #pragma unroll

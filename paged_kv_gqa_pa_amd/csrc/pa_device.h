@@ -34,6 +34,11 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // v_cvt_pk_bf16_f32
 }
+// Two fp32 values as bf16 (round to nearest even) in one packed conversion.
+__device__ __forceinline__ bf16x2 pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+}
 
 // Exchange across 16-lane rows without LDS: permlane16_swap of a value with
 // itself leaves row r's partner row (r ^ 1) in one of the two results, so
