@@ -9,7 +9,7 @@
 // g * G + r % G; wave w owns RT consecutive 16-row tiles (rows 16 RT w ..
 // 16 RT (w + 1) - 1) over the whole visible context, so no partial results
 // leave the workgroup.  The cache is
-// walked in stages of KB blocks (64 positions): the workgroup stages a
+// walked in stages of KB blocks (32 positions): the workgroup stages a
 // stage's K and V tiles in LDS with direct-to-LDS buffer loads (double
 // buffered, the next stage in flight while this one is used), and every wave
 // reads the shared tiles for its own rows.  A block's buffer resource covers
@@ -27,11 +27,31 @@
 #include "pa_kernels.h"
 #include "pa_mfma.h"
 
+// Shape of a workgroup, measured on 16 sequences x 512-token chunks after
+// U{0..1536} prior positions, 16/8 heads, D = 128, bf16, with a work plan:
+// four waves of two 16-row tiles each (128 rows; every K and V operand read
+// from LDS serves two products), stages of two blocks, two stages in the ring,
+// at most 168 VGPRs (three workgroups per CU): 92-94 us per call, against
+// 105 us for eight waves of one row tile with four-block stages, 106-125 us
+// for four-block stages with two row tiles (two workgroups per CU), 111 us
+// with three stages in the ring and 146 us for two-wave workgroups.
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+#ifndef PA_PREFILL_ROW_TILES
+#define PA_PREFILL_ROW_TILES 2
+#endif
 #ifndef PA_PREFILL_STAGE_BLOCKS
-#define PA_PREFILL_STAGE_BLOCKS 4
+#define PA_PREFILL_STAGE_BLOCKS 2
 #endif
 #ifndef PA_PREFILL_STAGES
 #define PA_PREFILL_STAGES 2
+#endif
+// Register budget: two workgroups per CU asked of the compiler, which then
+// fits the bf16 kernel in 164 VGPRs (three per CU); with no bound it spends
+// 88 accumulation registers and gets two.
+#ifndef PA_PREFILL_MIN_WGS
+#define PA_PREFILL_MIN_WGS 2
 #endif
 
 namespace pa {
@@ -47,7 +67,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <typename KV, int D, int NW, int RT>
-__global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
+__global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WGS) void prefill_rows(DecodeArgs a) {
   constexpr bool kInt8 = __is_same(KV, i8_t);
   constexpr int ROWB = D * int(sizeof(KV));      // bytes per key row
   constexpr int NL = ROWB / 64;                  // 1 KiB loads per 16-row tile
@@ -124,6 +144,9 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   // Row tile i of this wave: rows wrow0 + 16i .. +15.  Query rows as the B
   // operand of score product c: lane (row n, group grp) holds
   // q[n][32c + 8grp .. +7] (fp16 for an int8 cache).
+  // bf16 cache: a negative scale is carried by q's sign (exact), so that the
+  // softmax below works with a positive factor.
+  const uint32_t qflip = a.scale < 0.0f ? 0x80008000u : 0u;
   u32x4 qb[RT][NQ];
   float qsum[RT];
   int last_vis[RT];   // last position row n of tile i sees
@@ -148,7 +171,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
           qpart += float(hp[0]) + float(hp[1]);
         }
       } else {
-        qb[i][c] = w;
+        qb[i][c] = w ^ qflip;
       }
     }
     qsum[i] = kInt8 ? add_xor32(add_xor16(qpart)) : 0.0f;
@@ -172,6 +195,10 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
   const float sc = a.scale * kLog2e;
+  // The bf16 path's factor: |scale| log2(e), kept above zero so that a masked
+  // (-inf) score still gives -inf (a zero scale then yields weights that round
+  // to exactly 1, as it should).
+  const float sc_pos = fmaxf(fabsf(sc), __FLT_MIN__);
 
   // A ring of NBUF stage buffers, each its own LDS object, so that waiting
   // for one stage's direct-to-LDS loads does not also wait for the others'.
@@ -225,7 +252,8 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       const int kb = (li / NL) % KB;
       const int c = li % NL;
       const int blk = st * KB + kb;
-      const int valid = min(max(kend - blk * kBlockSize, 0), kBlockSize);
+      // (uniform; kept scalar so the buffer resource needs no per-lane loop)
+      const int valid = readfirstlane(min(max(kend - blk * kBlockSize, 0), kBlockSize));
       const size_t tile_off = (head_blocks + size_t(valid > 0 ? phys[kb] : 0)) * TILE_BYTES;
       const __amdgpu_buffer_rsrc_t r = make_rsrc((isv ? vbase : kbase) + tile_off, valid * ROWB);
       const int off = isv ? src_off_v[c] : src_off[c];
@@ -291,6 +319,54 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
     const float ssc[2] = {sc * ks0, sc * ks1};
     const float vsc[2] = {vs0, vs1};
     u32x4 pa[RT];
+    if constexpr (!kInt8) {
+      // bf16 cache: one factor for both blocks, so the row maximum is taken
+      // over the raw scores and each weight is exp2 of one fused multiply-add;
+      // the running sum adds the weights as rounded for the P.V product.
+      const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        float r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = s[i][e >> 2][e & 3];
+        if (edge) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int pos = (blk + (e >> 2)) * kBlockSize + 4 * grp + (e & 3);
+            r[e] = pos <= last_vis[i] ? r[e] : kNegInf;
+          }
+        }
+        float rmax = fmaxf(fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])),
+                           fmaxf(fmaxf(r[4], r[5]), fmaxf(r[6], r[7])));
+        rmax = max_xor32(max_xor16(rmax));
+        const float tmax = rmax * sc_pos;   // -inf stays -inf: sc_pos > 0
+        if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
+          const float mnew = fmaxf(m[i], tmax);
+          const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
+          m[i] = mnew;
+          lsum[i] *= alpha;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float ar = __shfl(alpha, 4 * grp + j);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) o[i][t][j] *= ar;
+          }
+        }
+        const float nref = m[i] == kNegInf ? 0.0f : -m[i];
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(r[e], sc_pos, nref));
+        pa[i] = u32x4{M::pack_round(p[0], p[1]), M::pack_round(p[2], p[3]),
+                      M::pack_round(p[4], p[5]), M::pack_round(p[6], p[7])};
+        float ls = lsum[i];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t pw = pa[i][w];
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), ones, ls, false);
+        }
+        lsum[i] = ls;
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
       float x[8];
@@ -328,6 +404,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
       lsum[i] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       pa[i] = u32x4{M::pack_round(p[0] * vsc[0], p[1] * vsc[0]), M::pack_round(p[2] * vsc[0], p[3] * vsc[0]),
                     M::pack_round(p[4] * vsc[1], p[5] * vsc[1]), M::pack_round(p[6] * vsc[1], p[7] * vsc[1])};
+    }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -422,20 +499,6 @@ __global__ __launch_bounds__(NW * kWave) void prefill_rows(DecodeArgs a) {
     }
   }
 }
-
-// Eight waves (128 query rows) share each staged K/V stage: measured on 16
-// sequences x 512-token chunks, 16/8 heads, D = 128 against four waves,
-// 296 us instead of 523 us per call (a stage's loads are then covered by
-// twice the products); larger stages or 16 waves were slower.
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 8
-#endif
-// 16-row tiles per wave: each K / V operand read from LDS serves this many
-// products.  Two tiles (measured 265 us against 238 us for one on the
-// 16 x 512-token workload) need 152 VGPRs, which halves the workgroups per CU.
-#ifndef PA_PREFILL_ROW_TILES
-#define PA_PREFILL_ROW_TILES 1
-#endif
 
 template <typename KV>
 hipError_t launch_prefill_t(const DecodeArgs& a, hipStream_t stream) {
