@@ -3,6 +3,8 @@
 The oracle is the variable-length verify definition (sequence b's T_b new tokens
 are its last positions; token t sees 0 .. L_b - T_b + t) at prefill sizes.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -60,6 +62,24 @@ def test_prefill_edges(G, D, kv):
     dc = DevCase(case)
     counts = [0, 3, 15, 16, 17, 64, 65, 90, 33, 90]    # sequence 1: 3 tokens, 1 position
     qp, qs, lens = _pack(case, counts, LENS)
+    err = max_abs_err(_prefill(case, dc, qp, qs, lens, T), _want(case, qp, qs, lens))
+    assert err < TOL[kv], err
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("scale", [-0.3, -1.0 / np.sqrt(128), 0.0, 1.5])
+def test_prefill_scales(scale, kv):
+    """Negative, zero and large softmax scales: the bf16 path carries a negative scale
+    in q's sign and takes the row maximum over the raw scores; a zero scale gives the
+    mean of the visible V rows; a large one makes the running maximum jump (rescales)."""
+    _say("prefill scale", scale, kv)
+    rng = np.random.default_rng(4100)
+    T = 70
+    case = dataclasses.replace(
+        _random_verify_case(rng, [90, 300, 80, 700], Hkv=2, G=2, D=128, T=T, poison=True, kv=kv),
+        scale=float(scale))
+    dc = DevCase(case)
+    qp, qs, lens = _packed(case, [70, 5, 17, 33])
     err = max_abs_err(_prefill(case, dc, qp, qs, lens, T), _want(case, qp, qs, lens))
     assert err < TOL[kv], err
 
