@@ -47,11 +47,12 @@
 #ifndef PA_PREFILL_STAGES
 #define PA_PREFILL_STAGES 2
 #endif
-// Register budget: two workgroups per CU asked of the compiler, which then
-// fits the bf16 kernel in 164 VGPRs (three per CU); with no bound it spends
-// 88 accumulation registers and gets two.
-#ifndef PA_PREFILL_MIN_WGS
-#define PA_PREFILL_MIN_WGS 2
+// Register budget: at least two waves per SIMD asked of the compiler (the
+// second launch bound is waves per SIMD), which then fits the bf16 kernel in
+// 164 VGPRs, i.e. three four-wave workgroups per CU; with no bound it spends
+// 88 accumulation registers and gets two.  Asking for three spills.
+#ifndef PA_PREFILL_MIN_WAVES_PER_SIMD
+#define PA_PREFILL_MIN_WAVES_PER_SIMD 2
 #endif
 
 namespace pa {
@@ -67,7 +68,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <typename KV, int D, int NW, int RT>
-__global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WGS) void prefill_rows(DecodeArgs a) {
+__global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void prefill_rows(DecodeArgs a) {
   constexpr bool kInt8 = __is_same(KV, i8_t);
   constexpr int ROWB = D * int(sizeof(KV));      // bytes per key row
   constexpr int NL = ROWB / 64;                  // 1 KiB loads per 16-row tile
