@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library default)")
     p.add_argument("--eager", action="store_true", help="launch from Python instead of a graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-buckets", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--decode-reps", type=int, default=20,
@@ -80,6 +81,37 @@ def attention_bytes(lens, T, q_heads, kv_heads, head_dim, kv_elem, q_elem=2):
     qo = len(lens) * T * q_heads * head_dim * q_elem * 2
     scales = blocks * kv_heads * 8 if kv_elem == 1 else 0
     return kv + qo + blocks * 4 + len(lens) * 4 + scales
+
+
+def bucket_timing(torch, pa, kc, vc, qs, nks, nvs, bt, cl, sm, table, scale, reps, sizes=(1, 8, 64)):
+    """The batch-64 step (pa_plan + 28 x (write + decode)) captured per batch-size bucket
+    by StepGraphs, for batches of the first n sequences; µs per step from graph replays
+    (inputs copied in once; each replay rewrites the same new-token slots)."""
+    from paged_kv_gqa_pa_amd.graphs import StepGraphs
+    NB = kc[0].shape[1]
+    used = np.zeros(NB, bool)
+    used[table[table >= 0]] = True
+    spare = int(np.flatnonzero(~used)[-1])
+    sg = StepGraphs(kc, vc, qs[0].shape[1], table.shape[1], spare, scale, buckets=sizes)
+    out = {}
+    for n in sizes:
+        sg.step([q[:n] for q in qs], [k[:n] for k in nks], [v[:n] for v in nvs], bt[:n], cl[:n],
+                sm[:n])
+        for _ in range(3):
+            sg.replay(n)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            sg.replay(n)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[str(n)] = {"us_per_step": round(us, 1), "tokens_per_s": round(n / (us * 1e-6), 1)}
+        print(f"[bench] step graph, batch {n}: {us:.1f} us/step, {n / (us * 1e-6):.0f} tokens/s",
+              flush=True)
+    del sg
+    return out
 
 
 def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
@@ -625,6 +657,13 @@ def main():
     print(f"[bench] streaming read {stream_gbps:.0f} GB/s; decode-pattern tile read "
           f"{tile[4]['gbps']:.0f} GB/s (4 waves), {tile[8]['gbps']:.0f} GB/s (8 waves)", flush=True)
 
+    # Captured steps per batch-size bucket (paged_kv_gqa_pa_amd.graphs): the first n
+    # sequences of the workload as a batch of n, each on its own bucket.
+    buckets = None
+    if not args.no_buckets:
+        buckets = bucket_timing(torch, pa, kc, vc, qs, nks, nvs, bt, cl, sm, table, scale,
+                                args.decode_reps)
+
     traffic = None
     if os.path.exists(args.traffic_file):
         try:
@@ -679,6 +718,8 @@ def main():
                                "tile read: the decode's K/V reads (exact rows, same grid order and "
                                "pieces) with no arithmetic, over the same 28 layers"},
     }
+    if buckets is not None:
+        res["step_graph_buckets"] = buckets
     if not args.no_other_workloads:
         res["other_workloads"] = other_workloads(torch, pa, wl, dev, use_plan=not args.no_plan)
     if cpu is not None:
