@@ -228,6 +228,12 @@ def pin_closed_forms(oracle):
     w0 = 1.0 / (1.0 + math.exp(s1 - s0))
     want = w0 * vc[0, 4, 0].astype(np.float64) + (1 - w0) * vc[0, 4, 1].astype(np.float64)
     assert np.abs(o[0, 0] - want).max() < 1e-12, "L=2 logistic weights"
+    # A negative scale is a scale like any other: two positions again, logistic weights
+    # of the negated scores (a softmax over -s favours the smaller score).
+    o = oracle.decode(q, kc, vc, table, np.array([2], np.int32), -0.7, "f32", "f32")
+    w0n = 1.0 / (1.0 + math.exp(s0 - s1))
+    want = w0n * vc[0, 4, 0].astype(np.float64) + (1 - w0n) * vc[0, 4, 1].astype(np.float64)
+    assert np.abs(o[0, 0] - want).max() < 1e-12, "negative scale, L=2 logistic weights"
     # Empty context: zero row, no NaN.
     o = oracle.decode(q, kc, vc, table, np.array([0], np.int32), 0.7, "f32", "f32")
     assert np.array_equal(o, np.zeros_like(o)), "L=0 -> zeros"

@@ -29,6 +29,8 @@ MUTATIONS = {
                           "K = gather_context(k_cache, block_tables[b], L, (g + 1) % Hkv, kv_tag, k_scale)\n            V = gather_context(v_cache, block_tables[b], L, (g + 1) % Hkv, kv_tag, v_scale)\n            out[b, g * G"),
     # dropped softmax scale
     "dropped_scale": ("s = (q_rows @ keys.T) * float(scale)", "s = (q_rows @ keys.T)"),
+    # the scale's sign dropped
+    "scale_magnitude_only": ("s = (q_rows @ keys.T) * float(scale)", "s = (q_rows @ keys.T) * abs(float(scale))"),
     # transposed operand: scores against V instead of K
     "scores_against_v": ("s = (q_rows @ keys.T) * float(scale)", "s = (q_rows @ values.T) * float(scale)"),
     # wrong normaliser
