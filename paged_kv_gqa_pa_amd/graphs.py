@@ -170,6 +170,17 @@ class StepGraphs:
             raise ValueError("block_tables / slot_mapping do not match context_lens")
         if block_tables.shape[1] > self.max_blocks:
             raise ValueError("block_tables wider than max_blocks_per_seq")
+        qshape = (n, self.q_heads, self.head_dim) if T == 1 else (n, T, self.q_heads, self.head_dim)
+        kvshape = (n * T, self.kv_heads, self.head_dim)
+        for l in range(self.layers):
+            if tuple(q[l].shape) != qshape or q[l].dtype != self.dtype:
+                raise ValueError(f"layer {l}: q must be {self.dtype} {qshape}")
+            if (tuple(k_new[l].shape) != kvshape or tuple(v_new[l].shape) != kvshape or
+                    k_new[l].dtype != self.dtype or v_new[l].dtype != self.dtype):
+                raise ValueError(f"layer {l}: k_new / v_new must be {self.dtype} {kvshape}")
+        if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or
+                slot_mapping.dtype != torch.int64):
+            raise ValueError("block_tables / context_lens int32, slot_mapping int64")
         B = self.bucket_for(n)
         b = self._bufs[B]
         w = block_tables.shape[1]

@@ -118,3 +118,12 @@ def test_bucket_limits():
         StepGraphs(kc[:1], vc[:1], HQ, MAXB, NB, 0.1)            # spare block outside the cache
     with pytest.raises(ValueError):
         StepGraphs(kc[:1], vc[:1], HQ, MAXB, NB - 1, 0.1, num_query_tokens=2, fused=True)
+    # inputs that would broadcast into the static buffers are refused
+    n = 3
+    q = [torch.zeros((1, HQ, D), device="cuda").bfloat16()]
+    kv = [torch.zeros((n, HKV, D), device="cuda").bfloat16()]
+    bt = torch.zeros((n, 4), dtype=torch.int32, device="cuda")
+    cl = torch.ones(n, dtype=torch.int32, device="cuda")
+    sm = torch.zeros(n, dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        graphs.step(q, kv, kv, bt, cl, sm)
