@@ -38,18 +38,6 @@
 #endif
 
 namespace pa {
-#ifdef PA_TIMING
-__device__ unsigned long long g_times[8192 * 6];
-#define PA_STAMP(k) do { if (threadIdx.x == 0 && blockIdx.x < 8192) { g_times[blockIdx.x * 6 + (k)] = __builtin_amdgcn_s_memrealtime(); if ((k) == 0) g_times[blockIdx.x * 6 + 5] = (unsigned long long)__builtin_amdgcn_s_getreg(4 | (31 << 11)) | ((unsigned long long)__builtin_amdgcn_s_getreg(20 | (31 << 11)) << 32); } } while (0)
-#else
-#define PA_STAMP(k) do { } while (0)
-#endif
-#ifdef PA_TIMING
-__device__ unsigned long long g_wtimes[8192 * 8];
-#define PA_WSTAMP(w) do { if ((threadIdx.x & 63) == 0 && blockIdx.x < 8192) g_wtimes[blockIdx.x * 8 + (w)] = __builtin_amdgcn_s_memrealtime(); } while (0)
-#else
-#define PA_WSTAMP(w) do { } while (0)
-#endif
 namespace {
 
 // Lane layout of a 16-token tile.  A lane's load unit is a 16-byte piece.  A
@@ -178,7 +166,6 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // KV head), then piece 1, ...  Consecutive ids go to different XCDs, so the
   // always-present first pieces spread evenly over the chip, and all pieces of
   // one (sequence, head) land on the same XCD whenever N*Hkv is a multiple of 8.
-  PA_STAMP(0);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPK;   // key row inside a load
@@ -217,7 +204,6 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   const int L = it.L;
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
   if (piece < 0 || piece >= n_pieces) return;
-  PA_STAMP(1);
   if constexpr (APPEND) {
     // The last piece writes the new row into the cache (one key row: the
     // first LPK lanes of wave 0, PPL pieces each).  Only this workgroup uses
@@ -455,8 +441,6 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     }
   }
 
-  PA_WSTAMP(wave);
-  PA_STAMP(2);
   // Merge the key rows of this wave (lanes c, c + LPK, c + 2 LPK, ...): all
   // rows are brought to the wave's running max, then the accumulators are
   // reduce-scattered over lane ^ 32 and lane ^ 16 (each swap step halves the
@@ -515,9 +499,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       }
     }
   }
-  PA_WSTAMP(4 + wave);
   __syncthreads();
-  PA_STAMP(3);
 
   const int Hq = a.q_heads;
   for (int t = threadIdx.x; t < G * D; t += NW * kWave) {
@@ -545,7 +527,6 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       if (d == 0) a.part_lse[prow] = lsum > 0.0f ? M + __log2f(lsum) : kNegInf;
     }
   }
-  PA_STAMP(4);
 }
 
 // ---------------------------------------------------------------------------
@@ -679,14 +660,6 @@ hipError_t dispatch_dim(const DecodeArgs& a, int G, bool ap, hipStream_t stream)
 
 }  // namespace
 
-#ifdef PA_TIMING
-extern "C" int pa_debug_times(unsigned long long* host, int n) {
-  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_times), sizeof(unsigned long long) * n) == hipSuccess ? 0 : -1;
-}
-extern "C" int pa_debug_wtimes(unsigned long long* host, int n) {
-  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_wtimes), sizeof(unsigned long long) * n) == hipSuccess ? 0 : -1;
-}
-#endif
 
 bool decode_group_supported(int G) { return (G >= 1 && G <= 8) || G == 16; }
 
