@@ -192,6 +192,10 @@ size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv
  *               stream.
  * Supported: head_dim 64 or 128; block_size 16; q_heads / kv_heads in 1..8
  * or 16; the dtype triples listed at the top.
+ * Precision: scores, softmax and the weighted sum accumulate in fp32.  Over a
+ * bf16 cache the softmax weights are rounded to bf16 for the weighted sum of
+ * V (the sum of the weights stays fp32); over an fp32 cache they stay fp32;
+ * over an int8 cache they are rounded to fp16 (see pa_verify).
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
