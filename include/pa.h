@@ -390,6 +390,11 @@ int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* 
  * Supported: PA_BF16 q with a PA_BF16 or PA_INT8 cache (k_scale / v_scale
  * for int8); head_dim 64 or 128; block_size 16.  Other arguments as
  * pa_decode; max_context_len is only checked against the table width.
+ * Precision: products on the matrix cores with fp32 accumulation.  Over a
+ * bf16 cache the softmax weights are rounded to bf16 and the row sums add
+ * those rounded weights, so every output row is a weighted mean of V rows
+ * with weights summing to 1; over an int8 cache the weights times the V scale
+ * are rounded to fp16 and the row sums stay fp32.
  */
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const float* k_scale, const float* v_scale, const int32_t* block_tables,
