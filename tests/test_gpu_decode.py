@@ -200,6 +200,22 @@ def test_edge_lengths_all_shapes(tag, D, G):
         assert np.array_equal(got, np.repeat(vrow, G, axis=0))
 
 
+@pytest.mark.parametrize("tag,G", [("f32", 2), ("bf16", 2), ("bf16", 6), ("int8", 2), ("int8", 6)])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1.5])
+def test_decode_scales(tag, G, scale):
+    """Negative, zero and large softmax scales on both decode kernels (vector ALUs:
+    f32 and bf16 groups below 4; matrix cores: bf16 groups of 4 or more and int8)."""
+    _say("decode scale", scale, tag, "G", G)
+    rng = np.random.default_rng(500 + G)
+    case = _random_case(rng, [1, 17, 100, 333, 700], Hkv=2, G=G, D=128, tag=tag)
+    case.scale = float(scale)
+    dc = DevCase(case)
+    want = _oracle_decode(case)
+    for split in (0, 64):
+        out = _decode(dc, split)
+        assert max_abs_err(out, want) < TOL[tag], (split, max_abs_err(out, want))
+
+
 def test_equal_keys_give_mean_of_v():
     _say("equal keys")
     rng = np.random.default_rng(9)
