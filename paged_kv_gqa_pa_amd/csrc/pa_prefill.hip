@@ -368,44 +368,46 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
         lsum[i] = ls;
       }
     } else {
+      // int8 cache: each block has its own K scale, so scores are scaled
+      // before the maximum; P carries the block's V scale.
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = s[i][e >> 2][e & 3];
-        x[e] = (kInt8 ? v - kI8Bias * qsum[i] : v) * ssc[e >> 2];
-      }
-      if (edge) {
+      for (int i = 0; i < RT; ++i) {
+        float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int pos = (blk + (e >> 2)) * kBlockSize + 4 * grp + (e & 3);
-          x[e] = pos <= last_vis[i] ? x[e] : kNegInf;
+          const float v = s[i][e >> 2][e & 3];
+          x[e] = (v - kI8Bias * qsum[i]) * ssc[e >> 2];
         }
-      }
-      float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      tmax = max_xor32(max_xor16(tmax));
-      if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
-        const float mnew = fmaxf(m[i], tmax);
-        const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
-        m[i] = mnew;
-        lsum[i] *= alpha;
+        if (edge) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float ar = __shfl(alpha, 4 * grp + j);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) o[i][t][j] *= ar;
+          for (int e = 0; e < 8; ++e) {
+            const int pos = (blk + (e >> 2)) * kBlockSize + 4 * grp + (e & 3);
+            x[e] = pos <= last_vis[i] ? x[e] : kNegInf;
+          }
         }
-      }
-      const float mref = m[i] == kNegInf ? 0.0f : m[i];
-      float p[8];
+        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        tmax = max_xor32(max_xor16(tmax));
+        if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
+          const float mnew = fmaxf(m[i], tmax);
+          const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
+          m[i] = mnew;
+          lsum[i] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] - mref);
-      lsum[i] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      pa[i] = u32x4{M::pack_round(p[0] * vsc[0], p[1] * vsc[0]), M::pack_round(p[2] * vsc[0], p[3] * vsc[0]),
-                    M::pack_round(p[4] * vsc[1], p[5] * vsc[1]), M::pack_round(p[6] * vsc[1], p[7] * vsc[1])};
-    }
+          for (int j = 0; j < 4; ++j) {
+            const float ar = __shfl(alpha, 4 * grp + j);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) o[i][t][j] *= ar;
+          }
+        }
+        const float mref = m[i] == kNegInf ? 0.0f : m[i];
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] - mref);
+        lsum[i] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pa[i] = u32x4{M::pack_round(p[0] * vsc[0], p[1] * vsc[0]), M::pack_round(p[2] * vsc[0], p[3] * vsc[0]),
+                      M::pack_round(p[4] * vsc[1], p[5] * vsc[1]), M::pack_round(p[6] * vsc[1], p[7] * vsc[1])};
+      }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
