@@ -79,24 +79,27 @@ def gather_context(cache, table_row, length, kv_head, tag, block_scale=None):
 def attend(q_rows, keys, values, scale, visible=None):
     """Dense softmax attention of query rows [R, D] over keys/values [L, D].
 
-    ``visible`` (bool [R, L]) limits which keys each row sees.  A row that sees
-    no key returns zeros.
+    ``visible`` (bool [R, L]) limits which keys each row sees (default: all).
+    Which keys count is decided by visibility alone, never by the values: a
+    NaN or infinite score, or a non-finite V row, at a visible position
+    propagates into the row's output as the dense formula gives it.  A row
+    that sees no key returns zeros.
     """
     q_rows = np.asarray(q_rows, np.float64)
-    R = q_rows.shape[0]
+    R, L = q_rows.shape[0], keys.shape[0]
     out = np.zeros((R, values.shape[1]), np.float64)
-    if keys.shape[0] == 0:
+    if L == 0:
         return out
-    s = (q_rows @ keys.T) * float(scale)
-    if visible is not None:
-        s = np.where(visible, s, -np.inf)
-    for r in range(R):
-        row = s[r]
-        seen = np.isfinite(row)
-        if not seen.any():
-            continue
-        e = np.exp(row[seen] - row[seen].max())
-        out[r] = (e / e.sum()) @ values[seen]
+    seen_all = np.ones((R, L), bool) if visible is None else np.asarray(visible, bool)
+    with np.errstate(invalid="ignore"):
+        s = (q_rows @ keys.T) * float(scale)
+        for r in range(R):
+            seen = seen_all[r]
+            if not seen.any():
+                continue
+            row = s[r, seen]
+            e = np.exp(row - row.max())
+            out[r] = (e / e.sum()) @ values[seen]
     return out
 
 

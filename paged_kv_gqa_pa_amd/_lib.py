@@ -135,6 +135,21 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
 
 
+def _int8_scales(kvd, k_scale, v_scale, kv_heads, num_blocks):
+    """The per-(KV head, block) scales of an int8 cache, checked against the cache's
+    shape (the kernels index them as [kv_heads, num_blocks]); None for other caches."""
+    if kvd != PA_INT8:
+        return None, None
+    for nm, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if s is None:
+            raise ValueError(f"{nm} is required for an int8 cache")
+        _need(s, nm, dtype=torch.float32, ndim=2)
+        if tuple(s.shape) != (kv_heads, num_blocks):
+            raise ValueError(f"{nm} must be [kv_heads, num_blocks] = {(kv_heads, num_blocks)}, "
+                             f"got {tuple(s.shape)}")
+    return k_scale, v_scale
+
+
 def version() -> int:
     return _load().pa_version()
 
@@ -263,15 +278,7 @@ def _attention(fn_verify: bool, out, q, k_cache, v_cache, block_tables, context_
     if Dq != D or block_tables.shape[0] != N or context_lens.shape[0] != N:
         raise ValueError("q, block_tables and context_lens disagree with the cache")
     kvd = _DTYPE[k_cache.dtype]
-    if kvd == PA_INT8:
-        for nm, s in (("k_scale", k_scale), ("v_scale", v_scale)):
-            if s is None:
-                raise ValueError(f"{nm} is required for an int8 cache")
-            _need(s, nm, dtype=torch.float32, ndim=2)
-            if tuple(s.shape) != (Hkv, NB):
-                raise ValueError(f"{nm} must be [kv_heads, num_blocks]")
-    else:
-        k_scale = v_scale = None
+    k_scale, v_scale = _int8_scales(kvd, k_scale, v_scale, Hkv, NB)
     need = _load().pa_workspace_size(N, T, Hq, Hkv, D, int(max_context_len), kvd, int(split_tokens))
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -336,13 +343,7 @@ def verify_varlen(out, q, k_cache, v_cache, block_tables, context_lens, query_st
     if Dq != D or context_lens.shape[0] != N or query_start.shape[0] != N + 1:
         raise ValueError("q, block_tables, context_lens and query_start disagree")
     kvd = _DTYPE[k_cache.dtype]
-    if kvd == PA_INT8:
-        for nm, s in (("k_scale", k_scale), ("v_scale", v_scale)):
-            if s is None:
-                raise ValueError(f"{nm} is required for an int8 cache")
-            _need(s, nm, dtype=torch.float32, ndim=2)
-    else:
-        k_scale = v_scale = None
+    k_scale, v_scale = _int8_scales(kvd, k_scale, v_scale, Hkv, NB)
     T = int(max_query_tokens)
     need = _load().pa_workspace_size(N, T, Hq, Hkv, D, int(max_context_len), kvd, int(split_tokens))
     if need and workspace is None:
@@ -407,13 +408,7 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, s
     if Dq != D or context_lens.shape[0] != N or query_start.shape[0] != N + 1:
         raise ValueError("q, block_tables, context_lens and query_start disagree")
     kvd = _DTYPE[k_cache.dtype]
-    if kvd == PA_INT8:
-        for nm, s in (("k_scale", k_scale), ("v_scale", v_scale)):
-            if s is None:
-                raise ValueError(f"{nm} is required for an int8 cache")
-            _need(s, nm, dtype=torch.float32, ndim=2)
-    else:
-        k_scale = v_scale = None
+    k_scale, v_scale = _int8_scales(kvd, k_scale, v_scale, Hkv, NB)
     mcl = block_tables.shape[1] * BS if max_context_len is None else int(max_context_len)
     args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
             _ptr(block_tables), _ptr(context_lens), _ptr(query_start), N, total,

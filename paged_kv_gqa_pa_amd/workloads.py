@@ -38,7 +38,8 @@ Draw recipe (fixed, so every consumer sees identical inputs):
   new tokens' K and V.  Values are standard normal float32, then encoded.
 * Unallocated blocks are zero, or poison (NaN; for int8 code 127 with scale
   1e30) when ``poison=True``; with poison the slots at positions >= L_b of a
-  sequence's last block are NaN as well (float caches only).
+  sequence's last block are poisoned as well (NaN; for int8 code 127, the
+  block keeping the scale of its drawn contents).
 """
 from __future__ import annotations
 
@@ -57,6 +58,8 @@ __all__ = [
     "encode",
     "assign_blocks",
     "slots_for_positions",
+    "poison_float",
+    "poison_int8",
 ]
 
 BLOCK_SIZE = 16
@@ -139,6 +142,40 @@ def slots_for_positions(block_tables, seq_ids, positions, block_size=BLOCK_SIZE)
     if (phys < 0).any():
         raise ValueError("position outside the allocated blocks")
     return phys * block_size + positions % block_size
+
+
+def poison_float(cache, tag, block_tables, context_lens, block_size=BLOCK_SIZE):
+    """Poison an fp32 or bf16 cache in place with NaN: every block no table row
+    uses, and the slots at positions >= L_b of a sequence's last block.  Returns
+    (spare blocks, poisoned tails)."""
+    fill = encode(np.full(1, np.nan, np.float32), tag)[0]
+    used = np.unique(block_tables[block_tables >= 0])
+    spare = np.setdiff1d(np.arange(cache.shape[1]), used)
+    cache[:, spare] = fill
+    tails = 0
+    for b, L in enumerate(np.asarray(context_lens)):
+        if int(L) % block_size:
+            phys = block_tables[b, (int(L) - 1) // block_size]
+            cache[:, phys, int(L) % block_size:, :] = fill
+            tails += 1
+    return len(spare), tails
+
+
+def poison_int8(codes, scales, block_tables, context_lens, block_size=BLOCK_SIZE):
+    """Poison an int8 cache in place: blocks no table row uses get code 127 and
+    scale 1e30; slots at positions >= L_b of a sequence's last block get code 127
+    (the block keeps its scale).  Returns (spare blocks, poisoned tails)."""
+    used = np.unique(block_tables[block_tables >= 0])
+    spare = np.setdiff1d(np.arange(codes.shape[1]), used)
+    codes[:, spare] = 127
+    scales[:, spare] = np.float32(1e30)
+    tails = 0
+    for b, L in enumerate(np.asarray(context_lens)):
+        if int(L) % block_size:
+            phys = block_tables[b, (int(L) - 1) // block_size]
+            codes[:, phys, int(L) % block_size:, :] = 127
+            tails += 1
+    return len(spare), tails
 
 
 # ----------------------------------------------------------------------------
@@ -272,15 +309,13 @@ def build_case(spec, layer: int = 0, poison: bool = False, seed: Optional[int] =
         v_cache = np.zeros(shape, np.int8)
         k_scale = np.ones((Hkv, spec.num_blocks), np.float32)
         v_scale = np.ones((Hkv, spec.num_blocks), np.float32)
-        if poison:
-            k_cache[...] = 127
-            v_cache[...] = 127
-            k_scale[...] = np.float32(1e30)
-            v_scale[...] = np.float32(1e30)
         k_cache[:, used] = kc
         v_cache[:, used] = vc
         k_scale[:, used] = ks
         v_scale[:, used] = vs
+        if poison:
+            poison_int8(k_cache, k_scale, table, lens, bs)
+            poison_int8(v_cache, v_scale, table, lens, bs)
         # New tokens are handed over in bf16; an int8 cache write is a separate step.
         new_k = f32_to_bf16_bits(nk32)
         new_v = f32_to_bf16_bits(nv32)
@@ -288,20 +323,11 @@ def build_case(spec, layer: int = 0, poison: bool = False, seed: Optional[int] =
         st = np.float32 if spec.kv_dtype == "f32" else np.uint16
         k_cache = np.zeros(shape, st)
         v_cache = np.zeros(shape, st)
-        if poison:
-            fill = encode(np.full(1, np.nan, np.float32), spec.kv_dtype)[0]
-            k_cache[...] = fill
-            v_cache[...] = fill
         k_cache[:, used] = encode(k32, spec.kv_dtype)
         v_cache[:, used] = encode(v32, spec.kv_dtype)
         if poison:
-            fill = encode(np.full(1, np.nan, np.float32), spec.kv_dtype)[0]
-            for b, L in enumerate(lens):
-                last = -(-int(L) // bs) - 1
-                if last >= 0 and L % bs:
-                    phys = table[b, last]
-                    k_cache[:, phys, L % bs:, :] = fill
-                    v_cache[:, phys, L % bs:, :] = fill
+            poison_float(k_cache, spec.kv_dtype, table, lens, bs)
+            poison_float(v_cache, spec.kv_dtype, table, lens, bs)
         new_k = encode(nk32, spec.kv_dtype)
         new_v = encode(nv32, spec.kv_dtype)
 

@@ -4,6 +4,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from paged_kv_gqa_pa_amd import workloads as wl
+from tests import parity_log
+
 TOL = {"f32": 1e-4, "bf16": 2e-2, "int8": 2e-2}
 
 
@@ -44,8 +47,25 @@ class DevCase:
         self.slot_mapping = opt(case.slot_mapping)
 
 
-def max_abs_err(gpu: torch.Tensor, want: np.ndarray) -> float:
-    got = host_f64(gpu)
+def max_abs_err(gpu, want: np.ndarray, tol: float = None) -> float:
+    """Largest |gpu - oracle| over all elements (gpu: a tensor or a host array); the
+    output must be finite.  Recorded per test with the tolerance it is held to
+    (``tol``, when the caller names it) and printed."""
+    got = host_f64(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
     assert got.shape == want.shape
     assert np.isfinite(got).all(), "non-finite output"
-    return float(np.abs(got - want).max()) if got.size else 0.0
+    err = float(np.abs(got - want).max()) if got.size else 0.0
+    ulp = None
+    if isinstance(gpu, torch.Tensor) and gpu.dtype == torch.bfloat16 and got.size:
+        # distance in bf16 steps from the oracle rounded to bf16: the kernel's own
+        # error, apart from the output rounding every bf16 result carries
+        ulp = int(np.abs(_bf16_order(host_bits(gpu)) -
+                         _bf16_order(wl.f32_to_bf16_bits(want.astype(np.float32)))).max())
+    parity_log.record(err, tol, ulp)
+    return err
+
+
+def _bf16_order(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns as integers in the order of the values they encode."""
+    b = bits.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)

@@ -17,6 +17,9 @@ disagrees with what the pages and the mathematics fix:
   it: an upper-triangular -1e9 matrix sliced at the chunk start;
 * invariants: physical placement of blocks does not matter; verify with one
   query token is decode; an int8 cache reads as code * per-block scale;
+* visibility, not value, decides which keys count: NaN and infinite scores or
+  values at visible positions propagate as the dense formula gives them, and
+  positions past the context or past a token's causal edge never matter;
 * variable-length verify against pure-Python loops over packed rows (with
   sequences of no query token and of more tokens than positions), equal
   counts against fixed-T verify, one token per sequence against decode;
@@ -361,6 +364,60 @@ def pin_int8_dequant(oracle):
         assert np.abs(got[b] - want).max() < 1e-12, "int8 dequant vs SDPA"
 
 
+def pin_visible_nonfinite(oracle):
+    """Visibility alone decides which keys count.  The dense formula (max-subtracted
+    exponentials over every visible position) gives NaN for a row that sees a NaN
+    score or a +inf score (inf - inf), weight 0 to a -inf score, and NaN in dimension
+    d for a row that sees a V row with NaN in d; positions a row does not see never
+    matter, whatever they hold."""
+    rng = np.random.default_rng(41)
+    D, nb = 4, 5
+    kc = rng.standard_normal((1, nb, 16, D)).astype(np.float32)
+    vc = rng.standard_normal((1, nb, 16, D)).astype(np.float32)
+    q = np.abs(rng.standard_normal((1, 2, D))).astype(np.float32) + np.float32(0.5)  # q > 0
+    table = np.array([[3, 1]], np.int32)
+    L = np.array([20], np.int32)
+
+    def with_key(pos, row):
+        k = kc.copy()
+        k[0, table[0, pos // 16], pos % 16] = row
+        return k
+
+    # NaN score at a visible position: every element of every head's row is NaN.
+    k_nan = with_key(7, np.array([np.nan, 0, 0, 0], np.float32))
+    o = oracle.decode(q, k_nan, vc, table, L, 0.5, "f32", "f32")
+    assert np.isnan(o).all(), "a visible NaN score must give a NaN row"
+    # +inf score (q > 0 times +inf): inf - inf in the exponent, NaN again.
+    k_inf = with_key(18, np.array([np.inf, 0, 0, 0], np.float32))
+    o = oracle.decode(q, k_inf, vc, table, L, 0.5, "f32", "f32")
+    assert np.isnan(o).all(), "a visible +inf score must give a NaN row"
+    # -inf score at the last position: weight exactly 0, so the row is that of the
+    # context without it (brute force over the first L - 1 positions).
+    k_ninf = with_key(19, np.array([-np.inf, 0, 0, 0], np.float32))
+    o = oracle.decode(q, k_ninf, vc, table, L, 0.5, "f32", "f32")
+    want = _brute_decode(q, kc, vc, table, L - 1, 0.5, 2)
+    assert np.isfinite(o).all() and np.abs(o - want).max() <= 1e-12, "-inf score has weight 0"
+    # NaN in dimension 2 of a visible V row: NaN in that dimension only.
+    v_nan = vc.copy()
+    v_nan[0, table[0, 0], 5, 2] = np.nan
+    o = oracle.decode(q, kc, v_nan, table, L, 0.5, "f32", "f32")
+    assert np.isnan(o[..., 2]).all() and np.isfinite(np.delete(o, 2, axis=-1)).all(), \
+        "a visible NaN value poisons its dimension"
+    # Verify: token t sees positions 0 .. L - T + t.  A NaN key at L - T + 1 reaches
+    # tokens 1 and 2 only; token 0 is unchanged (and finite).
+    T = 3
+    qv = np.abs(rng.standard_normal((1, T, 2, D))).astype(np.float32)
+    k_nan = with_key(int(L[0]) - T + 1, np.array([np.nan, 0, 0, 0], np.float32))
+    o = oracle.verify(qv, k_nan, vc, table, L, 0.5, "f32", "f32")
+    clean = oracle.verify(qv, kc, vc, table, L, 0.5, "f32", "f32")
+    assert np.isnan(o[0, 1:]).all(), "tokens that see the NaN key must be NaN"
+    assert np.array_equal(o[0, 0], clean[0, 0]), "a token that does not see it is unchanged"
+    # Positions past the context never matter: a NaN key at position L is not read.
+    k_past = with_key(int(L[0]), np.array([np.nan] * D, np.float32))
+    o = oracle.decode(q, k_past, vc, table, L, 0.5, "f32", "f32")
+    assert np.isfinite(o).all(), "a position past the context must not be read"
+
+
 def pin_cache_write(oracle):
     rng = np.random.default_rng(5)
     Hkv, nb, D = 3, 7, 8
@@ -382,4 +439,4 @@ def pin_cache_write(oracle):
 
 PINS = [pin_bruteforce_tiny, pin_closed_forms, pin_golden, pin_gqa_against_library,
         pin_verify_prefill_mask, pin_placement_invariance, pin_int8_dequant, pin_cache_write,
-        pin_verify_varlen]
+        pin_verify_varlen, pin_visible_nonfinite]

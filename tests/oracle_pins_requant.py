@@ -79,8 +79,9 @@ def pin_error_bound(o):
         target = codes[0, 0].astype(np.float64) * float(scales[0, 0])
         target[off] = row
         deq = c1.astype(np.float64) * float(s1)
-        # half a step of the new scale, plus the old rows' own rounding carried over
-        bound = 0.5 * float(s1) * (1 + 1e-6) + 0.5 * float(scales[0, 0]) * 0
+        # half a step of the new scale (the target holds the old rows as they were
+        # stored, so their earlier rounding is not part of this bound)
+        bound = 0.5 * float(s1) * (1 + 1e-6)
         assert np.abs(deq[off] - target[off]).max() <= bound, "new row within scale / 2"
         assert np.abs(deq - target).max() <= 0.5 * float(s1) * (1 + 1e-5) + 1e-30, "block within scale / 2"
         assert float(s1) * 127 >= np.abs(target).max() * (1 - 1e-6), "scale covers the block maximum"

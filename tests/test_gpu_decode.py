@@ -89,19 +89,28 @@ def test_long_ctx_int8_parity():
 
 
 def test_long_ctx_int8_poison_and_small_split():
-    _say("long_ctx_int8 poison, first 2 seqs, split 256")
-    case = wl.build_case("long_ctx_int8", poison=True)
-    dc = DevCase(case)
-    sel = slice(0, 2)
-    out = torch.empty_like(dc.q[sel])
-    pa.decode(out, dc.q[sel].contiguous(), dc.k_cache, dc.v_cache,
-              dc.block_tables[sel].contiguous(), dc.context_lens[sel].contiguous(), case.scale,
-              case.max_context_len, dc.k_scale, dc.v_scale, split_tokens=256)
+    """Two long-context sequences cut to lengths that end inside a block; their table
+    rows end there (-1 after), the tails and every block no row uses are poisoned
+    (code 127, unused blocks with scale 1e30); 256-position pieces."""
+    _say("long_ctx_int8 poison, first 2 seqs cut to 32763 / 20003, split 256")
+    case = wl.build_case("long_ctx_int8")
+    lens = np.array([32768 - 5, 20000 + 3], np.int32)
+    table = case.block_tables[:2].copy()
+    for b, L in enumerate(lens):
+        table[b, -(-int(L) // 16):] = -1
+    kc, vc = case.k_cache.copy(), case.v_cache.copy()
+    ks, vs = case.k_scale.copy(), case.v_scale.copy()
+    spare, tails = wl.poison_int8(kc, ks, table, lens)
+    wl.poison_int8(vc, vs, table, lens)
+    assert spare >= 16384 - 2048 - 1251 and tails == 2
+    q = np.ascontiguousarray(case.q[:2])
+    out = torch.empty_like(dev(q))
+    pa.decode(out, dev(q), dev(kc), dev(vc), dev(table), dev(lens), case.scale,
+              case.max_context_len, dev(ks), dev(vs), split_tokens=256)
     torch.cuda.synchronize()
-    want = oracle.decode(case.q[sel], case.k_cache, case.v_cache, case.block_tables[sel],
-                         case.context_lens[sel], case.scale, "bf16", "int8", case.k_scale,
-                         case.v_scale)
-    assert max_abs_err(out, want) < TOL["int8"]
+    want = oracle.decode(q, kc, vc, table, lens, case.scale, "bf16", "int8", ks, vs)
+    err = max_abs_err(out, want, TOL["int8"])
+    assert err < TOL["int8"], err
 
 
 def test_placement_invariance_bitwise():
@@ -151,8 +160,10 @@ def test_split_invariance_fp32():
         assert np.abs(o - outs[0]).max() < 1e-6
 
 
-def _random_case(rng, lens, Hkv, G, D, tag, qtag=None, nb=None):
-    """A PagedCase-like object with random contents for the given lengths."""
+def _random_case(rng, lens, Hkv, G, D, tag, qtag=None, nb=None, poison=False):
+    """A PagedCase-like object with random contents for the given lengths; with
+    `poison`, the blocks no sequence uses and the tails of partial last blocks hold
+    NaN (int8: code 127, and scale 1e30 for the unused blocks)."""
     qtag = qtag or ("f32" if tag == "f32" else "bf16")
     lens = np.asarray(lens, np.int32)
     maxb = max(1, -(-int(lens.max()) // 16))
@@ -166,8 +177,14 @@ def _random_case(rng, lens, Hkv, G, D, tag, qtag=None, nb=None):
     if tag == "int8":
         kc, ks = wl.quantize_int8_blocks(k32)
         vc, vs = wl.quantize_int8_blocks(v32)
+        if poison:
+            wl.poison_int8(kc, ks, table, lens)
+            wl.poison_int8(vc, vs, table, lens)
     else:
         kc, vc = wl.encode(k32, tag), wl.encode(v32, tag)
+        if poison:
+            wl.poison_float(kc, tag, table, lens)
+            wl.poison_float(vc, tag, table, lens)
     q = wl.encode(rng.standard_normal((N, Hkv * G, D), dtype=np.float32), qtag)
     spec = wl.Spec("random", 0, N, Hkv * G, Hkv, D, nb, qtag, tag, max(16, int(lens.max())))
     return wl.PagedCase(spec=spec, layer=0, context_lens=lens, block_tables=table, q=q,
@@ -185,12 +202,13 @@ EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 200, 511, 512, 513, 10
 def test_edge_lengths_all_shapes(tag, D, G):
     _say("edge lengths", tag, "D", D, "G", G)
     rng = np.random.default_rng(100 + G + D)
-    case = _random_case(rng, EDGE_LENS, Hkv=2, G=G, D=D, tag=tag)
+    case = _random_case(rng, EDGE_LENS, Hkv=2, G=G, D=D, tag=tag, poison=True)
     dc = DevCase(case)
     want = _oracle_decode(case)
     for split in (0, 32):
         out = _decode(dc, split)
-        assert max_abs_err(out, want) < TOL[tag], (split, max_abs_err(out, want))
+        err = max_abs_err(out, want, TOL[tag])
+        assert err < TOL[tag], (split, err)
         got = out.float().cpu().numpy()
         assert (got[0] == 0).all(), "empty context must give zeros"
     if tag != "int8":
@@ -372,7 +390,7 @@ def test_decode_append_negative_slot_writes_nothing():
     _, want_v = oracle.reshape_and_cache(nk, nv, case.k_cache, case.v_cache, slots)
     case.v_cache = want_v
     want = _oracle_decode(case)
-    assert np.abs(out[1].double().cpu().numpy() - want[1]).max() < TOL["bf16"]
+    assert max_abs_err(out[1], want[1], TOL["bf16"]) < TOL["bf16"]
 
 
 @pytest.mark.parametrize("tag,G", [("f32", 2), ("bf16", 6), ("int8", 6)])

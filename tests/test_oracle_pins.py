@@ -52,6 +52,11 @@ MUTATIONS = {
     # context length off by one
     "varlen_drop_last_token": ("out[lo:hi] = verify(q[None, lo:hi]", "out[lo:hi - 1] = verify(q[None, lo:hi - 1]"),
     "varlen_first_seq_length": ("context_lens[b:b + 1], scale, q_tag", "context_lens[0:1], scale, q_tag"),
+    # keys chosen by the finiteness of their score instead of by visibility
+    "mask_by_finite_score": ("seen = seen_all[r]", "seen = seen_all[r] & np.isfinite(s[r])"),
+    # visibility ignored (every row sees the whole context)
+    "visibility_ignored": ("seen_all = np.ones((R, L), bool) if visible is None else np.asarray(visible, bool)",
+                           "seen_all = np.ones((R, L), bool)"),
     "context_short_by_one": ("L = int(context_lens[b])\n        for g in range(Hkv):", "L = max(int(context_lens[b]) - 1, 0)\n        for g in range(Hkv):"),
 }
 
