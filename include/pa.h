@@ -205,6 +205,32 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same call without a workspace argument.
+ *
+ * The split-K partials go to a fixed array of PA_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on every GPU it runs on, from the first such call on
+ * that GPU until the process ends.  Nothing is allocated or freed per call.
+ * Results are those of pa_decode with the same arguments, bit for bit (same
+ * kernels).  Sizes whose partials exceed the array (pa_workspace_size(...) >
+ * PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on one GPU uses that GPU's single array: calls that
+ * may overlap on one GPU (different streams without ordering between them)
+ * race and give unspecified results; calls ordered on one stream are safe.
+ * The array's contents between calls are not part of the result (each call
+ * writes every partial it reads).  Other arguments as pa_decode.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int q_heads, int kv_heads,
+                      int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, float scale, int q_dtype, int kv_dtype,
+                      int split_tokens, void* stream);
+
+/*
  * pa_decode_append -- pa_reshape_and_cache of one new token per sequence
  * followed by pa_decode, in one launch where pa_decode runs on the vector
  * ALUs (fp32, bf16 groups below 4 query heads per KV head); elsewhere the

@@ -25,7 +25,7 @@ PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 
 EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_quant",
             "pa_default_split_tokens",
-            "pa_workspace_size", "pa_decode", "pa_decode_append", "pa_verify", "pa_verify_varlen",
+            "pa_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_decode_append", "pa_verify", "pa_verify_varlen",
             "pa_prefill", "pa_plan_size", "pa_plan", "pa_decode_planned",
             "pa_decode_append_planned", "pa_verify_planned", "pa_prefill_plan_size",
             "pa_prefill_plan", "pa_prefill_planned"]
@@ -66,6 +66,8 @@ def _load():
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,           # pointers
                               i, i, i, i, i, i, i, i,                   # sizes
                               f, i, i, i, vp, sz, vp]
+    lib.pa_decode_noalloc.restype = i
+    lib.pa_decode_noalloc.argtypes = lib.pa_decode.argtypes[:-3] + [vp]
     lib.pa_decode_append.restype = i
     lib.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i, i, i, i, i, i, i, i,
@@ -302,6 +304,34 @@ def _attention(fn_verify: bool, out, q, k_cache, v_cache, block_tables, context_
     if plan is not None:
         args += list(pp)
     _check(fn(*args, _stream(stream)))
+    return out
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                   k_scale=None, v_scale=None, split_tokens=0, stream=None):
+    """pa_decode_noalloc: decode with the split-K partials in the library's fixed device
+    array (no workspace; nothing allocated)."""
+    _need(q, "q", ndim=3)
+    _need(out, "out", dtype=q.dtype, ndim=3)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    Hkv, NB, BS, D = k_cache.shape
+    N, Hq, Dq = q.shape
+    if Dq != D or block_tables.shape[0] != N or context_lens.shape[0] != N:
+        raise ValueError("q, block_tables and context_lens disagree with the cache")
+    kvd = _DTYPE[k_cache.dtype]
+    k_scale, v_scale = _int8_scales(kvd, k_scale, v_scale, Hkv, NB)
+    _check(_load().pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), N, Hq, Hkv, D, BS, NB, block_tables.shape[1],
+        int(max_context_len), float(scale), _DTYPE[q.dtype], kvd, int(split_tokens),
+        _stream(stream)))
     return out
 
 

@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/pa.h"
 #include "pa_kernels.h"
 
@@ -286,6 +288,42 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
 
 }  // namespace
 
+namespace {
+
+// The fixed device array behind pa_decode_noalloc: the split-K partials of a
+// call live here instead of in a caller workspace.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` only
+// names the symbol; its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and that pointer is what
+// the kernels receive.
+__device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "scratch array address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int pa_version(void) { return 100; }
@@ -374,6 +412,33 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                        context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
                        num_blocks, max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
                        split_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int q_heads, int kv_heads,
+                      int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, float scale, int q_dtype, int kv_dtype,
+                      int split_tokens, void* stream) {
+  SplitPlan plan;
+  int st = plan_pieces(num_seqs, 1, q_heads, kv_heads, head_dim, max_context_len, kv_dtype,
+                       split_tokens, &plan);
+  if (st != PA_OK) return st;
+  const size_t need = plan.total();
+  if (need > size_t(PA_NOALLOC_SCRATCH_BYTES))
+    return fail(PA_ERR_WORKSPACE,
+                "these sizes need %zu bytes of partials; the fixed scratch array holds %zu "
+                "(use pa_decode with a workspace, or a longer split_tokens)",
+                need, size_t(PA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0 && num_seqs > 0) {
+    st = scratch_ptr(&ws);
+    if (st != PA_OK) return st;
+  }
+  return run_attention(false, out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
+                       split_tokens, ws, ws ? size_t(PA_NOALLOC_SCRATCH_BYTES) : 0, stream);
 }
 
 int pa_decode_append(void* out, const void* q, const void* key, const void* value,
