@@ -31,6 +31,10 @@ import numpy as np
 WORKLOAD = "batch64_28layer_bf16"
 METRIC = "paged GQA decode attention: achieved HBM GB/s (% of peak) + tokens/s at batch 64"
 HBM_PEAK_GBPS = 8000.0
+ROTATION_BYTES = 1 << 30
+# The five seeded workloads by their configuration keys.
+CONFIG_KEYS = {"tiny_fp32": "C1", "qwen2_1p5b_bf16": "C2", "batch64_28layer_bf16": "C3",
+               "spec_verify_bf16": "C4", "long_ctx_int8": "C5"}
 
 
 def parse():
@@ -43,7 +47,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-buckets", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="target CPU time of the oracle baseline sample")
+                   help="target CPU time of the oracle baseline sample (batch-64 workload)")
+    p.add_argument("--cpu-seconds-other", type=float, default=3.0,
+                   help="target CPU time per leg of the oracle baselines of the other workloads")
     p.add_argument("--decode-reps", type=int, default=20,
                    help="graph replays of the 28 decode launches for the per-kernel timing")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -122,7 +128,8 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
     lengths and block tables are the seeded ones."""
     out = {}
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "int8": torch.int8}
-    for name in ("qwen2_1p5b_bf16", "spec_verify_bf16", "spec_verify_varlen_bf16", "long_ctx_int8"):
+    for name in ("tiny_fp32", "qwen2_1p5b_bf16", "spec_verify_bf16", "spec_verify_varlen_bf16",
+                 "long_ctx_int8"):
         varlen = name == "spec_verify_varlen_bf16"
         spec = wl.CONFIGS["spec_verify_bf16" if varlen else name]
         lens, table = wl.structure(spec)
@@ -136,8 +143,15 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
                                 spec.kv_heads, spec.head_dim, spec.num_blocks)
         kdt = tdt[spec.kv_dtype]
         elem = {torch.bfloat16: 2, torch.float32: 4, torch.int8: 1}[kdt]
-        cache_bytes = Hkv * NB * 16 * D * elem
-        R = max(1, min(64, int(np.ceil(1.0e9 / (2 * cache_bytes)))))
+        q_elem = 4 if spec.q_dtype == "f32" else 2
+        # Bytes one call touches (its K/V rows, q, out, table entries, lengths, scales);
+        # replicas enough that one rotation touches at least 1 GiB of distinct memory, four
+        # times the 256 MB last-level cache.  The tiny workload (58 KB, launch-bound)
+        # runs on one copy: its time is reported with no roofline claim.
+        touched = (attention_bytes(lens, 1, Hq, Hkv, D, elem, q_elem) +
+                   (int(counts.sum()) if varlen else N * T) * Hq * D * q_elem * 2 -
+                   N * Hq * D * q_elem * 2)
+        R = 1 if name == "tiny_fp32" else int(np.ceil(ROTATION_BYTES / touched))
 
         def mk():
             if kdt == torch.int8:
@@ -157,7 +171,8 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
             qs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
         else:
             total = N * T
-            q = torch.randn((N, T, Hq, D) if T > 1 else (N, Hq, D), device=dev, dtype=torch.bfloat16)
+            q = torch.randn((N, T, Hq, D) if T > 1 else (N, Hq, D), device=dev,
+                            dtype=torch.float32 if spec.q_dtype == "f32" else torch.bfloat16)
         o = torch.empty_like(q)
         split = pa.default_split_tokens(Hq, Hkv, D, kdt, num_query_tokens=T)
         wsb = pa.workspace_size(N, T, Hq, Hkv, D, spec.max_len, kdt, split)
@@ -198,17 +213,23 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * R * cycles)
-        alg = attention_bytes(lens, 1, Hq, Hkv, D, elem) + (total - N) * Hq * D * 2 * 2
+        alg = touched
         gbps = alg / (us * 1e-6) / 1e9
-        out[name] = {"us_per_call": round(us, 2), "algorithmic_bytes": alg,
+        out[name] = {"config": CONFIG_KEYS.get(name, CONFIG_KEYS["spec_verify_bf16"] + " (1..5 tokens)"),
+                     "us_per_call": round(us, 2), "algorithmic_bytes": alg,
                      "hbm_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "query_tokens_per_s": round(total / (us * 1e-6), 1),
+                     "rotation": {"replicas": R, "bytes_touched_per_call": alg,
+                                  "bytes_per_rotation": R * alg, "calls_per_graph": R * cycles},
                      "split_tokens": split, "work_plan": plan is not None,
                      "kernel": "rows_pass1" if (T > 1 or elem == 1 or Hq // Hkv >= 4) else "decode_pass1",
                      "shape": f"N={N} T={'1..5 per sequence, ' + str(total) + ' rows' if varlen else T} "
                               f"Hq={Hq} Hkv={Hkv} D={D} kv={spec.kv_dtype}"}
-        print(f"[bench] {name}: {us:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}%)",
-              flush=True)
+        if name == "tiny_fp32":
+            out[name]["note"] = "launch-bound (58 KB per call): time reported, no roofline claim"
+            del out[name]["frac"]
+        print(f"[bench] {name}: {us:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}%), "
+              f"{R} replicas x {alg / 1e6:.1f} MB per rotation", flush=True)
         del kc, vc, g
         torch.cuda.empty_cache()
     out["int8_requant_write"] = requant_write_timing(torch, pa, dev, reps)
@@ -419,15 +440,135 @@ def cpu_baseline(target_s: float):
     return res
 
 
-def _cpu_model():
+# The oracle per (sequence, KV head) unit of the other configurations: the cases are
+# built before the pool forks, so the workers see them.
+_CPU_CASES = {}
+
+
+def _oracle_unit(name, b, g):
+    """The oracle's result for sequence b, KV head g (its G query heads) of a config."""
+    import oracle
+    c = _CPU_CASES[name]
+    spec = c.spec
+    G = spec.q_heads // spec.kv_heads
+    hs = slice(g * G, (g + 1) * G)
+    ks = None if c.k_scale is None else c.k_scale[g:g + 1]
+    vs = None if c.v_scale is None else c.v_scale[g:g + 1]
+    if spec.num_query_tokens > 1:
+        return oracle.verify(c.q[b:b + 1, :, hs], c.k_cache[g:g + 1], c.v_cache[g:g + 1],
+                             c.block_tables[b:b + 1], c.context_lens[b:b + 1], c.scale,
+                             spec.q_dtype, spec.kv_dtype, ks, vs)
+    return oracle.decode(c.q[b:b + 1, hs], c.k_cache[g:g + 1], c.v_cache[g:g + 1],
+                         c.block_tables[b:b + 1], c.context_lens[b:b + 1], c.scale,
+                         spec.q_dtype, spec.kv_dtype, ks, vs)
+
+
+def _oracle_unit_task(args):
+    return _oracle_unit(*args).shape
+
+
+def oracle_config_baselines(target_s, workers):
+    """The fp64 oracle timed on every other configuration (C1, C2, C4, C5) over its
+    (sequence, KV head) units: (i) one core, one BLAS thread, units in order until
+    about target_s seconds have passed (a whole call or a bounded part of one);
+    (ii) a process pool of `workers` processes over the units, whole calls repeated
+    for about target_s seconds.  Query tokens per second and GB/s on the same
+    algorithmic bytes the GPU figures use."""
+    import multiprocessing as mp
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from paged_kv_gqa_pa_amd import workloads as wl
+    names = ("tiny_fp32", "qwen2_1p5b_bf16", "spec_verify_bf16", "long_ctx_int8")
+    for n in names:
+        _CPU_CASES[n] = wl.build_case(n)
+    out = {}
+    try:
+        for n in names:
+            c = _CPU_CASES[n]
+            spec = c.spec
+            units = [(n, b, g) for b in range(spec.num_seqs) for g in range(spec.kv_heads)]
+            tokens = spec.num_seqs * spec.num_query_tokens
+            kv_elem = {"f32": 4, "bf16": 2, "int8": 1}[spec.kv_dtype]
+            alg = attention_bytes(c.context_lens, spec.num_query_tokens, spec.q_heads,
+                                  spec.kv_heads, spec.head_dim, kv_elem,
+                                  4 if spec.q_dtype == "f32" else 2)
+            ctx = threadpool_limits(1) if threadpool_limits else None
+            try:
+                done, t0 = 0, time.perf_counter()
+                while True:
+                    _oracle_unit(*units[done % len(units)])
+                    done += 1
+                    el = time.perf_counter() - t0
+                    if el >= target_s:
+                        break
+            finally:
+                if ctx is not None:
+                    ctx.__exit__(None, None, None)
+            per_call = el / done * len(units)
+            out[CONFIG_KEYS[n]] = {
+                "workload": n, "unit": "query tokens/s", "kind": "oracle",
+                "algorithmic_bytes": alg,
+                "one_core": {"value": round(tokens / per_call, 3), "cores": 1,
+                             "gbps": round(alg / per_call / 1e9, 4),
+                             "sample": f"{done} (sequence, KV head) units (a call has "
+                                       f"{len(units)}) in {el:.1f} s on one core"}}
+        with mp.get_context("fork").Pool(workers, initializer=_pool_init) as pool:
+            pool.map(_oracle_unit_task, [("tiny_fp32", 0, 0)] * workers)   # start-up
+            for n in names:
+                spec = _CPU_CASES[n].spec
+                units = [(n, b, g) for b in range(spec.num_seqs) for g in range(spec.kv_heads)]
+                r = out[CONFIG_KEYS[n]]
+                calls, t0 = 0, time.perf_counter()
+                while True:
+                    pool.map(_oracle_unit_task, units, chunksize=max(1, len(units) // (4 * workers)))
+                    calls += 1
+                    el = time.perf_counter() - t0
+                    if el >= target_s:
+                        break
+                per_call = el / calls
+                tokens = spec.num_seqs * spec.num_query_tokens
+                r["all_cores"] = {"value": round(tokens / per_call, 3), "cores": workers,
+                                  "gbps": round(r["algorithmic_bytes"] / per_call / 1e9, 4),
+                                  "sample": f"{calls} whole calls over a {workers}-process pool "
+                                            f"in {el:.1f} s"}
+    finally:
+        _CPU_CASES.clear()
+    return out
+
+
+def _cpu_model():
+    """The host CPU as lscpu names it (model name, family / model / stepping, sockets and
+    cores), else /proc/cpuinfo's model name."""
+    import subprocess
+    info = {}
+    try:
+        res = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in res.stdout.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info[k.strip()] = v.strip()
+    except (OSError, subprocess.SubprocessError):
         pass
-    return "unknown"
+    name = info.get("Model name")
+    if not name:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        name = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    parts = [name or "unknown"]
+    if info.get("CPU family"):
+        parts.append(f"family {info['CPU family']} model {info.get('Model', '?')} "
+                     f"stepping {info.get('Stepping', '?')}")
+    if info.get("Socket(s)"):
+        parts.append(f"{info['Socket(s)']} socket(s) x {info.get('Core(s) per socket', '?')} cores x "
+                     f"{info.get('Thread(s) per core', '?')} threads")
+    return "; ".join(parts)
 
 
 def main():
@@ -439,11 +580,17 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        # before the GPU is touched: the all-cores leg forks worker processes
+        # before the GPU is touched: the all-cores legs fork worker processes
         print("[bench] cpu baseline ...", flush=True)
         cpu = cpu_baseline(args.cpu_seconds)
         print(f"[bench] cpu baseline: {cpu['value']} tokens/s on 1 core, "
               f"{cpu['all_cores']['value']} on {cpu['all_cores']['cores']}", flush=True)
+        cpu["other_configs"] = oracle_config_baselines(args.cpu_seconds_other,
+                                                       cpu["all_cores"]["cores"])
+        for k, r in cpu["other_configs"].items():
+            print(f"[bench] cpu baseline {k} {r['workload']}: {r['one_core']['value']} query "
+                  f"tokens/s on 1 core, {r['all_cores']['value']} on {r['all_cores']['cores']}",
+                  flush=True)
 
     import torch
     from paged_kv_gqa_pa_amd import _lib as pa
