@@ -193,9 +193,10 @@ size_t pa_workspace_size(int num_seqs, int num_query_tokens, int q_heads, int kv
  * Supported: head_dim 64 or 128; block_size 16; q_heads / kv_heads in 1..8
  * or 16; the dtype triples listed at the top.
  * Precision: scores, softmax and the weighted sum accumulate in fp32.  Over a
- * bf16 cache the softmax weights are rounded to bf16 for the weighted sum of
- * V (the sum of the weights stays fp32); over an fp32 cache they stay fp32;
- * over an int8 cache they are rounded to fp16 (see pa_verify).
+ * bf16 cache the softmax weights are rounded to bf16 (to nearest even) for the
+ * weighted sum of V and the row's sum of weights adds those rounded weights,
+ * so each output row is a weighted mean of V rows whose weights sum to 1; over
+ * an fp32 cache the weights stay fp32; over an int8 cache see pa_verify.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
@@ -277,8 +278,15 @@ int pa_decode_append(void* out, const void* q, const void* key, const void* valu
  * PA_ERR_UNSUPPORTED.
  * Supported dtypes: PA_BF16 q with a PA_BF16 or PA_INT8 cache (bf16 output;
  * int8 needs k_scale / v_scale); head_dim 64 or 128.  Scores and the output
- * accumulate in fp32 on the matrix cores; the softmax weights are rounded to
- * bf16 (bf16 cache) or fp16 (int8 cache) for the weighted sum of V.
+ * accumulate in fp32 on the matrix cores.  The softmax weights are rounded to
+ * bf16 (to nearest even) for the weighted sum of V -- over an int8 cache each
+ * weight times its block's V scale, against the exact codes -- and the row's
+ * sum of weights adds the rounded weights (an int8 block's divided by its V
+ * scale again), so numerator and denominator use one set of weights.
+ * int8 caches: the scores are fp16 products: q is converted to fp16 (to
+ * nearest even; exact for bf16 values of magnitude 6.1e-5 .. 65504, infinite
+ * past it), the codes exactly.  The V scales of the blocks read must be
+ * positive and finite.
  */
 int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
@@ -416,11 +424,9 @@ int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* 
  * Supported: PA_BF16 q with a PA_BF16 or PA_INT8 cache (k_scale / v_scale
  * for int8); head_dim 64 or 128; block_size 16.  Other arguments as
  * pa_decode; max_context_len is only checked against the table width.
- * Precision: products on the matrix cores with fp32 accumulation.  Over a
- * bf16 cache the softmax weights are rounded to bf16 and the row sums add
- * those rounded weights, so every output row is a weighted mean of V rows
- * with weights summing to 1; over an int8 cache the weights times the V scale
- * are rounded to fp16 and the row sums stay fp32.
+ * Precision: products on the matrix cores with fp32 accumulation; weights
+ * rounded and summed as pa_verify describes (the same ranges hold for int8
+ * caches).
  */
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const float* k_scale, const float* v_scale, const int32_t* block_tables,

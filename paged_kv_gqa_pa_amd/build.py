@@ -39,8 +39,22 @@ def hipcc() -> str:
     return path if os.path.exists(path) else shutil.which("hipcc") or "hipcc"
 
 
+def _fresh(obj: str, src: str) -> bool:
+    """With PA_BUILD_INCREMENTAL=1 in the environment, an object newer than its source
+    and every header is reused (a development shortcut; build() compiles everything
+    otherwise)."""
+    if os.environ.get("PA_BUILD_INCREMENTAL") != "1" or not os.path.exists(obj):
+        return False
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC)
+                                        if h.endswith(".h")]
+    deps.append(os.path.join(HERE, "..", "include", "pa.h"))
+    return all(os.path.getmtime(obj) > os.path.getmtime(d) for d in deps if os.path.exists(d))
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    if _fresh(obj, src) and not extra:
+        return obj
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(HERE, "..", "include"),
            "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -326,7 +326,8 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       // bf16 cache: the lane's key rows in pairs, each dimension's two values
       // in one word, so that one packed product adds both rows' terms.  The
       // weights are rounded to bf16 for this product (as on the matrix
-      // cores); the running sum keeps them in fp32.
+      // cores), and the running sum adds the rounded weights: numerator and
+      // denominator use one set of weights.
       uint32_t vp[KR / 2][E];
 #pragma unroll
       for (int k2 = 0; k2 < KR / 2; ++k2)
@@ -342,16 +343,17 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
       for (int h = 0; h < G; ++h) {
         const float mref = m[h] == kNegInf ? 0.0f : m[h];
         float pw[KR];
-        float psum = 0.0f;
 #pragma unroll
-        for (int k = 0; k < KR; ++k) {
-          pw[k] = fast_exp2(s[h][k] - mref);
-          psum += pw[k];
-        }
-        l[h] += psum;
+        for (int k = 0; k < KR; ++k) pw[k] = fast_exp2(s[h][k] - mref);
         bf16x2 pp[KR / 2];
+        const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+        float lh = l[h];
 #pragma unroll
-        for (int k2 = 0; k2 < KR / 2; ++k2) pp[k2] = pack_bf16x2(pw[2 * k2], pw[2 * k2 + 1]);
+        for (int k2 = 0; k2 < KR / 2; ++k2) {
+          pp[k2] = pack_bf16x2(pw[2 * k2], pw[2 * k2 + 1]);
+          lh = __builtin_amdgcn_fdot2_f32_bf16(pp[k2], ones, lh, false);
+        }
+        l[h] = lh;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           float x = acc[h][e];

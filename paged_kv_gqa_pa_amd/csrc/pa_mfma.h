@@ -1,5 +1,5 @@
 // Matrix-core operand helpers shared by the kernels that run attention on
-// the MFMA units (gfx950): products and conversions per cache element type.
+// the MFMA units (gfx950): products and conversions.
 #pragma once
 
 #include "pa_device.h"
@@ -12,7 +12,8 @@ typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRows = 16;  // query rows of one matrix tile
 
-// Products and conversions per cache element type.
+// Score products (K tile on the left, query rows on the right) and the
+// identity product that turns int8 V codes, per cache element type.
 template <typename KV> struct MOps;
 template <> struct MOps<bf16_t> {
   static constexpr uint32_t kOne = 0x3F80u;  // bf16 1.0
@@ -20,19 +21,6 @@ template <> struct MOps<bf16_t> {
   __device__ static f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
-  }
-  __device__ static f32x4 mm16(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-  }
-  // Two fp32 values that are bf16 numbers: their high halves.
-  __device__ static uint32_t pack_exact(float lo, float hi) {
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-  }
-  // Two fp32 values rounded to nearest even, in one packed conversion.
-  __device__ static uint32_t pack_round(float lo, float hi) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
   }
 };
 template <> struct MOps<i8_t> {
@@ -46,11 +34,33 @@ template <> struct MOps<i8_t> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4, a),
                                                  __builtin_bit_cast(h16x4, b), c, 0, 0, 0);
   }
-  __device__ static uint32_t pack_exact(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-  }
-  __device__ static uint32_t pack_round(float lo, float hi) { return pack_exact(lo, hi); }
 };
+
+// P.V products, bf16 for every cache type: P is a softmax weight (times an
+// int8 block's V scale), rounded to bf16, so its range is fp32's; V is a bf16
+// cache value or an int8 code, exact in bf16.
+__device__ __forceinline__ f32x4 pv16(u32x2 p, u32x2 v, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, p),
+                                                   __builtin_bit_cast(s16x4, v), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 pv32(u32x4 p, u32x4 v, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, p),
+                                                __builtin_bit_cast(bf16x8, v), c, 0, 0, 0);
+}
+// Two fp32 values that are bf16 numbers (int8 codes here): their high halves.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+// Two fp32 values rounded to nearest even, in one packed conversion.
+__device__ __forceinline__ uint32_t pack_bf16_round(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, pack_bf16x2(lo, hi));
+}
+// acc + the two bf16 values packed in w (one dot product against (1, 1); the
+// products are exact).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+}
 
 // bf16 V tiles staged in LDS for transposed reads.  16-byte chunk k of key
 // row r sits at chunk position k ^ vswz(r): the rows an output block's read
@@ -75,6 +85,13 @@ __device__ __forceinline__ u32x2 v_operand_tr(const char* sv, int t, int lane) {
   const char* p = sv + r * ROWB + 16 * (k ^ vswz<ROWB>(r)) + 8 * (lane & 1);
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
   return __builtin_bit_cast(u32x2, v);
+}
+
+// Two fp32 values as fp16, rounded to nearest even (values past fp16's range
+// become infinite).
+__device__ __forceinline__ f16x2 to_f16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_convertvector(f32x2{lo, hi}, f16x2);
 }
 
 // Eight codes (two words) as the fp16 numbers c + 1152.

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
       if constexpr (kInt8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e]), bf16_hi(w[e]));
+          const f16x2 hp = to_f16x2(bf16_lo(w[e]), bf16_hi(w[e]));
           qb[i][c][e] = __builtin_bit_cast(uint32_t, hp);
           qpart += float(hp[0]) + float(hp[1]);
         }
@@ -237,9 +237,11 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
       const bool need = blk * kBlockSize < kend;
       phys[kb] = need ? min(max(bt[readfirstlane(blk)], 0), a.num_blocks - 1) : 0;
       if constexpr (kInt8) {
+        // a block past the needed range is fully masked: any finite, nonzero
+        // scale keeps its zero weights zero (the row sum divides by the V scale)
         typedef const __attribute__((address_space(4))) float* const_f32_ptr;
-        ks[kb] = need ? ((const_f32_ptr)a.k_scale)[head_blocks + phys[kb]] : 0.0f;
-        vs[kb] = need ? ((const_f32_ptr)a.v_scale)[head_blocks + phys[kb]] : 0.0f;
+        ks[kb] = need ? ((const_f32_ptr)a.k_scale)[head_blocks + phys[kb]] : 1.0f;
+        vs[kb] = need ? ((const_f32_ptr)a.v_scale)[head_blocks + phys[kb]] : 1.0f;
       }
     }
   };
@@ -319,12 +321,12 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
     const bool edge = (blk + 2) * kBlockSize - 1 > w_minvis;   // uniform per wave
     const float ssc[2] = {sc * ks0, sc * ks1};
     const float vsc[2] = {vs0, vs1};
+    const float ivsc[2] = {kInt8 ? __builtin_amdgcn_rcpf(vs0) : 1.0f, kInt8 ? __builtin_amdgcn_rcpf(vs1) : 1.0f};
     u32x4 pa[RT];
     if constexpr (!kInt8) {
       // bf16 cache: one factor for both blocks, so the row maximum is taken
       // over the raw scores and each weight is exp2 of one fused multiply-add;
       // the running sum adds the weights as rounded for the P.V product.
-      const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
 #pragma unroll
       for (int i = 0; i < RT; ++i) {
         float r[8];
@@ -357,14 +359,11 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(r[e], sc_pos, nref));
-        pa[i] = u32x4{M::pack_round(p[0], p[1]), M::pack_round(p[2], p[3]),
-                      M::pack_round(p[4], p[5]), M::pack_round(p[6], p[7])};
+        pa[i] = u32x4{pack_bf16_round(p[0], p[1]), pack_bf16_round(p[2], p[3]),
+                      pack_bf16_round(p[4], p[5]), pack_bf16_round(p[6], p[7])};
         float ls = lsum[i];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t pw = pa[i][w];
-          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), ones, ls, false);
-        }
+        for (int w = 0; w < 4; ++w) ls = add_bf16_pair(pa[i][w], ls);
         lsum[i] = ls;
       }
     } else {
@@ -404,9 +403,13 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] - mref);
-        lsum[i] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        pa[i] = u32x4{M::pack_round(p[0] * vsc[0], p[1] * vsc[0]), M::pack_round(p[2] * vsc[0], p[3] * vsc[0]),
-                      M::pack_round(p[4] * vsc[1], p[5] * vsc[1]), M::pack_round(p[6] * vsc[1], p[7] * vsc[1])};
+        pa[i] = u32x4{pack_bf16_round(p[0] * vsc[0], p[1] * vsc[0]), pack_bf16_round(p[2] * vsc[0], p[3] * vsc[0]),
+                      pack_bf16_round(p[4] * vsc[1], p[5] * vsc[1]), pack_bf16_round(p[6] * vsc[1], p[7] * vsc[1])};
+        // the row sum adds the weights as rounded for the product, each block's
+        // divided by its V scale again
+        const float t0 = add_bf16_pair(pa[i][0], add_bf16_pair(pa[i][1], 0.0f));
+        const float t1 = add_bf16_pair(pa[i][2], add_bf16_pair(pa[i][3], 0.0f));
+        lsum[i] = __builtin_fmaf(t1, ivsc[1], __builtin_fmaf(t0, ivsc[0], lsum[i]));
       }
     }
 #pragma unroll
@@ -418,14 +421,14 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
         if constexpr (kInt8) {
           const uint32_t u = *reinterpret_cast<const uint32_t*>(sv + sw(n, t) + 4 * grp) ^ 0x80808080u;
           const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
-          vb[h] = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
+          vb[h] = u32x2{pack_bf16_exact(tv[0], tv[1]), pack_bf16_exact(tv[2], tv[3])};
         } else {
           vb[h] = v_operand_tr<ROWB>(sv, t, lane);
         }
       }
       const u32x4 v8 = {vb[0][0], vb[0][1], vb[1][0], vb[1][1]};
 #pragma unroll
-      for (int i = 0; i < RT; ++i) o[i][t] = M::qk(pa[i], v8, o[i][t]);
+      for (int i = 0; i < RT; ++i) o[i][t] = pv32(pa[i], v8, o[i][t]);
     }
   };
 
@@ -435,7 +438,11 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
   // frees buffer (st - 1) % NBUF, which the stage st + NBUF - 1 loads issued
   // right after it overwrite.  The loop is unrolled by NBUF so that buffers
   // and each stage's int8 scales are compile-time choices.
-  float ks[NBUF][KB] = {}, vs[NBUF][KB] = {};
+  float ks[NBUF][KB], vs[NBUF][KB];
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) ks[u][kb] = vs[u][kb] = 1.0f;
   int phys_next[KB] = {};
   auto wait_tiles = [&](int later) {   // stage st done; `later` stages may still load
     static_assert(NBUF - 2 <= 3 && (NBUF - 2) * LPW <= 63, "vmcnt range");

@@ -22,10 +22,11 @@
 //       the next), the values passing through exactly.
 //
 // bf16 caches run all products in bf16 (P rounded to bf16).  int8 caches run
-// them in fp16: a code c becomes the exact fp16 number c + 1152 (byte permute
-// under a constant high byte), the scores lose the K bias as
-// -1152 * sum_d q[row, d], the V bias is removed by starting the transposing
-// product's accumulator at -1152, and P carries the tile's V scale.
+// the score products in fp16: a code c becomes the exact fp16 number c + 1152
+// (byte permute under a constant high byte) and the scores lose the K bias as
+// -1152 * sum_d q[row, d]; the transposing product removes the V bias by
+// starting its accumulator at -1152, and P.V runs in bf16 (the codes are
+// exact bf16 numbers) with P carrying the tile's V scale.
 //
 // Row t*G + i is query token t of head g*G + i; token t sees positions
 // 0 .. L - T + t.  Pieces, workspace partials and the merge pass are shared
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
       if constexpr (kInt8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const auto hp = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e]), bf16_hi(w[e]));
+          const f16x2 hp = to_f16x2(bf16_lo(w[e]), bf16_hi(w[e]));
           qb[c][e] = __builtin_bit_cast(uint32_t, hp);
           qpart += float(hp[0]) + float(hp[1]);
         }
@@ -275,9 +276,16 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
     float p[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[j] - mref);
-    lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    // P as the A operand (row n, keys 4*grp ..); an int8 tile's V scale rides on it.
-    const u32x2 pa = {M::pack_round(p[0] * vs, p[1] * vs), M::pack_round(p[2] * vs, p[3] * vs)};
+    // P as the A operand (row n, keys 4*grp ..), bf16; an int8 tile's V scale
+    // rides on it.
+    const u32x2 pa = {pack_bf16_round(p[0] * vs, p[1] * vs), pack_bf16_round(p[2] * vs, p[3] * vs)};
+    // The row sum adds the weights as rounded for the P.V product (an int8 tile's
+    // divided by its V scale again), so numerator and denominator use one set of
+    // weights.
+    if constexpr (kInt8)
+      lsum = __builtin_fmaf(add_bf16_pair(pa[0], add_bf16_pair(pa[1], 0.0f)), __builtin_amdgcn_rcpf(vs), lsum);
+    else
+      lsum = add_bf16_pair(pa[0], add_bf16_pair(pa[1], lsum));
     // V of keys 4*grp .. 4*grp+3 at dim 16t + n (the B operand).
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -286,11 +294,11 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         // key n's codes of dims 16t + 4grp .. +3, turned by the identity product
         const uint32_t u = *reinterpret_cast<const uint32_t*>(sv + sw(n, t) + 4 * grp) ^ 0x80808080u;
         const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
-        vb = u32x2{M::pack_exact(tv[0], tv[1]), M::pack_exact(tv[2], tv[3])};
+        vb = u32x2{pack_bf16_exact(tv[0], tv[1]), pack_bf16_exact(tv[2], tv[3])};
       } else {
         vb = v_operand_tr<ROWB>(sv, t, lane);   // four keys of one dim
       }
-      o[t] = M::mm16(pa, vb, o[t]);
+      o[t] = pv16(pa, vb, o[t]);
     }
     // This slot is loaded again next: its reads must be done first.
     __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));

@@ -154,3 +154,45 @@ def test_int8_scale_shape_checked(entry, bad):
             else:
                 pa.prefill(o, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qs,
                            case.scale, T, ks, dc.v_scale)
+
+
+@pytest.mark.parametrize("v_lo,v_hi", [(1e-6, 1e-6), (200.0, 250.0), (1e-4, 250.0), (1e-9, 1e4)])
+def test_int8_v_scale_range(v_lo, v_hi):
+    """V scales from tiny to large, mixed per block (the weights times the scale are
+    bf16, so no scale over- or underflows them): decode, verify and prefill keep the
+    oracle's values to 8e-3 of the output's magnitude (bf16 output rounding is 2^-9
+    of it)."""
+    _say("int8 v_scale range", v_lo, v_hi)
+    case = _case(3, 5, 90)
+    rng = np.random.default_rng(91)
+    used = np.unique(case.block_tables[case.block_tables >= 0])
+    case.v_scale[:, used] = np.exp(rng.uniform(np.log(v_lo), np.log(v_hi), size=(2, len(used))))
+    dc = DevCase(case)
+
+    def check(out, want):
+        got = out.double().cpu().numpy()
+        rel = float(np.abs(got - want).max() / np.abs(want).max())
+        max_abs_err(got / np.abs(want).max(), want / np.abs(want).max(), 8e-3)
+        assert rel < 8e-3, rel
+
+    want = oracle.verify(case.q, case.k_cache, case.v_cache, case.block_tables,
+                         case.context_lens, case.scale, "bf16", "int8", case.k_scale,
+                         case.v_scale)
+    out = torch.empty_like(dc.q)
+    pa.verify(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, case.scale,
+              case.max_context_len, dc.k_scale, dc.v_scale, split_tokens=512)
+    torch.cuda.synchronize()
+    check(out, want)
+    q1 = dc.q[:, 4].contiguous()
+    out1 = torch.empty_like(q1)
+    pa.decode(out1, q1, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, case.scale,
+              case.max_context_len, dc.k_scale, dc.v_scale)
+    torch.cuda.synchronize()
+    check(out1, want[:, 4])
+    qs = (np.arange(case.num_seqs + 1) * 5).astype(np.int32)
+    qp = dc.q.reshape(-1, *dc.q.shape[2:])
+    outp = torch.empty_like(qp)
+    pa.prefill(outp, qp, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, dev(qs),
+               case.scale, 5, dc.k_scale, dc.v_scale)
+    torch.cuda.synchronize()
+    check(outp, want.reshape(-1, *want.shape[2:]))
