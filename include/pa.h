@@ -273,9 +273,12 @@ int pa_decode_append(void* out, const void* q, const void* key, const void* valu
  * row that sees none returns zeros.
  *
  * out, q        [num_seqs, num_query_tokens, q_heads, head_dim], q_dtype
- * other arguments as pa_decode.  num_query_tokens * (q_heads / kv_heads)
- * must be <= 16 (the row count of one matrix-core tile), else
- * PA_ERR_UNSUPPORTED.
+ * other arguments as pa_decode.  Any num_query_tokens and group size: the
+ * num_query_tokens * (q_heads / kv_heads) query rows of a (sequence, KV head)
+ * take one to three 16-row matrix-core tiles that share every K and V read
+ * (up to 48 rows, with split-K pieces as pa_decode); beyond 48 rows the call
+ * runs on the prefill kernel (pa_prefill's definition, which is this one; no
+ * pieces, the workspace and a work plan are then not used).
  * Supported dtypes: PA_BF16 q with a PA_BF16 or PA_INT8 cache (bf16 output;
  * int8 needs k_scale / v_scale); head_dim 64 or 128.  Scores and the output
  * accumulate in fp32 on the matrix cores.  The softmax weights are rounded to
@@ -386,8 +389,8 @@ int pa_verify_planned(void* out, const void* q, const void* k_cache, const void*
  *               that nothing outside q / out is touched).  Rows of out that
  *               belong to no sequence are not written.
  * total_query_tokens  <= num_seqs * max_query_tokens, else PA_ERR_INVALID_ARG.
- * max_query_tokens    the largest T_b; max_query_tokens * (q_heads /
- *               kv_heads) <= 16.
+ * max_query_tokens    the largest T_b (beyond 48 rows per (sequence, KV
+ *               head) the call runs on the prefill kernel, as pa_verify).
  * split_tokens  0 = the matrix-core default (pa_default_split_tokens with
  *               num_query_tokens >= 2), so a sequence's result does not depend
  *               on the other sequences of the call.

@@ -178,11 +178,21 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
                             max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype);
   if (st != PA_OK) return st;
   const int G = q_heads / kv_heads;
+  // Verify calls with more query rows per (sequence, KV head) than the
+  // matrix-core decode kernel's row tiles hold run on the prefill kernel, which
+  // has no row limit (and no pieces: each sequence's whole context in one
+  // workgroup per 128 rows).
+  const bool verify_on_prefill = is_verify && !pa::rows_supported(q_dtype, kv_dtype, head_dim, G, T);
   if (is_verify) {
-    if (!pa::rows_supported(q_dtype, kv_dtype, head_dim, G, T))
+    if (verify_on_prefill && !pa::prefill_supported(q_dtype, kv_dtype, head_dim))
       return fail(PA_ERR_UNSUPPORTED,
                   "verify not built for q=%d kv=%d head_dim=%d group=%d tokens=%d", q_dtype,
                   kv_dtype, head_dim, G, T);
+    if (verify_on_prefill && (long(T) * q_heads > 2147483647L ||
+                              long(num_seqs) * kv_heads *
+                                      ((long(T) * G + pa::prefill_rows_per_workgroup() - 1) /
+                                       pa::prefill_rows_per_workgroup()) > kMaxGrid))
+      return fail(PA_ERR_UNSUPPORTED, "too many query rows or workgroups");
   } else if (!pa::decode_group_supported(G)) {
     return fail(PA_ERR_UNSUPPORTED, "group size %d not built (1..8 or 16)", G);
   }
@@ -214,7 +224,7 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
                   work_plan_bytes);
   }
   if (num_seqs == 0) return PA_OK;
-  const size_t need = plan.total();
+  const size_t need = verify_on_prefill ? 0 : plan.total();
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu",
                 need, workspace ? workspace_bytes : size_t(0));
@@ -250,9 +260,18 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.query_start = vl.on ? vl.query_start : nullptr;
   a.plan = static_cast<const int32_t*>(work_plan);
   a.total_query_tokens = vl.on ? vl.total : num_seqs * T;
+  hipError_t e = hipSuccess;
+  if (verify_on_prefill) {
+    a.plan = nullptr;   // a decode-kernel plan orders other units
+    a.part_o = a.part_lse = nullptr;
+    a.split_tokens = 0;
+    a.max_pieces = 1;
+    e = pa::launch_prefill(a, s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "verify launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+  }
   // Verify calls, and decode over an int8 cache, run on the matrix cores.
   const bool rows = vl.on || rows_kernel(T, G, kv_dtype);
-  hipError_t e = hipSuccess;
   if (rows && app.on) {
     // The matrix-core kernel has no fused write: the cache write runs first,
     // then the same decode as pa_decode (identical results).
@@ -514,7 +533,7 @@ int pa_plan(const int32_t* block_tables, const int32_t* context_lens, int num_se
   // units (a unit's kv_heads workgroups are consecutive).
   const int G = q_heads / kv_heads;
   const int resident = rows_kernel(num_query_tokens, G, kv_dtype)
-                           ? pa::rows_pass1_resident(kv_dtype, head_dim)
+                           ? pa::rows_pass1_resident(kv_dtype, head_dim, num_query_tokens * G)
                            : pa::decode_pass1_resident(kv_dtype == PA_F32 ? PA_F32 : PA_BF16,
                                                        kv_dtype, head_dim, G);
   int dev = 0, cus = 0;

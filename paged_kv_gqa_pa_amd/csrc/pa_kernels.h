@@ -129,7 +129,7 @@ struct PlanArgs {
 
 // Workgroups of one attention kernel resident per CU (occupancy query).
 int decode_pass1_resident(int q_dtype, int kv_dtype, int head_dim, int G);
-int rows_pass1_resident(int kv_dtype, int head_dim);
+int rows_pass1_resident(int kv_dtype, int head_dim, int rows);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 
@@ -164,8 +164,10 @@ int prefill_rows_per_workgroup();
 hipError_t launch_reshape_and_cache(const CacheArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache_quant(const QuantCacheArgs& a, hipStream_t stream);
 hipError_t launch_decode_pass1(const DecodeArgs& a, bool append, hipStream_t stream);
-// Matrix-core kernel for R = T * G <= 16 query rows per (sequence, KV head):
-// every verify call, and decode over an int8 cache.
+// Matrix-core kernel for R = T * G <= 16 * kMaxRowTiles query rows per
+// (sequence, KV head), in row tiles of 16: verify calls, and decode over an
+// int8 cache or with bf16 groups of 4 or more query heads.
+constexpr int kMaxRowTiles = 3;
 hipError_t launch_rows_pass1(const DecodeArgs& a, hipStream_t stream);
 bool decode_group_supported(int G);
 bool rows_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T);

@@ -127,9 +127,16 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
   if (!planned) {
     tile = tiles - 1 - rank / a.num_seqs;
     b = rank % a.num_seqs;
-    const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
-    q0 = min(max(s0, 0), a.total_query_tokens);
-    T = min(max(s1 - s0, 0), min(a.num_query_tokens, a.total_query_tokens - q0));
+    if (a.query_start) {
+      const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
+      q0 = min(max(s0, 0), a.total_query_tokens);
+      T = min(max(s1 - s0, 0), min(a.num_query_tokens, a.total_query_tokens - q0));
+    } else {
+      // a fixed number of query tokens per sequence (a verify call with more
+      // rows than the decode kernels take)
+      T = a.num_query_tokens;
+      q0 = b * T;
+    }
     L = min(a.context_lens[b], max_len);
   }
   const int R = T * G;

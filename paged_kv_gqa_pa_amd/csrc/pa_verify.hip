@@ -40,7 +40,7 @@
 namespace pa {
 namespace {
 
-template <typename KV, int D, int NW, int NS>
+template <typename KV, int D, int NW, int NS, int RT>
 __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   constexpr bool kInt8 = __is_same(KV, i8_t);
   constexpr int ROWB = D * int(sizeof(KV));  // bytes per key row
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   constexpr int CPR = ROWB / 16;             // 16-byte chunks per key row
   constexpr int RPB = ROWB >= 256 ? 1 : 256 / ROWB;
   constexpr int SLOT = 2 * TILE_BYTES;       // one (K, V) tile pair
-  constexpr int OHALF = kRows / 2 * D * 4;   // O rows of one half
+  constexpr int OHALF = kRows / 2 * D * 4;   // O rows of one half of a row tile
   constexpr int WBYTES = SLOT > OHALF ? SLOT : OHALF;
   using M = MOps<KV>;
 
@@ -80,7 +80,8 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
     T = min(max(s1 - s0, 0), min(T, a.total_query_tokens - q0));
     if (T == 0) return;
   }
-  const int R = T * G;
+  const int R = T * G;   // at most 16 * RT (the launch picks RT)
+  const int L = it.L;
 
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;     // key row of an operand read / query row of S, P
@@ -88,39 +89,42 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   const int split_blocks = a.split_tokens / kBlockSize;
   const int blk_begin = piece * split_blocks;
 
-  const int t_row = n / G;
-  const int h_row = g * G + (n - t_row * G);
-  // Query rows as the B operand of score product c: lane (row n, group grp)
-  // holds q[n][32c + 8grp .. +7] (fp16 for an int8 cache).
-  u32x4 qb[NQ];
-  float qpart = 0.0f;
-  {
+  // Row tile i holds rows 16i .. 16i + 15.  Query rows as the B operand of
+  // score product c: lane (row n of tile i, group grp) holds
+  // q[16i + n][32c + 8grp .. +7] (fp16 for an int8 cache).
+  u32x4 qb[RT][NQ];
+  float qsum[RT];     // row n's sum of (fp16) q over all dims (int8 K bias)
+  int last_vis[RT];   // last position row n may see (rows past R see nothing)
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int row = kRows * i + n;
+    const bool row_ok = row < R;
+    const int t_row = row / G;
+    const int h_row = g * G + (row - t_row * G);
+    last_vis[i] = row_ok ? L - T + t_row : -1;
     const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) +
                        ((size_t(q0) + t_row) * Hq + h_row) * D + 8 * grp;
+    float qpart = 0.0f;
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-      const u32x4 w = n < R ? load16(qp + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 w = row_ok ? load16(qp + 32 * c) : u32x4{0u, 0u, 0u, 0u};
       if constexpr (kInt8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const f16x2 hp = to_f16x2(bf16_lo(w[e]), bf16_hi(w[e]));
-          qb[c][e] = __builtin_bit_cast(uint32_t, hp);
+          qb[i][c][e] = __builtin_bit_cast(uint32_t, hp);
           qpart += float(hp[0]) + float(hp[1]);
         }
       } else {
-        qb[c] = w;
+        qb[i][c] = w;
       }
     }
+    qsum[i] = kInt8 ? add_xor32(add_xor16(qpart)) : 0.0f;
   }
-  // Row n's sum of (fp16) q over all dims: the four groups of row n.
-  const float qsum = kInt8 ? add_xor32(add_xor16(qpart)) : 0.0f;
 
-  const int L = it.L;
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
   if (piece < 0 || piece >= n_pieces) return;
   const int blk_end = min(cdiv(L, kBlockSize), blk_begin + split_blocks);
-  // Last position row n may see (rows past R see nothing).
-  const int last_vis = n < R ? L - T + t_row : -1;
 
   const size_t head_blocks = size_t(g) * a.num_blocks;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
@@ -162,11 +166,16 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   }
   const f32x4 vinit = {M::kVInit, M::kVInit, M::kVInit, M::kVInit};
 
-  float m = kNegInf;   // reference maximum of row n (log2 units)
-  float lsum = 0.0f;   // this lane's share of row n's sum
-  f32x4 o[NT];
+  float m[RT], lsum[RT];   // reference maximum of row n of tile i (log2 units); this
+                           // lane's share of its sum
+  f32x4 o[RT][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RT; ++i) {
+    m[i] = kNegInf;
+    lsum[i] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Tiles are loaded straight into the wave's LDS ring: load c of a tile
   // fills 1 KiB of LDS, lane i writing 16 bytes at i * 16; the lane fetches
@@ -234,9 +243,12 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         }
       }
     }
-    // Scores of keys 4*grp .. 4*grp+3 for row n: product c takes key n's dims
-    // 32c + 8grp .. +7 as the A operand.
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    // Scores of keys 4*grp .. 4*grp+3 for row n of each row tile: product c
+    // takes key n's dims 32c + 8grp .. +7 as the A operand (read once for all
+    // row tiles).  Row tiles past R hold no rows (uniform per workgroup).
+    f32x4 s[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
       u32x4 kop;
@@ -247,46 +259,58 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
       } else {
         kop = *reinterpret_cast<const u32x4*>(sk + sw(n, 4 * c + grp));
       }
-      s = M::qk(kop, qb[c], s);
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+        if (i == 0 || kRows * i < R) s[i] = M::qk(kop, qb[i][c], s[i]);
     }
     const float ssc = sc * ks;
-    float tmax = kNegInf;
+    u32x2 pa[RT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int pos = blk * kBlockSize + 4 * grp + j;
-      const float x = (kInt8 ? s[j] - kI8Bias * qsum : s[j]) * ssc;
-      s[j] = pos <= last_vis ? x : kNegInf;
-      tmax = fmaxf(tmax, s[j]);
-    }
-    tmax = max_xor32(max_xor16(tmax));   // row n over the 16 keys of the tile
-    if (__builtin_amdgcn_ballot_w64(tmax > m + kSlack) != 0) {
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
-      m = mnew;
-      lsum *= alpha;
-      // O rows 4*grp + j take the factor of that row (held by lane 4*grp + j).
+    for (int i = 0; i < RT; ++i) {
+      if (i > 0 && kRows * i >= R) {
+        pa[i] = u32x2{0u, 0u};
+        continue;
+      }
+      float tmax = kNegInf;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float ar = __shfl(alpha, 4 * grp + j);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) o[t][j] *= ar;
+        const int pos = blk * kBlockSize + 4 * grp + j;
+        const float x = (kInt8 ? s[i][j] - kI8Bias * qsum[i] : s[i][j]) * ssc;
+        s[i][j] = pos <= last_vis[i] ? x : kNegInf;
+        tmax = fmaxf(tmax, s[i][j]);
       }
-    }
-    const float mref = m == kNegInf ? 0.0f : m;
-    float p[4];
+      tmax = max_xor32(max_xor16(tmax));   // row n over the 16 keys of the tile
+      if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
+        const float mnew = fmaxf(m[i], tmax);
+        const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
+        m[i] = mnew;
+        lsum[i] *= alpha;
+        // O rows 4*grp + j take the factor of that row (held by lane 4*grp + j).
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[j] - mref);
-    // P as the A operand (row n, keys 4*grp ..), bf16; an int8 tile's V scale
-    // rides on it.
-    const u32x2 pa = {pack_bf16_round(p[0] * vs, p[1] * vs), pack_bf16_round(p[2] * vs, p[3] * vs)};
-    // The row sum adds the weights as rounded for the P.V product (an int8 tile's
-    // divided by its V scale again), so numerator and denominator use one set of
-    // weights.
-    if constexpr (kInt8)
-      lsum = __builtin_fmaf(add_bf16_pair(pa[0], add_bf16_pair(pa[1], 0.0f)), __builtin_amdgcn_rcpf(vs), lsum);
-    else
-      lsum = add_bf16_pair(pa[0], add_bf16_pair(pa[1], lsum));
-    // V of keys 4*grp .. 4*grp+3 at dim 16t + n (the B operand).
+        for (int j = 0; j < 4; ++j) {
+          const float ar = __shfl(alpha, 4 * grp + j);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) o[i][t][j] *= ar;
+        }
+      }
+      const float mref = m[i] == kNegInf ? 0.0f : m[i];
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = fast_exp2(s[i][j] - mref);
+      // P as the A operand (row n, keys 4*grp ..), bf16; an int8 tile's V scale
+      // rides on it.
+      pa[i] = u32x2{pack_bf16_round(p[0] * vs, p[1] * vs), pack_bf16_round(p[2] * vs, p[3] * vs)};
+      // The row sum adds the weights as rounded for the P.V product (an int8
+      // tile's divided by its V scale again), so numerator and denominator use
+      // one set of weights.
+      if constexpr (kInt8)
+        lsum[i] = __builtin_fmaf(add_bf16_pair(pa[i][0], add_bf16_pair(pa[i][1], 0.0f)),
+                                 __builtin_amdgcn_rcpf(vs), lsum[i]);
+      else
+        lsum[i] = add_bf16_pair(pa[i][0], add_bf16_pair(pa[i][1], lsum[i]));
+    }
+    // V of keys 4*grp .. 4*grp+3 at dim 16t + n (the B operand), read once for
+    // all row tiles.
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       u32x2 vb;
@@ -298,7 +322,9 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
       } else {
         vb = v_operand_tr<ROWB>(sv, t, lane);   // four keys of one dim
       }
-      o[t] = pv16(pa, vb, o[t]);
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+        if (i == 0 || kRows * i < R) o[i][t] = pv16(pa[i], vb, o[i][t]);
     }
     // This slot is loaded again next: its reads must be done first.
     __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
@@ -332,45 +358,53 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
   __asm__ __volatile__("" ::: "memory");
 
-  // Row totals (the four key quads of each row); the wave's O rows go to its
-  // own LDS region (its staging buffers are no longer read), then the waves
-  // are merged.
-  const float lrow = add_xor32(add_xor16(lsum));
-  if (grp == 0) {
-    ml_of(wave)[n] = m;
-    ml_of(wave)[kRows + n] = lrow;
-  }
-  // O rows 0-7 go to the wave's slot-0 region, rows 8-15 to its slot-1 region.
-  float* const s_ow = reinterpret_cast<float*>(grp < 2 ? s_w0 : s_w1);
+  // Per row tile: row totals (the four key quads of each row), the wave's O
+  // rows to its own LDS region (its staging buffers are no longer read), then
+  // the waves are merged; a barrier before the next tile reuses the regions.
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s_ow[(4 * (grp & 1) + j) * D + 16 * t + n] = o[t][j];
-  __syncthreads();
-
-  for (int t = threadIdx.x; t < R * D; t += NW * kWave) {
-    const int row = t / D, d = t % D;
-    float mx = ml_of(0)[row];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, ml_of(w)[row]);
-    float lt = 0.0f, ot = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = ml_of(w)[row];
-      const float f = mw == kNegInf ? 0.0f : fast_exp2(mw - mx);
-      lt = __builtin_fmaf(ml_of(w)[kRows + row], f, lt);
-      const char* rb = (row < kRows / 2 ? s_ring0 : s_ring1) + w * WBYTES;
-      ot = __builtin_fmaf(reinterpret_cast<const float*>(rb)[(row % (kRows / 2)) * D + d], f, ot);
+  for (int i = 0; i < RT; ++i) {
+    if (i > 0 && kRows * i >= R) break;   // uniform per workgroup
+    if (i > 0) __syncthreads();
+    const float lrow = add_xor32(add_xor16(lsum[i]));
+    if (grp == 0) {
+      ml_of(wave)[n] = m[i];
+      ml_of(wave)[kRows + n] = lrow;
     }
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    const int tq = row / G;
-    const size_t orow = (size_t(q0) + tq) * Hq + size_t(g) * G + (row - tq * G);
-    if (n_pieces == 1) {
-      reinterpret_cast<bf16_t*>(a.out)[orow * D + d].bits = f32_to_bf16(ot * inv);
-    } else {
-      const size_t prow = orow * a.max_pieces + piece;
-      a.part_o[prow * D + d] = ot * inv;
-      if (d == 0) a.part_lse[prow] = lt > 0.0f ? mx + __log2f(lt) : kNegInf;
+    // O rows 0-7 of the tile go to the wave's slot-0 region, rows 8-15 to its
+    // slot-1 region.
+    float* const s_ow = reinterpret_cast<float*>(grp < 2 ? s_w0 : s_w1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_ow[(4 * (grp & 1) + j) * D + 16 * t + n] = o[i][t][j];
+    __syncthreads();
+
+    const int rows_here = min(R - kRows * i, kRows);
+    for (int t = threadIdx.x; t < rows_here * D; t += NW * kWave) {
+      const int rl = t / D, d = t % D;
+      float mx = ml_of(0)[rl];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, ml_of(w)[rl]);
+      float lt = 0.0f, ot = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = ml_of(w)[rl];
+        const float f = mw == kNegInf ? 0.0f : fast_exp2(mw - mx);
+        lt = __builtin_fmaf(ml_of(w)[kRows + rl], f, lt);
+        const char* rb = (rl < kRows / 2 ? s_ring0 : s_ring1) + w * WBYTES;
+        ot = __builtin_fmaf(reinterpret_cast<const float*>(rb)[(rl % (kRows / 2)) * D + d], f, ot);
+      }
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      const int row = kRows * i + rl;
+      const int tq = row / G;
+      const size_t orow = (size_t(q0) + tq) * Hq + size_t(g) * G + (row - tq * G);
+      if (n_pieces == 1) {
+        reinterpret_cast<bf16_t*>(a.out)[orow * D + d].bits = f32_to_bf16(ot * inv);
+      } else {
+        const size_t prow = orow * a.max_pieces + piece;
+        a.part_o[prow * D + d] = ot * inv;
+        if (d == 0) a.part_lse[prow] = lt > 0.0f ? mx + __log2f(lt) : kNegInf;
+      }
     }
   }
 }
@@ -383,45 +417,65 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
 #define PA_ROWS_SLOTS_INT8 2
 #endif
 template <typename KV> struct RowsSlots : std::integral_constant<int, 2> {};
+#ifndef PA_ROWS_WAVES
+#define PA_ROWS_WAVES 8
+#endif
 template <> struct RowsSlots<i8_t> : std::integral_constant<int, PA_ROWS_SLOTS_INT8> {};
 
-template <typename KV>
-hipError_t launch_rows_t(const DecodeArgs& a, hipStream_t stream) {
+// Row tiles per (sequence, KV head) for rows = T * G query rows.
+__host__ __device__ constexpr int row_tiles(long rows) { return int((rows + kRows - 1) / kRows); }
+
+template <typename KV, int RT>
+hipError_t launch_rows_rt(const DecodeArgs& a, hipStream_t stream) {
   // Eight waves per (piece, sequence, KV head): a long piece's tiles spread
   // over more waves, and with one such workgroup per CU (its LDS ring takes
   // 128 KiB for bf16, D = 128) later workgroups fill CUs as early ones finish.
   // Measured against four waves: verify 35.2 -> 33.4 us, Qwen2-shaped decode
   // 9.5 -> 9.2 us, long-context int8 equal at twice the piece length.
-#ifndef PA_ROWS_WAVES
-#define PA_ROWS_WAVES 8
-#endif
   constexpr int NW = PA_ROWS_WAVES;
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
   if (a.head_dim == 128)
-    rows_pass1<KV, 128, NW, RowsSlots<KV>::value><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    rows_pass1<KV, 128, NW, RowsSlots<KV>::value, RT><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   else
-    rows_pass1<KV, 64, NW, RowsSlots<KV>::value><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+    rows_pass1<KV, 64, NW, RowsSlots<KV>::value, RT><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <typename KV>
+hipError_t launch_rows_t(const DecodeArgs& a, hipStream_t stream) {
+  switch (row_tiles(long(a.num_query_tokens) * (a.q_heads / a.kv_heads))) {
+    case 1: return launch_rows_rt<KV, 1>(a, stream);
+    case 2: return launch_rows_rt<KV, 2>(a, stream);
+    case 3: return launch_rows_rt<KV, 3>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename KV, int D, int RT>
+int resident_rt() {
+  int n = 0;
+  constexpr int NW = PA_ROWS_WAVES;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &n, rows_pass1<KV, D, NW, RowsSlots<KV>::value, RT>, NW * kWave, 0);
+  return e == hipSuccess && n > 0 ? n : 1;
+}
+template <typename KV, int D>
+int resident_d(int rt) {
+  return rt <= 1 ? resident_rt<KV, D, 1>() : rt == 2 ? resident_rt<KV, D, 2>() : resident_rt<KV, D, 3>();
 }
 
 }  // namespace
 
 bool rows_supported(int q_dtype, int kv_dtype, int head_dim, int G, int T) {
   return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kI8) &&
-         (head_dim == 64 || head_dim == 128) && G >= 1 && T >= 1 && long(G) * T <= kRows;
+         (head_dim == 64 || head_dim == 128) && G >= 1 && T >= 1 &&
+         long(G) * T <= long(kRows) * kMaxRowTiles;
 }
 
-int rows_pass1_resident(int kv_dtype, int head_dim) {
-  int n = 0;
-  constexpr int NW = PA_ROWS_WAVES;
-  hipError_t e;
-  if (kv_dtype == kI8)
-    e = head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<i8_t, 64, NW, RowsSlots<i8_t>::value>, NW * kWave, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<i8_t, 128, NW, RowsSlots<i8_t>::value>, NW * kWave, 0);
-  else
-    e = head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<bf16_t, 64, NW, RowsSlots<bf16_t>::value>, NW * kWave, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows_pass1<bf16_t, 128, NW, RowsSlots<bf16_t>::value>, NW * kWave, 0);
-  return e == hipSuccess && n > 0 ? n : 1;
+int rows_pass1_resident(int kv_dtype, int head_dim, int rows) {
+  const int rt = row_tiles(rows);
+  if (kv_dtype == kI8) return head_dim == 64 ? resident_d<i8_t, 64>(rt) : resident_d<i8_t, 128>(rt);
+  return head_dim == 64 ? resident_d<bf16_t, 64>(rt) : resident_d<bf16_t, 128>(rt);
 }
 
 hipError_t launch_rows_pass1(const DecodeArgs& a, hipStream_t stream) {

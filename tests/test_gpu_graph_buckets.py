@@ -26,11 +26,11 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _caches(seed):
+def _caches(seed, hkv=HKV):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
-    kc = [torch.randn((HKV, NB, 16, D), generator=g, device="cuda").bfloat16() for _ in range(LAYERS)]
-    vc = [torch.randn((HKV, NB, 16, D), generator=g, device="cuda").bfloat16() for _ in range(LAYERS)]
+    kc = [torch.randn((hkv, NB, 16, D), generator=g, device="cuda").bfloat16() for _ in range(LAYERS)]
+    vc = [torch.randn((hkv, NB, 16, D), generator=g, device="cuda").bfloat16() for _ in range(LAYERS)]
     return kc, vc
 
 
@@ -64,17 +64,19 @@ def _eager(kc, vc, q, kn, vn, table, lens, slots, T, fused, scale):
     return outs
 
 
-@pytest.mark.parametrize("T,fused", [(1, False), (1, True), (5, False)])
-def test_bucketed_steps_match_eager(T, fused):
-    _say("bucketed step graphs T", T, "fused", fused)
+@pytest.mark.parametrize("T,fused,hq,hkv", [(1, False, HQ, HKV), (1, True, HQ, HKV),
+                                            (5, False, HQ, HKV),
+                                            (5, False, 12, 2)])   # Qwen2 heads: 30 rows per group
+def test_bucketed_steps_match_eager(T, fused, hq, hkv):
+    _say("bucketed step graphs T", T, "fused", fused, "heads", hq, hkv)
     spare = NB - 1
     scale = 1.0 / float(np.sqrt(D))
-    kc, vc = _caches(7)
+    kc, vc = _caches(7, hkv)
     kc_e = [k.clone() for k in kc]
     vc_e = [v.clone() for v in vc]
-    graphs = StepGraphs(kc, vc, HQ, MAXB, spare, scale, buckets=(1, 4, 16, 64),
+    graphs = StepGraphs(kc, vc, hq, MAXB, spare, scale, buckets=(1, 4, 16, 64),
                         num_query_tokens=T, fused=fused)
-    rng = np.random.default_rng(40 + T + int(fused))
+    rng = np.random.default_rng(40 + T + int(fused) + hq)
     for n in (1, 3, 16, 37):
         lens, table, slots = _batch(rng, n, T, spare)
         for step in range(2):
@@ -84,10 +86,10 @@ def test_bucketed_steps_match_eager(T, fused):
                                   for b in range(n) for p in range(int(lens[b]) - T, int(lens[b]))],
                                  np.int64)
             _say("  batch", n, "bucket", graphs.bucket_for(n), "step", step)
-            qshape = (n, HQ, D) if T == 1 else (n, T, HQ, D)
+            qshape = (n, hq, D) if T == 1 else (n, T, hq, D)
             q = [torch.randn(qshape, device="cuda").bfloat16() for _ in range(LAYERS)]
-            kn = [torch.randn((n * T, HKV, D), device="cuda").bfloat16() for _ in range(LAYERS)]
-            vn = [torch.randn((n * T, HKV, D), device="cuda").bfloat16() for _ in range(LAYERS)]
+            kn = [torch.randn((n * T, hkv, D), device="cuda").bfloat16() for _ in range(LAYERS)]
+            vn = [torch.randn((n * T, hkv, D), device="cuda").bfloat16() for _ in range(LAYERS)]
             want = _eager(kc_e, vc_e, q, kn, vn, table, lens, slots, T, fused, scale)
             got = graphs.step(q, kn, vn, dev(table), dev(lens), dev(slots))
             torch.cuda.synchronize()

@@ -58,7 +58,7 @@ def test_int8_poison_decode(G, split):
     assert err < TOL["int8"], err
 
 
-@pytest.mark.parametrize("G,T", [(2, 5), (3, 5)])
+@pytest.mark.parametrize("G,T", [(2, 5), (3, 5), (6, 5), (8, 5)])
 def test_int8_poison_verify(G, T):
     _say("int8 poison verify G", G, "T", T)
     case = _case(G, T, 50 + G)

@@ -154,7 +154,7 @@ def test_planned_decode_equals_unplanned_bitwise(tag, G, D):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "int8"])
-@pytest.mark.parametrize("G,T", [(2, 5), (3, 5), (1, 16)])
+@pytest.mark.parametrize("G,T", [(2, 5), (3, 5), (1, 16), (6, 5), (8, 5)])
 def test_planned_verify_equals_unplanned_bitwise(kv, G, T):
     _say("planned verify", kv, "G", G, "T", T)
     rng = np.random.default_rng(600 + G + T)

@@ -88,7 +88,10 @@ EDGE = [0, 1, 2, 3, 4, 5, 6, 15, 16, 17, 21, 33, 100, 255, 256, 257, 700]
 
 
 @pytest.mark.parametrize("kv", ["bf16", "int8"])
-@pytest.mark.parametrize("G,T", [(1, 1), (1, 16), (2, 5), (3, 5), (2, 8), (8, 2), (16, 1), (6, 2)])
+# up to 16 rows per (sequence, KV head): one row tile; 17..48: two or three row
+# tiles; beyond 48 the prefill kernel
+@pytest.mark.parametrize("G,T", [(1, 1), (1, 16), (2, 5), (3, 5), (2, 8), (8, 2), (16, 1), (6, 2),
+                                 (4, 5), (6, 5), (8, 5), (16, 3), (3, 17), (16, 5), (8, 16)])
 @pytest.mark.parametrize("D", [64, 128])
 def test_verify_edges(G, T, D, kv):
     _say("verify edges", kv, "G", G, "T", T, "D", D)
@@ -130,8 +133,27 @@ def test_verify_rows_match_decode_at_shorter_contexts():
 
 def test_verify_unsupported_shapes_rejected():
     rng = np.random.default_rng(3)
-    case = _random_verify_case(rng, [20], Hkv=1, G=4, D=128, T=5)   # 20 rows > 16
+    case = _random_verify_case(rng, [20], Hkv=1, G=4, D=96, T=5)   # head_dim 96 is not built
     dc = DevCase(case)
     with pytest.raises(pa.PAError) as ei:
         _verify(dc)
     assert ei.value.status == pa.PA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("G,T", [(6, 5), (8, 5), (16, 5)])
+def test_verify_many_rows_full_size(G, T, kv):
+    """The speculative workload's sequences (64, context U{256..1024} + T) with group
+    sizes whose rows fill two or three row tiles, or go to the prefill kernel (80 rows),
+    on a poisoned cache; every output row against the oracle."""
+    _say("verify many rows", kv, "G", G, "T", T)
+    spec = wl.CONFIGS["spec_verify_bf16"]
+    lens, _ = wl.structure(spec)
+    lens = (lens - spec.num_query_tokens + T).astype(np.int32)
+    rng = np.random.default_rng(1300 + G + T)
+    case = _random_verify_case(rng, lens[:32], Hkv=2, G=G, D=128, T=T, poison=True, kv=kv)
+    dc = DevCase(case)
+    want = _oracle_verify(case)
+    for split in (0, 256):
+        err = max_abs_err(_verify(dc, split), want, TOL[kv])
+        assert err < TOL[kv], (split, err)

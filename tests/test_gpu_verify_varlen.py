@@ -45,7 +45,7 @@ def _want(case, qp, qs, lens):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "int8"])
-@pytest.mark.parametrize("G,T", [(2, 5), (3, 5), (8, 2), (1, 16), (16, 1)])
+@pytest.mark.parametrize("G,T", [(2, 5), (3, 5), (8, 2), (1, 16), (16, 1), (6, 5), (8, 5), (16, 4)])
 @pytest.mark.parametrize("D", [64, 128])
 def test_varlen_edges(G, T, D, kv):
     """Counts 0..T per sequence (with lengths from 0 up), poisoned cache tails, one
@@ -124,9 +124,14 @@ def test_varlen_invalid_arguments():
     case = _random_verify_case(rng, [20, 30], Hkv=1, G=4, D=128, T=4)
     dc = DevCase(case)
     qp, qs, lens = _packed(case, [4, 4])
-    with pytest.raises(pa.PAError) as ei:      # 5 tokens x 4 heads > 16 rows
-        _run(case, dc, qp, qs, lens, 5)
+    case96 = _random_verify_case(rng, [20, 30], Hkv=1, G=4, D=96, T=4)
+    q96, qs96, lens96 = _packed(case96, [4, 4])
+    with pytest.raises(pa.PAError) as ei:      # head_dim 96 is not built
+        _run(case96, DevCase(case96), q96, qs96, lens96, 4)
     assert ei.value.status == pa.PA_ERR_UNSUPPORTED
+    # a larger max_query_tokens than any sequence uses (5 x 4 heads = 20 rows: two row
+    # tiles) gives the same rows
+    assert max_abs_err(_run(case, dc, qp, qs, lens, 5), _want(case, qp, qs, lens)) < TOL["bf16"]
     with pytest.raises(pa.PAError) as ei:      # 8 packed rows > 2 sequences x 3 tokens
         _run(case, dc, qp, qs, lens, 3)
     assert ei.value.status == pa.PA_ERR_INVALID_ARG
