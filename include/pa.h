@@ -50,11 +50,17 @@
  * Errors: each call returns a pa_status.  Argument errors are detected on the
  *   host before anything is enqueued; a failed launch returns PA_ERR_HIP.
  *   pa_last_error() returns a message for the calling thread's last failure.
- *   Device-side preconditions are NOT checked (the host cannot read device
- *   memory): block-table entries that are read must lie in [0, num_blocks),
+ *   Device-side preconditions (the host cannot read device memory):
+ *   block-table entries that are read lie in [0, num_blocks), 0 <=
  *   context_lens[b] <= min(max_context_len, max_blocks_per_seq * block_size),
- *   and slots must be < num_blocks * block_size.  Violating them reads or
- *   writes out of bounds.
+ *   slots are < num_blocks * block_size (or negative: skipped), and
+ *   query_start offsets are non-decreasing within [0, total_query_tokens].
+ *   The kernels clamp every index they form, so a violation gives an
+ *   unspecified result (e.g. positions past max_context_len are not attended
+ *   to) but never an access outside the buffers.  The release library does
+ *   not report violations; the debug library (libpa_debug.so, built with
+ *   PA_DEVICE_CHECKS=1, same ABI) records each kind in a per-GPU status word
+ *   that pa_device_check_status reads.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -79,6 +85,31 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2 } pa_dtype;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int pa_version(void);
+
+/*
+ * Device-side precondition checks (debug library only).  Bits of the status
+ * word: a block-table entry read outside [0, num_blocks); a context length
+ * below 0 or past max_blocks_per_seq * block_size; a context length past
+ * max_context_len (its positions beyond the pieces the grid covers are not
+ * attended to); a cache slot >= num_blocks * block_size; query_start offsets
+ * decreasing, past total_query_tokens or a sequence with more than
+ * max_query_tokens tokens.
+ */
+#define PA_CHECK_TABLE_ENTRY   1u
+#define PA_CHECK_CONTEXT_TABLE 2u
+#define PA_CHECK_CONTEXT_MAX   4u
+#define PA_CHECK_SLOT          8u
+#define PA_CHECK_QUERY_START   16u
+
+/*
+ * pa_device_check_status -- the current GPU's check status word: the OR of the
+ * PA_CHECK_* bits of every violation the library's kernels met since it was
+ * last cleared (clear != 0 clears it after the read).  Synchronises the
+ * device (hipDeviceSynchronize) and copies 4 bytes to the host: a debugging
+ * aid, not for a step loop.  The release library has no checks: it sets
+ * *flags = 0 and returns PA_ERR_UNSUPPORTED.
+ */
+int pa_device_check_status(unsigned* flags, int clear);
 
 /* Message describing the calling thread's most recent non-OK status. */
 const char* pa_last_error(void);

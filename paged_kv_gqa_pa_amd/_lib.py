@@ -18,12 +18,14 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIB_VARIANT=debug selects the build with device-side precondition checks.
+LIB_PATH = os.path.join(_HERE, "libpa_debug.so" if os.environ.get("PA_LIB_VARIANT") == "debug"
+                        else "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
 PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 
-EXPORTED = ["pa_version", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_quant",
+EXPORTED = ["pa_version", "pa_last_error", "pa_device_check_status", "pa_reshape_and_cache", "pa_reshape_and_cache_quant",
             "pa_default_split_tokens",
             "pa_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_decode_append", "pa_verify", "pa_verify_varlen",
             "pa_prefill", "pa_plan_size", "pa_plan", "pa_decode_planned",
@@ -54,6 +56,8 @@ def _load():
     lib.pa_version.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
+    lib.pa_device_check_status.restype = i
+    lib.pa_device_check_status.argtypes = [ctypes.POINTER(ctypes.c_uint), i]
     lib.pa_reshape_and_cache.restype = i
     lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.pa_reshape_and_cache_quant.restype = i
@@ -154,6 +158,19 @@ def _int8_scales(kvd, k_scale, v_scale, kv_heads, num_blocks):
 
 def version() -> int:
     return _load().pa_version()
+
+
+PA_CHECK_TABLE_ENTRY, PA_CHECK_CONTEXT_TABLE, PA_CHECK_CONTEXT_MAX = 1, 2, 4
+PA_CHECK_SLOT, PA_CHECK_QUERY_START = 8, 16
+
+
+def device_check_status(clear: bool = True) -> int:
+    """The debug library's status word (PA_CHECK_* bits of the preconditions violated
+    since the last clear); synchronises the device.  Raises PAError(PA_ERR_UNSUPPORTED)
+    with the release library, which checks nothing."""
+    flags = ctypes.c_uint(0)
+    _check(_load().pa_device_check_status(ctypes.byref(flags), int(bool(clear))))
+    return flags.value
 
 
 def default_split_tokens(q_heads: int, kv_heads: int, head_dim: int, kv_dtype: torch.dtype,

@@ -14,6 +14,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpa.so")
+# The same library with device-side precondition checks (PA_DEVICE_CHECKS).
+DEBUG_OUT = os.path.join(HERE, "libpa_debug.so")
+DEBUG_FLAGS = ["-DPA_DEVICE_CHECKS=1"]
 PROBE_OUT = os.path.join(HERE, "libpa_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -51,9 +54,10 @@ def _fresh(obj: str, src: str) -> bool:
     return all(os.path.getmtime(obj) > os.path.getmtime(d) for d in deps if os.path.exists(d))
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    if _fresh(obj, src) and not extra:
+def _compile(src: str, extra, objdir: str = None) -> str:
+    objdir = objdir or OBJDIR
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    if _fresh(obj, src) and (not extra or objdir != OBJDIR):
         return obj
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(HERE, "..", "include"),
            "-c", os.path.join(CSRC, src), "-o", obj]
@@ -74,16 +78,25 @@ def _link(objs, out):
 
 
 def build(verbose: bool = True, extra_flags=()) -> str:
-    """Compile every HIP source, link libpa.so and libpa_probe.so; returns libpa's path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
-    jobs = min(len(srcs), max(1, (os.cpu_count() or 2)))
+    """Compile every HIP source, link libpa.so, libpa_debug.so (device checks) and
+    libpa_probe.so; returns libpa's path.  PA_BUILD_SKIP_DEBUG=1 in the environment
+    leaves the debug library out (a development shortcut)."""
+    dbg_dir = os.path.join(OBJDIR, "debug")
+    os.makedirs(dbg_dir, exist_ok=True)
+    jobs_list = [(s, list(extra_flags), OBJDIR) for s in SOURCES + PROBE_SOURCES]
+    with_debug = os.environ.get("PA_BUILD_SKIP_DEBUG") != "1"
+    if with_debug:
+        jobs_list += [(s, list(extra_flags) + DEBUG_FLAGS, dbg_dir) for s in SOURCES]
+    jobs = min(len(jobs_list), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
-    _link(objs[:len(SOURCES)], OUT)
-    _link(objs[len(SOURCES):], PROBE_OUT)
+        objs = list(ex.map(lambda j: _compile(*j), jobs_list))
+    n = len(SOURCES)
+    _link(objs[:n], OUT)
+    _link(objs[n:n + len(PROBE_SOURCES)], PROBE_OUT)
+    if with_debug:
+        _link(objs[n + len(PROBE_SOURCES):], DEBUG_OUT)
     if verbose:
-        print(f"built {OUT} and {PROBE_OUT}")
+        print(f"built {OUT}, {PROBE_OUT}" + (f" and {DEBUG_OUT}" if with_debug else ""))
     return OUT
 
 

@@ -31,6 +31,8 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+unsigned* status_ptr();
+
 struct SplitPlan {
   int split_tokens = 0;
   int max_pieces = 1;
@@ -94,8 +96,13 @@ int plan_pieces(int num_seqs, int T, int q_heads, int kv_heads, int head_dim,
     return fail(PA_ERR_INVALID_ARG, "split_tokens %d must be a multiple of %d in [%d, %d]",
                 split_tokens, pa::kBlockSizeHost, pa::kBlockSizeHost, pa::kMaxSplitTokens);
   plan->split_tokens = st;
-  plan->max_pieces = max_context_len > 0 ? (max_context_len + st - 1) / st : 1;
-  const size_t rows = size_t(num_seqs) * T * q_heads;
+  plan->max_pieces = max_context_len > 0 ? int((long(max_context_len) + st - 1) / st) : 1;
+  const size_t rows = size_t(num_seqs) * T * q_heads;   // each factor < 2^31: fits
+  // partial outputs and log-sum-exps must be addressable: rows * pieces *
+  // (head_dim + 1) fp32 values (checked by division, so nothing wraps)
+  if (rows > 0 && size_t(plan->max_pieces) * (head_dim + 1) * sizeof(float) >
+                      (size_t(1) << 62) / rows)
+    return fail(PA_ERR_UNSUPPORTED, "workspace for these sizes exceeds 2^62 bytes");
   plan->o_bytes = round_up(rows * plan->max_pieces * head_dim * sizeof(float));
   plan->lse_bytes = round_up(rows * plan->max_pieces * sizeof(float));
   if (long(plan->max_pieces) * num_seqs * kv_heads > kMaxGrid)
@@ -173,6 +180,8 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   int st = plan_pieces(num_seqs, T, q_heads, kv_heads, head_dim, max_context_len, kv_dtype,
                        split_tokens, &plan, vl.on);
   if (st != PA_OK) return st;
+  if (app.on && kv_dtype == PA_INT8)
+    return fail(PA_ERR_UNSUPPORTED, "append into an int8 cache is not built");
   st = check_attention_args(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                             context_lens, num_seqs, kv_heads, block_size, num_blocks,
                             max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype);
@@ -197,8 +206,6 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
     return fail(PA_ERR_UNSUPPORTED, "group size %d not built (1..8 or 16)", G);
   }
   if (app.on) {
-    if (kv_dtype == PA_INT8)
-      return fail(PA_ERR_UNSUPPORTED, "append into an int8 cache is not built");
     if (num_seqs > 0 && (!app.key || !app.value || !app.slot_mapping))
       return fail(PA_ERR_INVALID_ARG, "null key, value or slot_mapping");
     if (!aligned(app.key, 16) || !aligned(app.value, 16) || !aligned(app.slot_mapping, 8))
@@ -259,6 +266,7 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.slot_mapping = app.slot_mapping;
   a.query_start = vl.on ? vl.query_start : nullptr;
   a.plan = static_cast<const int32_t*>(work_plan);
+  a.check_status = status_ptr();
   a.total_query_tokens = vl.on ? vl.total : num_seqs * T;
   hipError_t e = hipSuccess;
   if (verify_on_prefill) {
@@ -277,7 +285,7 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
     // then the same decode as pa_decode (identical results).
     pa::CacheArgs c{app.key, app.value, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
                     app.slot_mapping, num_seqs, kv_heads, num_blocks,
-                    head_dim * elem_size(kv_dtype)};
+                    head_dim * elem_size(kv_dtype), a.check_status};
     e = pa::launch_reshape_and_cache(c, s);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
   }
@@ -317,28 +325,52 @@ namespace {
 // the kernels receive.
 __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
 
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch_ptr[kMaxDevices] = {};
+#if PA_DEVICE_CHECKS
+// The device-check status word of a debug build (one per GPU).
+__device__ unsigned check_status_word;
+#endif
 
-// Device address of the current device's scratch array (looked up on the
-// first call on that device).
-int scratch_ptr(void** out) {
+constexpr int kMaxDevices = 64;
+std::mutex g_symbol_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+void* g_status_ptr[kMaxDevices] = {};
+
+// Device address of one of this file's device symbols on the current device,
+// looked up once per device (with that device current) and cached in
+// cache[device].
+int symbol_ptr(const void* symbol, void** cache, const char* what, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices)
     return fail(PA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_ptr[dev]) {
+  std::lock_guard<std::mutex> lock(g_symbol_mu);
+  if (!cache[dev]) {
     void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    e = hipGetSymbolAddress(&p, symbol);
     if (e != hipSuccess || !p)
-      return fail(PA_ERR_HIP, "scratch array address on device %d: %s", dev, hipGetErrorString(e));
-    g_scratch_ptr[dev] = p;
+      return fail(PA_ERR_HIP, "%s address on device %d: %s", what, dev, hipGetErrorString(e));
+    cache[dev] = p;
   }
-  *out = g_scratch_ptr[dev];
+  *out = cache[dev];
   return PA_OK;
+}
+
+int scratch_ptr(void** out) {
+  return symbol_ptr(HIP_SYMBOL(scratch), g_scratch_ptr, "scratch array", out);
+}
+
+// The status word the kernels of a debug build report to (nullptr in release
+// builds, whose kernels check nothing).
+unsigned* status_ptr() {
+#if PA_DEVICE_CHECKS
+  void* p = nullptr;
+  return symbol_ptr(&check_status_word, g_status_ptr, "check status word", &p) == PA_OK
+             ? static_cast<unsigned*>(p)
+             : nullptr;
+#else
+  return nullptr;
+#endif
 }
 
 }  // namespace
@@ -346,6 +378,27 @@ int scratch_ptr(void** out) {
 extern "C" {
 
 int pa_version(void) { return 100; }
+
+int pa_device_check_status(unsigned* flags, int clear) {
+  if (!flags) return fail(PA_ERR_INVALID_ARG, "null flags pointer");
+  *flags = 0;
+#if PA_DEVICE_CHECKS
+  void* p = nullptr;
+  int st = symbol_ptr(&check_status_word, g_status_ptr, "check status word", &p);
+  if (st != PA_OK) return st;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(flags, p, sizeof(unsigned), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    const unsigned zero = 0;
+    e = hipMemcpy(p, &zero, sizeof(unsigned), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "reading the check status word: %s", hipGetErrorString(e));
+  return PA_OK;
+#else
+  (void)clear;
+  return fail(PA_ERR_UNSUPPORTED, "device checks are not built into this library (libpa_debug.so has them)");
+#endif
+}
 
 const char* pa_last_error(void) { return g_err; }
 
@@ -362,7 +415,8 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_INT8)
     return fail(PA_ERR_INVALID_ARG, "unknown kv dtype %d", kv_dtype);
   if (num_tokens == 0) return PA_OK;
-  if (long(num_tokens) * kv_heads * head_dim * elem_size(kv_dtype) / 16 > kMaxGrid)
+  // 16-byte chunks of all rows (each factor below 2^31, so no product overflows)
+  if (long(num_tokens) * kv_heads > kMaxGrid / (head_dim * elem_size(kv_dtype) / 16))
     return fail(PA_ERR_UNSUPPORTED, "num_tokens * kv_heads * head_dim too large");
   if (!key || !value || !k_cache || !v_cache || !slot_mapping)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
@@ -370,7 +424,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
       !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
     return fail(PA_ERR_INVALID_ARG, "misaligned pointer argument");
   pa::CacheArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, kv_heads, num_blocks,
-                  head_dim * elem_size(kv_dtype)};
+                  head_dim * elem_size(kv_dtype), status_ptr()};
   hipError_t e = pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
   return PA_OK;
@@ -401,7 +455,7 @@ int pa_reshape_and_cache_quant(const void* key, const void* value, int8_t* k_cac
       !aligned(slot_mapping, 8))
     return fail(PA_ERR_INVALID_ARG, "misaligned pointer argument");
   pa::QuantCacheArgs a{key, value, k_cache, v_cache, k_scale, v_scale, slot_mapping,
-                       num_tokens, kv_heads, num_blocks, head_dim, in_dtype};
+                       num_tokens, kv_heads, num_blocks, head_dim, in_dtype, status_ptr()};
   hipError_t e = pa::launch_reshape_and_cache_quant(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
   return PA_OK;
@@ -684,6 +738,7 @@ int run_prefill(void* out, const void* q, const void* k_cache, const void* v_cac
   a.q_dtype = q_dtype;
   a.kv_dtype = kv_dtype;
   a.plan = static_cast<const int32_t*>(plan);
+  a.check_status = status_ptr();
   hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return PA_OK;

@@ -26,6 +26,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheArgs a) {
     const u32x4 k = load16(reinterpret_cast<const char*>(a.key) + src);
     const u32x4 v = load16(reinterpret_cast<const char*>(a.value) + src);
     const int64_t slot = a.slot_mapping[tok];
+    if (ch == 0 && g == 0) check(slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
     if (slot < 0 || slot >= int64_t(a.num_blocks) * kBlockSize) continue;
     const size_t dst = (size_t(g) * a.num_blocks * kBlockSize + size_t(slot)) * a.row_bytes +
                        size_t(ch) * 16;
@@ -91,6 +92,7 @@ __global__ __launch_bounds__(256) void requant_write_kernel(QuantCacheArgs a) {
   const int64_t sc = jc < a.num_tokens ? a.slot_mapping[jc] : -1;
   const int64_t slot = uint32_t(__builtin_amdgcn_readlane(int(sc), tok - cbase)) |
                        (int64_t(__builtin_amdgcn_readlane(int(sc >> 32), tok - cbase)) << 32);
+  if (threadIdx.x == 0 && tensor == 0) check(slot < nslots, kCheckSlot, a.check_status);
   if (slot < 0 || slot >= nslots) return;
   const int64_t blk = slot / kBlockSize;
   if (__builtin_amdgcn_ballot_w64(jc < tok && in_block(sc, blk)) != 0) return;

@@ -37,6 +37,7 @@
 #define PA_PPL2_MAX_G 4
 #endif
 
+
 namespace pa {
 namespace {
 
@@ -208,6 +209,8 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     // The last piece writes the new row into the cache (one key row: the
     // first LPK lanes of wave 0, PPL pieces each).  Only this workgroup uses
     // position L - 1, and it takes that row from registers, not the cache.
+    if (piece == n_pieces - 1 && threadIdx.x == 0)
+      check(slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
     if (piece == n_pieces - 1 && wave == 0 && r == 0 && slot >= 0 &&
         slot < int64_t(a.num_blocks) * kBlockSize) {
       const size_t dst = (size_t(g) * a.num_blocks * kBlockSize + size_t(slot)) * GE::ROWB;
@@ -244,7 +247,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // instruction stream, and so the wait counts, identical but reads nothing:
   // its buffer resource has zero records.
   auto fetch = [&](int blk, bool live, P (&kt)[LPB], P (&vt)[LPB]) {
-    const int phys = min(max(tab.at(blk - blk_begin), 0), a.num_blocks - 1);
+    const int entry = tab.at(blk - blk_begin);
+    if (lane == 0) check(!live || (entry >= 0 && entry < a.num_blocks), kCheckTableEntry, a.check_status);
+    const int phys = min(max(entry, 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * GE::TILE_BYTES;
     const int bytes = live ? GE::TILE_BYTES : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);
@@ -618,14 +623,24 @@ __global__ __launch_bounds__(256) void merge_pieces(MergeArgs a) {
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4
 #endif
-#ifndef PA_RING
-#define PA_RING 2
+
+
+// Register ring depth per shape: three tile buffers for bf16 groups of up to
+// two query heads (measured in one process on the same caches, batch-64
+// workload: 19.75 -> 19.56 us per launch; the 235 VGPRs still leave two
+// workgroups per CU), two elsewhere (a third buffer costs occupancy there).
+template <typename KV, int G>
+struct RingDepth : std::integral_constant<int, (__is_same(KV, bf16_t) && G <= 2) ? 3 : 2> {};
+#ifdef PA_RING
+#define PA_RING_OF(KV, G) PA_RING
+#else
+#define PA_RING_OF(KV, G) RingDepth<KV, G>::value
 #endif
 
 template <typename Q, typename KV, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, bool append, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;      // waves per workgroup
-  constexpr int kRing = PA_RING;           // tiles in flight per wave
+  constexpr int kRing = PA_RING_OF(KV, G); // tile buffers per wave
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
   if (append) {
     decode_pass1<Q, KV, D, G, NW, kRing, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
@@ -671,7 +686,7 @@ int resident_t() {
   int n = 0;
   constexpr int NW = PA_DECODE_WAVES;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, decode_pass1<Q, KV, D, G, NW, PA_RING, false>, NW * kWave, 0) != hipSuccess)
+          &n, decode_pass1<Q, KV, D, G, NW, PA_RING_OF(KV, G), false>, NW * kWave, 0) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }

@@ -118,6 +118,19 @@ __device__ __forceinline__ uint32_t f16pair_hi(uint32_t u) {  // bytes 2,3
 
 __device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Debug builds: record a violated precondition (ok == false) in the status
+// word; callers pass conditions that are uniform across the calling lanes and
+// call it from one lane.  Release builds: nothing.
+__device__ __forceinline__ void check(bool ok, unsigned bit, unsigned* status) {
+#if PA_DEVICE_CHECKS
+  if (!ok && status) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  (void)ok;
+  (void)bit;
+  (void)status;
+#endif
+}
+
 // The block-table entries of one piece, held across the wave: entry i of the
 // piece sits in element i / 64 of lane i % 64 (a vector value, so it stays in
 // registers).  NREG elements cover 64 * NREG blocks.
@@ -207,6 +220,10 @@ __device__ __forceinline__ WorkItem work_item(const DecodeArgs& a, PieceTable<NR
       it.piece = r.w < 0 ? -1 : min(r.y, a.max_pieces - 1);
       it.g = blockIdx.x - unit * a.kv_heads;
       it.L = min(max(r.z, 0), max_len);
+      if (threadIdx.x == 0) {
+        check(r.z >= 0 && r.z <= max_len, kCheckContextTable, a.check_status);
+        check(r.z <= a.max_pieces * a.split_tokens, kCheckContextMax, a.check_status);
+      }
       return it;
     }
   }
@@ -218,7 +235,12 @@ __device__ __forceinline__ WorkItem work_item(const DecodeArgs& a, PieceTable<NR
   const int begin = it.piece * sb;
   tab.load(a.block_tables + size_t(it.b) * a.max_blocks_per_seq, begin,
            min(a.max_blocks_per_seq, begin + sb), lane);
-  it.L = min(a.context_lens[it.b], max_len);
+  const int L_raw = a.context_lens[it.b];
+  it.L = min(L_raw, max_len);
+  if (threadIdx.x == 0) {
+    check(L_raw >= 0 && L_raw <= max_len, kCheckContextTable, a.check_status);
+    check(L_raw <= a.max_pieces * a.split_tokens, kCheckContextMax, a.check_status);
+  }
   return it;
 }
 

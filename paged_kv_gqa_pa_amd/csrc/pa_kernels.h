@@ -4,9 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Device-side precondition checks (a debug build, -DPA_DEVICE_CHECKS=1): a
+// kernel that meets a violated precondition sets its bit in the status word
+// whose address the launch passes (`check_status`) and goes on with the
+// clamped value it uses anyway; release builds compile the checks out.
+#ifndef PA_DEVICE_CHECKS
+#define PA_DEVICE_CHECKS 0
+#endif
+
 namespace pa {
 
 enum DType : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+
+// Status bits (the same values as the PA_CHECK_* constants of pa.h).
+constexpr unsigned kCheckTableEntry = 1u;     // a block-table entry read lies outside [0, num_blocks)
+constexpr unsigned kCheckContextTable = 2u;   // context_lens[b] < 0 or > max_blocks_per_seq * 16
+constexpr unsigned kCheckContextMax = 4u;     // context_lens[b] > max_context_len (pieces not launched)
+constexpr unsigned kCheckSlot = 8u;           // a cache slot >= num_blocks * 16
+constexpr unsigned kCheckQueryStart = 16u;    // query_start decreasing, past total, or above max tokens
 
 constexpr int kBlockSizeHost = 16;  // tokens per cache block
 constexpr int kMaxSplitTokens = 4096;  // a piece's table entries: kTabRegs per lane
@@ -22,6 +37,7 @@ struct CacheArgs {
   int kv_heads;
   int num_blocks;
   int row_bytes;  // head_dim * element size
+  unsigned* check_status;  // device checks (debug builds), else nullptr
 };
 
 struct QuantCacheArgs {
@@ -37,6 +53,7 @@ struct QuantCacheArgs {
   int num_blocks;
   int head_dim;
   int in_dtype;
+  unsigned* check_status;  // device checks (debug builds), else nullptr
 };
 
 struct DecodeArgs {
@@ -76,6 +93,7 @@ struct DecodeArgs {
   float scale;
   int q_dtype;
   int kv_dtype;
+  unsigned* check_status;  // device checks (debug builds), else nullptr
 };
 
 

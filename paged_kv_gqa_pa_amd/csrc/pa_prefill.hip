@@ -129,6 +129,9 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
     b = rank % a.num_seqs;
     if (a.query_start) {
       const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
+      if (threadIdx.x == 0)
+        check(s0 >= 0 && s1 >= s0 && s1 <= a.total_query_tokens && s1 - s0 <= a.num_query_tokens,
+              kCheckQueryStart, a.check_status);
       q0 = min(max(s0, 0), a.total_query_tokens);
       T = min(max(s1 - s0, 0), min(a.num_query_tokens, a.total_query_tokens - q0));
     } else {
@@ -137,7 +140,9 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
       T = a.num_query_tokens;
       q0 = b * T;
     }
-    L = min(a.context_lens[b], max_len);
+    const int L_raw = a.context_lens[b];
+    if (threadIdx.x == 0) check(L_raw >= 0 && L_raw <= max_len, kCheckContextTable, a.check_status);
+    L = min(L_raw, max_len);
   }
   const int R = T * G;
   const int row0 = tile * NW * WROWS;
@@ -242,7 +247,9 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
     for (int kb = 0; kb < KB; ++kb) {
       const int blk = st * KB + kb;
       const bool need = blk * kBlockSize < kend;
-      phys[kb] = need ? min(max(bt[readfirstlane(blk)], 0), a.num_blocks - 1) : 0;
+      const int entry = need ? bt[readfirstlane(blk)] : 0;
+      if (threadIdx.x == 0) check(entry >= 0 && entry < a.num_blocks, kCheckTableEntry, a.check_status);
+      phys[kb] = min(max(entry, 0), a.num_blocks - 1);
       if constexpr (kInt8) {
         // a block past the needed range is fully masked: any finite, nonzero
         // scale keeps its zero weights zero (the row sum divides by the V scale)

@@ -76,6 +76,9 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   int q0 = b * T;
   if (a.query_start) {
     const int s0 = a.query_start[b], s1 = a.query_start[b + 1];
+    if (threadIdx.x == 0)
+      check(s0 >= 0 && s1 >= s0 && s1 <= a.total_query_tokens && s1 - s0 <= T, kCheckQueryStart,
+            a.check_status);
     q0 = min(max(s0, 0), a.total_query_tokens);
     T = min(max(s1 - s0, 0), min(T, a.total_query_tokens - q0));
     if (T == 0) return;
@@ -194,7 +197,9 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
     src_off_v[c] = kSwizzleV ? src_off[c] : r * ROWB + 16 * (p ^ vswz<ROWB>(r));
   }
   auto fetch = [&](int blk, bool live, int slot, float& ks, float& vs) {
-    const int phys = min(max(tab.at(blk - blk_begin), 0), a.num_blocks - 1);
+    const int entry = tab.at(blk - blk_begin);
+    if (lane == 0) check(!live || (entry >= 0 && entry < a.num_blocks), kCheckTableEntry, a.check_status);
+    const int phys = min(max(entry, 0), a.num_blocks - 1);
     const size_t tile = (head_blocks + size_t(phys)) * TILE_BYTES;
     const int bytes = live ? TILE_BYTES : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + tile, bytes);
@@ -410,9 +415,10 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
 }
 
 // LDS ring slots per wave: two (with eight waves a bf16 ring fills 128 KiB).
-// int8 tiles are half the size, but four slots were measured slower on the
-// long-context workload (30.7 us against 29.4 us per call): as in the
-// vector-ALU decode, more tiles in flight per wave only add contention.
+// int8 tiles are half the size, but three and four slots were measured slower
+// on the long-context workload, in one process on the same caches (29.8 and
+// 30.3 us against 28.6 us per call; also with the refill issued before the
+// tile's arithmetic): more tiles in flight per wave only add contention.
 #ifndef PA_ROWS_SLOTS_INT8
 #define PA_ROWS_SLOTS_INT8 2
 #endif
