@@ -77,6 +77,18 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over groups of N consecutive lanes (N a power of two, N <= 16), by
+// the butterflies of group_sum.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, true));
+  if constexpr (N >= 4) x = fmaxf(x, __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, true));
+  if constexpr (N >= 8) x = fmaxf(x, __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, true));
+  if constexpr (N >= 16) x = fmaxf(x, __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, true));
+  static_assert(N <= 16, "group_max: at most one DPP row");
+  return x;
+}
+
 // Reduction over the lanes that share lane % S (S a power of two < 64): every
 // lane receives the result.  Within a row, rotations by S, 2S, ... < 16 gather
 // the lanes of stride S (a rotation sum over a cyclic group covers each member

@@ -364,8 +364,14 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   __asm__ __volatile__("" ::: "memory");
 
   // Per row tile: row totals (the four key quads of each row), the wave's O
-  // rows to its own LDS region (its staging buffers are no longer read), then
-  // the waves are merged; a barrier before the next tile reuses the regions.
+  // rows to its own LDS region (its staging buffers are no longer read); then
+  // one thread per row turns the waves' maxima and sums into one weight per
+  // wave (exp2(m_w - M) / total) and the row's output index, and every output
+  // element is a weighted sum of the waves' values, read in one batch.  A
+  // barrier before the next tile reuses the regions.
+  __shared__ float s_coef[NW][kRows];
+  __shared__ float s_lse[kRows];
+  __shared__ long long s_orow[kRows];
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
     if (i > 0 && kRows * i >= R) break;   // uniform per workgroup
@@ -385,30 +391,64 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
     __syncthreads();
 
     const int rows_here = min(R - kRows * i, kRows);
-    for (int t = threadIdx.x; t < rows_here * D; t += NW * kWave) {
-      const int rl = t / D, d = t % D;
-      float mx = ml_of(0)[rl];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, ml_of(w)[rl]);
-      float lt = 0.0f, ot = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = ml_of(w)[rl];
-        const float f = mw == kNegInf ? 0.0f : fast_exp2(mw - mx);
-        lt = __builtin_fmaf(ml_of(w)[kRows + rl], f, lt);
-        const char* rb = (rl < kRows / 2 ? s_ring0 : s_ring1) + w * WBYTES;
-        ot = __builtin_fmaf(reinterpret_cast<const float*>(rb)[(rl % (kRows / 2)) * D + d], f, ot);
-      }
+    // Row weights: lane w of each group of NW lanes in the first waves takes
+    // wave w's maximum and sum of row rl (rows past R included, they hold
+    // -inf and 0); the group reduces them with DPP.
+    static_assert(NW <= 16 && (NW & (NW - 1)) == 0, "weights use groups of NW lanes in one DPP row");
+    if (threadIdx.x < kRows * NW) {
+      const int rl = threadIdx.x / NW, w = threadIdx.x % NW;
+      const float mw = ml_of(w)[rl], lw = ml_of(w)[kRows + rl];
+      const float mx = group_max<NW>(mw);
+      const float f = mw == kNegInf ? 0.0f : fast_exp2(mw - mx);
+      const float lt = group_sum<NW>(lw * f);
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      const int row = kRows * i + rl;
-      const int tq = row / G;
-      const size_t orow = (size_t(q0) + tq) * Hq + size_t(g) * G + (row - tq * G);
-      if (n_pieces == 1) {
-        reinterpret_cast<bf16_t*>(a.out)[orow * D + d].bits = f32_to_bf16(ot * inv);
-      } else {
-        const size_t prow = orow * a.max_pieces + piece;
-        a.part_o[prow * D + d] = ot * inv;
-        if (d == 0) a.part_lse[prow] = lt > 0.0f ? mx + __log2f(lt) : kNegInf;
+      s_coef[w][rl] = f * inv;
+      if (w == 0 && rl < rows_here) {
+        s_lse[rl] = lt > 0.0f ? mx + __log2f(lt) : kNegInf;
+        const int row = kRows * i + rl;
+        const int tq = row / G;
+        s_orow[rl] = (long long)((size_t(q0) + tq) * Hq + size_t(g) * G + (row - tq * G));
+      }
+    }
+    __syncthreads();
+
+    // Two output elements per thread per pass, their LDS reads issued
+    // together (a row index past the tile is clamped for the read and not
+    // stored).
+    for (int t0 = threadIdx.x; t0 < rows_here * D; t0 += 2 * NW * kWave) {
+      float ot[2];
+      int rls[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = t0 + u * NW * kWave;
+        const int rl = min(t / D, kRows - 1), d = t % D;
+        rls[u] = t < rows_here * D ? rl : -1;
+        const int half = rl < kRows / 2 ? 0 : 1;
+        const int off = (rl % (kRows / 2)) * D + d;
+        float ow[NW], cw[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          cw[w] = s_coef[w][rl];
+          ow[w] = reinterpret_cast<const float*>((half ? s_ring1 : s_ring0) + w * WBYTES)[off];
+        }
+        float x = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x = __builtin_fmaf(ow[w], cw[w], x);
+        ot[u] = x;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int rl = rls[u];
+        if (rl < 0) continue;
+        const int d = (t0 + u * NW * kWave) % D;
+        const size_t orow = size_t(s_orow[rl]);
+        if (n_pieces == 1) {
+          reinterpret_cast<bf16_t*>(a.out)[orow * D + d].bits = f32_to_bf16(ot[u]);
+        } else {
+          const size_t prow = orow * a.max_pieces + piece;
+          a.part_o[prow * D + d] = ot[u];
+          if (d == 0) a.part_lse[prow] = s_lse[rl];
+        }
       }
     }
   }
