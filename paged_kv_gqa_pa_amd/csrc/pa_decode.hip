@@ -511,17 +511,26 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   const int Hq = a.q_heads;
   for (int t = threadIdx.x; t < G * D; t += NW * kWave) {
     const int h = t / D, d = t % D;
-    float M = s_m[0][h];
+    // Every LDS value this output needs, read in one batch.
+    float mw[NW], lw[NW], xw[NW][RG];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = s_m[w][h];
+      lw[w] = s_l[w][h];
+#pragma unroll
+      for (int j = 0; j < RG; ++j) xw[w][j] = s_acc[w][j][h][d];
+    }
+    float M = mw[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, mw[w]);
     float lsum = 0.0f, o = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = s_m[w][h] == kNegInf ? 0.0f : fast_exp2(s_m[w][h] - M);
-      lsum = __builtin_fmaf(s_l[w][h], f, lsum);
-      float x = s_acc[w][0][h][d];
+      const float f = mw[w] == kNegInf ? 0.0f : fast_exp2(mw[w] - M);
+      lsum = __builtin_fmaf(lw[w], f, lsum);
+      float x = xw[w][0];
 #pragma unroll
-      for (int j = 1; j < RG; ++j) x += s_acc[w][j][h][d];
+      for (int j = 1; j < RG; ++j) x += xw[w][j];
       o = __builtin_fmaf(x, f, o);
     }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
