@@ -1,10 +1,13 @@
 """Benchmark: batch-64 paged GQA decode step over 28 layer caches on one MI355X.
 
-One step = for each of 28 layers: pa_reshape_and_cache of one new K/V token
-per sequence, then pa_decode of one query token per sequence (64 sequences,
-16 query / 8 KV heads, head_dim 128, bf16, block size 16, context = 256-token
-prompt + U{1..256} generated tokens, a shuffled pool of 16384 blocks per
-layer, one shared block table).  Each step first makes one work plan
+One step = for each of 28 layers: the new K/V token of every sequence written
+into that layer's cache, then decode attention of one query token per sequence
+over the context that includes it (64 sequences, 16 query / 8 KV heads,
+head_dim 128, bf16, block size 16, context = 256-token prompt + U{1..256}
+generated tokens, a shuffled pool of 16384 blocks per layer, one shared block
+table).  The timed step runs each layer as one pa_decode_append launch (the
+write and the decode in one kernel); the same step as pa_reshape_and_cache +
+pa_decode (two launches per layer) is timed beside it.  Each step first makes one work plan
 (pa_plan: the step's (sequence, piece) units ordered longest first, shared by
 the 28 layers); ``--no-plan`` starts the work in the natural order instead.
 The step is captured once in a HIP graph and replayed (the pages' change 4:
@@ -89,16 +92,19 @@ def attention_bytes(lens, T, q_heads, kv_heads, head_dim, kv_elem, q_elem=2):
     return kv + qo + blocks * 4 + len(lens) * 4 + scales
 
 
-def bucket_timing(torch, pa, kc, vc, qs, nks, nvs, bt, cl, sm, table, scale, reps, sizes=(1, 8, 64)):
-    """The batch-64 step (pa_plan + 28 x (write + decode)) captured per batch-size bucket
-    by StepGraphs, for batches of the first n sequences; µs per step from graph replays
-    (inputs copied in once; each replay rewrites the same new-token slots)."""
+def bucket_timing(torch, pa, kc, vc, qs, nks, nvs, bt, cl, sm, table, scale, reps, sizes=(1, 8, 64),
+                  fused=True):
+    """The batch-64 step (pa_plan + 28 x write + decode: one pa_decode_append launch per
+    layer, or with fused=False pa_reshape_and_cache + pa_decode) captured per batch-size
+    bucket by StepGraphs, for batches of the first n sequences; µs per step from graph
+    replays (inputs copied in once; each replay rewrites the same new-token slots)."""
     from paged_kv_gqa_pa_amd.graphs import StepGraphs
     NB = kc[0].shape[1]
     used = np.zeros(NB, bool)
     used[table[table >= 0]] = True
     spare = int(np.flatnonzero(~used)[-1])
-    sg = StepGraphs(kc, vc, qs[0].shape[1], table.shape[1], spare, scale, buckets=sizes)
+    sg = StepGraphs(kc, vc, qs[0].shape[1], table.shape[1], spare, scale, buckets=sizes,
+                    fused=fused)
     out = {}
     for n in sizes:
         sg.step([q[:n] for q in qs], [k[:n] for k in nks], [v[:n] for v in nvs], bt[:n], cl[:n],
@@ -114,8 +120,8 @@ def bucket_timing(torch, pa, kc, vc, qs, nks, nvs, bt, cl, sm, table, scale, rep
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         out[str(n)] = {"us_per_step": round(us, 1), "tokens_per_s": round(n / (us * 1e-6), 1)}
-        print(f"[bench] step graph, batch {n}: {us:.1f} us/step, {n / (us * 1e-6):.0f} tokens/s",
-              flush=True)
+        print(f"[bench] step graph{'' if fused else ' (write, then decode)'}, batch {n}: "
+              f"{us:.1f} us/step, {n / (us * 1e-6):.0f} tokens/s", flush=True)
     del sg
     return out
 
@@ -704,33 +710,31 @@ def main():
         print("[bench] calibration copy: 256 MiB read + 256 MiB written", flush=True)
         del src, dst
 
-    # Whole step: K steps between events (one before each step and one after the
-    # last), synchronised on both sides; the total gives the mean, the gaps the
-    # per-step median, min and max.
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    ev[0].record()
-    for i in range(args.steps):
-        run_step()
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
-    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    tok_s = N / (ms_step / 1e3)
-    print(f"[bench] step {ms_step * 1e3:.1f} us", flush=True)
+    # Whole step: W untimed steps, then K steps between events (one before each
+    # step and one after the last), synchronised on both sides; the total gives
+    # the mean, the gaps the per-step median, min and max.
+    def timed_steps(run):
+        for _ in range(max(1, args.warmup)):
+            run()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record()
+        for i in range(args.steps):
+            run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return (ev[0].elapsed_time(ev[-1]) / args.steps,
+                sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)))
 
-    # The same step through pa_decode_append (write + decode in one launch).
-    for _ in range(max(1, args.warmup)):
-        run_fused()
-    torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record()
-    for _ in range(args.steps):
-        run_fused()
-    f1.record()
-    torch.cuda.synchronize()
-    ms_fused = f0.elapsed_time(f1) / args.steps
-    print(f"[bench] fused step {ms_fused * 1e3:.1f} us", flush=True)
+    # The step: per layer, pa_decode_append writes the new token's K and V into
+    # the layer's cache and attends over the context that includes it (one launch).
+    ms_step, per_step = timed_steps(run_fused)
+    tok_s = N / (ms_step / 1e3)
+    print(f"[bench] step (write + decode in one launch per layer) {ms_step * 1e3:.1f} us", flush=True)
+    # The same step as two launches per layer: pa_reshape_and_cache, then pa_decode.
+    ms_split, per_split = timed_steps(run_step)
+    print(f"[bench] step (pa_reshape_and_cache + pa_decode per layer) {ms_split * 1e3:.1f} us",
+          flush=True)
 
     # Decode kernel alone: back-to-back launches over the 28 layers (distinct caches,
     # 2.8 GB per pass, far beyond the 256 MB last-level cache), events on the launch stream.
@@ -809,7 +813,9 @@ def main():
     buckets = None
     if not args.no_buckets:
         buckets = bucket_timing(torch, pa, kc, vc, qs, nks, nvs, bt, cl, sm, table, scale,
-                                args.decode_reps)
+                                args.decode_reps, fused=True)
+        buckets["write_then_decode"] = bucket_timing(torch, pa, kc, vc, qs, nks, nvs, bt, cl, sm,
+                                                     table, scale, args.decode_reps, fused=False)
 
     traffic = None
     if os.path.exists(args.traffic_file):
@@ -839,13 +845,17 @@ def main():
         "config": {"workload": WORKLOAD, "num_seqs": N, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "block_size": 16, "layers": Lyr, "num_blocks_per_layer": NB,
                    "context": "256 + U{1..256} (new token included)",
-                   "step": ("28 x (reshape_and_cache + decode)" if plan is None else
-                            "pa_plan + 28 x (reshape_and_cache + decode with the plan)"),
+                   "step": ("" if plan is None else "pa_plan + ") +
+                           "28 x pa_decode_append (per layer: the new token's K/V written into "
+                           "the cache and attention over the context that includes it, one launch)",
                    "launch": "eager" if args.eager else "hipgraph",
                    "split_tokens": args.split or pa.default_split_tokens(Hq, Hkv, D, torch.bfloat16)},
-        "fused_step": {"ms_per_step": round(ms_fused, 4), "tokens_per_s": round(N / (ms_fused / 1e3), 1),
-                       "entry_point": "pa_decode_append (cache write + decode in one launch)" +
-                                      ("" if plan is None else ", after one pa_plan per step")},
+        "write_then_decode_step": {
+            "ms_per_step": round(ms_split, 4), "tokens_per_s": round(N / (ms_split / 1e3), 1),
+            "step_ms": {"median": round(per_split[len(per_split) // 2], 4),
+                        "min": round(per_split[0], 4), "max": round(per_split[-1], 4)},
+            "entry_points": "28 x (pa_reshape_and_cache + pa_decode)" +
+                            ("" if plan is None else ", after one pa_plan per step")},
         "hbm_gbps": round(gbps, 1),
         "pct_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
