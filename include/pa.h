@@ -264,9 +264,10 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
 
 /*
  * pa_decode_append -- pa_reshape_and_cache of one new token per sequence
- * followed by pa_decode, in one launch where pa_decode runs on the vector
- * ALUs (fp32, bf16 groups below 4 query heads per KV head); elsewhere the
- * cache-write launch and then the matrix-core decode, with pa_decode's result.
+ * followed by pa_decode, in one launch (the kernel pa_decode would run for
+ * the shape: vector ALUs for fp32 and bf16 groups below 4 query heads per KV
+ * head, matrix cores for larger bf16 groups), with pa_decode's result bit for
+ * bit.
  *
  * key, value     [num_seqs, kv_heads, head_dim], kv_dtype: the new token of
  *                each sequence, written to slot_mapping[b] (skipped when

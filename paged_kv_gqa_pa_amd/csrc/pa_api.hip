@@ -278,17 +278,10 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
     if (e != hipSuccess) return fail(PA_ERR_HIP, "verify launch failed: %s", hipGetErrorString(e));
     return PA_OK;
   }
-  // Verify calls, and decode over an int8 cache, run on the matrix cores.
+  // Verify calls, decode over an int8 cache and bf16 decode with large groups
+  // run on the matrix cores; both kernels take the fused cache write (bf16 and
+  // fp32 caches; int8 append was refused above).
   const bool rows = vl.on || rows_kernel(T, G, kv_dtype);
-  if (rows && app.on) {
-    // The matrix-core kernel has no fused write: the cache write runs first,
-    // then the same decode as pa_decode (identical results).
-    pa::CacheArgs c{app.key, app.value, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
-                    app.slot_mapping, num_seqs, kv_heads, num_blocks,
-                    head_dim * elem_size(kv_dtype), a.check_status};
-    e = pa::launch_reshape_and_cache(c, s);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
-  }
   e = rows ? pa::launch_rows_pass1(a, s) : pa::launch_decode_pass1(a, app.on, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pass-1 launch failed: %s", hipGetErrorString(e));
   if (plan.max_pieces > 1) {

@@ -40,7 +40,7 @@
 namespace pa {
 namespace {
 
-template <typename KV, int D, int NW, int NS, int RT>
+template <typename KV, int D, int NW, int NS, int RT, bool AP = false>
 __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   constexpr bool kInt8 = __is_same(KV, i8_t);
   constexpr int ROWB = D * int(sizeof(KV));  // bytes per key row
@@ -85,6 +85,19 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   }
   const int R = T * G;   // at most 16 * RT (the launch picks RT)
   const int L = it.L;
+  // Decode with append (AP, bf16 caches): lane k < CPR of every wave holds
+  // 16-byte chunk k of the new token's K and V rows (position L - 1) and its slot.
+  constexpr bool append = AP && !kInt8;
+  u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+  int64_t new_slot = -1;
+  if constexpr (append) {
+    if (lane < CPR) {
+      const size_t off = (size_t(b) * a.kv_heads + g) * ROWB + 16 * size_t(lane);
+      nk = load16(reinterpret_cast<const char*>(a.new_k) + off);
+      nv = load16(reinterpret_cast<const char*>(a.new_v) + off);
+    }
+    new_slot = a.slot_mapping[b];
+  }
 
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;     // key row of an operand read / query row of S, P
@@ -128,6 +141,24 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
   if (piece < 0 || piece >= n_pieces) return;
   const int blk_end = min(cdiv(L, kBlockSize), blk_begin + split_blocks);
+  // The tile holding position L - 1 takes that row from the input (below); the
+  // last piece's wave 0 also writes it into the cache slot (slots < 0 are
+  // skipped, slots past the pool ignored).  Only this workgroup uses the
+  // position, so no other reader waits on the write.
+  const int blk_new = append && L > 0 ? (L - 1) / kBlockSize : -1;
+  if constexpr (append) {
+    if (piece == n_pieces - 1) {
+      if (threadIdx.x == 0)
+        check(new_slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
+      if (wave == 0 && lane < CPR && new_slot >= 0 &&
+          new_slot < int64_t(a.num_blocks) * kBlockSize) {
+        const size_t dst =
+            (size_t(g) * a.num_blocks * kBlockSize + size_t(new_slot)) * ROWB + 16 * lane;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + dst) = nk;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + dst) = nv;
+      }
+    }
+  }
 
   const size_t head_blocks = size_t(g) * a.num_blocks;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
@@ -233,7 +264,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
     // The tile's LDS writes are counted with the vector-memory loads.
     __builtin_amdgcn_s_waitcnt((PENDING & 15) | ((PENDING >> 4) << 14) | (7 << 4) | (15 << 8));
     __asm__ __volatile__("" ::: "memory");
-    const char* const sk = kbuf(slot);
+    char* const sk = kbuf(slot);
     char* const sv = vbuf(slot);
     // bf16 key rows past the context may hold anything, even NaN: their V rows
     // are cleared (a zero weight must meet a finite value); their scores are
@@ -246,6 +277,13 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
           if (blk * kBlockSize + key >= L)
             *reinterpret_cast<u32x4*>(sv + 1024 * c + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
         }
+      }
+      // Append: the staged row of position L - 1 is replaced by the input row,
+      // chunk k at its swizzled place in the K and in the V tile.
+      if (append && blk == blk_new && lane < CPR) {
+        const int r = (L - 1) % kBlockSize;
+        *reinterpret_cast<u32x4*>(sk + r * ROWB + 16 * (lane ^ ((r / RPB) & (CPR - 1)))) = nk;
+        *reinterpret_cast<u32x4*>(sv + r * ROWB + 16 * (lane ^ vswz<ROWB>(r))) = nv;
       }
     }
     // Scores of keys 4*grp .. 4*grp+3 for row n of each row tile: product c
@@ -480,6 +518,19 @@ hipError_t launch_rows_rt(const DecodeArgs& a, hipStream_t stream) {
   // 9.5 -> 9.2 us, long-context int8 equal at twice the piece length.
   constexpr int NW = PA_ROWS_WAVES;
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
+  if (a.new_k) {
+    // Decode with append: one query token per sequence, bf16 cache, groups of
+    // at most 16 heads (one row tile); the host refuses other shapes.
+    if constexpr (RT == 1 && !__is_same(KV, i8_t)) {
+      if (a.head_dim == 128)
+        rows_pass1<KV, 128, NW, RowsSlots<KV>::value, 1, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+      else
+        rows_pass1<KV, 64, NW, RowsSlots<KV>::value, 1, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (a.head_dim == 128)
     rows_pass1<KV, 128, NW, RowsSlots<KV>::value, RT><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
   else

@@ -343,8 +343,38 @@ def test_decode_append_equals_write_then_decode_bitwise():
     assert max_abs_err(out, _oracle_decode(case)) < TOL["bf16"]
 
 
+@pytest.mark.parametrize("planned", [False, True])
+def test_decode_append_matrix_core_equals_write_then_decode_bitwise(planned):
+    """Qwen2-shaped layer (G = 6, bf16: the matrix-core kernel): one launch gives the
+    two calls' output bits and cache bytes, with and without a work plan."""
+    _say("decode_append qwen2 shape, planned", planned)
+    case = wl.build_case("qwen2_1p5b_bf16")
+    two, one = DevCase(case), DevCase(case)
+    plan = None
+    if planned:
+        plan = pa.make_plan(two.block_tables, two.context_lens, case.spec.q_heads,
+                            case.spec.kv_heads, case.spec.head_dim, case.max_context_len,
+                            torch.bfloat16)
+    pa.reshape_and_cache(two.new_k, two.new_v, two.k_cache, two.v_cache, two.slot_mapping)
+    ref = torch.empty_like(two.q)
+    pa.decode(ref, two.q, two.k_cache, two.v_cache, two.block_tables, two.context_lens,
+              case.scale, case.max_context_len, plan=plan)
+    out = torch.empty_like(one.q)
+    pa.decode_append(out, one.q, one.new_k, one.new_v, one.k_cache, one.v_cache,
+                     one.slot_mapping, one.block_tables, one.context_lens, case.scale,
+                     case.max_context_len, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    want_k, want_v = oracle.reshape_and_cache(case.new_k, case.new_v, case.k_cache,
+                                              case.v_cache, case.slot_mapping)
+    assert host_bits(one.k_cache).tobytes() == want_k.tobytes()
+    assert host_bits(one.v_cache).tobytes() == want_v.tobytes()
+    case.k_cache, case.v_cache = want_k, want_v
+    assert max_abs_err(out, _oracle_decode(case)) < TOL["bf16"]
+
+
 @pytest.mark.parametrize("tag", ["f32", "bf16"])
-@pytest.mark.parametrize("G", [1, 2, 6])
+@pytest.mark.parametrize("G", [1, 2, 4, 6, 8])
 @pytest.mark.parametrize("split", [0, 32])
 def test_decode_append_edges(tag, G, split):
     _say("decode_append edges", tag, "G", G, "split", split)

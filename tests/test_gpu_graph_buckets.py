@@ -65,6 +65,7 @@ def _eager(kc, vc, q, kn, vn, table, lens, slots, T, fused, scale):
 
 
 @pytest.mark.parametrize("T,fused,hq,hkv", [(1, False, HQ, HKV), (1, True, HQ, HKV),
+                                            (1, True, 12, 2),     # fused on the matrix cores
                                             (5, False, HQ, HKV),
                                             (5, False, 12, 2)])   # Qwen2 heads: 30 rows per group
 def test_bucketed_steps_match_eager(T, fused, hq, hkv):
