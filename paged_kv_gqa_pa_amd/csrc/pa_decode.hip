@@ -12,9 +12,10 @@
 // (16 bytes each), so a load holds KPL = 64 / LPK key rows and a tile takes
 // LPB = 16 / KPL loads.  A key's score for one head is a sum over its LPK
 // lanes (DPP butterflies inside 16-lane rows).  Each lane keeps its own
-// online-softmax state for the key rows it sees (one per load), so the
-// per-tile work needs no cross-row exchange; rows, then waves, are merged
-// once at the end.
+// running sum and accumulator for the key rows it sees (one per load), so the
+// per-tile work needs no cross-row exchange; the reference maximum is one per
+// wave (raised rarely, see below), so at the end the rows of a wave add up
+// as they are, and then the waves are merged.
 //
 // With a single piece the workgroup writes the output row directly.  With
 // several pieces it writes a normalised partial output and its log2-sum-exp
@@ -265,10 +266,11 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   // anything, even NaN, and a zero weight must meet a finite value.
   //
   // Delayed rescaling: m is a reference maximum, not necessarily the running
-  // one.  Weights are exp2(s - m); the accumulator is rescaled only when some
-  // score of the wave exceeds its lane's reference by more than kSlack (log2
-  // units), so weights stay below 2^kSlack in fp32 and the rescale (one
-  // multiply per accumulator element) almost never runs.  The final
+  // one, and the same in every lane of the wave.  Weights are exp2(s - m); the
+  // accumulator is rescaled only when some score of the wave exceeds the
+  // reference by more than kSlack (log2 units), and then the reference becomes
+  // the wave's maximum, so weights stay below 2^kSlack in fp32 and the rescale
+  // (one multiply per accumulator element) almost never runs.  The final
   // normalisation by the running sum makes the result independent of m.
   constexpr float kSlack = 8.0f;
   auto process = [&](auto mask_tag, int blk, P (&kt)[LPB], P (&vt)[LPB]) {
@@ -319,6 +321,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
         float smax = s[h][0];
 #pragma unroll
         for (int k = 1; k < KR; ++k) smax = fmaxf(smax, s[h][k]);
+        smax = stride_max<LPK>(smax);   // over the wave's key rows: one reference per wave
         const float mnew = fmaxf(m[h], smax);
         const float alpha = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mnew);
         m[h] = mnew;
@@ -448,11 +451,14 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     }
   }
 
-  // Merge the key rows of this wave (lanes c, c + LPK, c + 2 LPK, ...): all
-  // rows are brought to the wave's running max, then the accumulators are
-  // reduce-scattered over lane ^ 32 and lane ^ 16 (each swap step halves the
-  // values a lane holds), and the row groups left inside a 16-lane row are
-  // summed with the other waves through LDS.
+  // Merge the key rows of this wave (lanes c, c + LPK, c + 2 LPK, ...): they
+  // share the wave's reference maximum, so the sums add as they are and the
+  // accumulators are reduce-scattered over lane ^ 32 and lane ^ 16 (each swap
+  // step halves the values a lane holds); the row groups left inside a
+  // 16-lane row are summed with the other waves through LDS.  (A reference per
+  // lane, brought to the wave's maximum here, put one more reduction, an exp2
+  // and a multiply per accumulator value on the launch's last workgroup:
+  // 0.15 us per launch on the batch-64 workload, same process and caches.)
   constexpr int V = G * E;                                   // accumulator values per lane
   constexpr int X32 = LPK <= 32 ? 2 : 1, X16 = LPK <= 16 ? 2 : 1;
   constexpr int KEEP = V / (X32 * X16);                      // values a lane keeps
@@ -460,12 +466,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   float red[V];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mw = stride_max<LPK>(m[h]);
-    const float f = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mw);
-    l[h] = stride_sum<LPK>(l[h] * f);
-    m[h] = mw;
+    l[h] = stride_sum<LPK>(l[h]);
 #pragma unroll
-    for (int e = 0; e < E; ++e) red[h * E + e] = acc[h][e] * f;
+    for (int e = 0; e < E; ++e) red[h * E + e] = acc[h][e];
   }
   if constexpr (X32 == 2) {
     // Lanes 0-31 keep the reduced first half of the values, lanes 32-63 the second.
