@@ -87,6 +87,71 @@ __device__ __forceinline__ u32x2 v_operand_tr(const char* sv, int t, int lane) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Byte offset of an LDS location inside the workgroup's LDS (p points into a
+// __shared__ object).
+typedef __attribute__((address_space(3))) const char* lds_cptr_t;
+__device__ __forceinline__ uint32_t lds_offset(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_cptr_t)p;
+}
+
+// The LDS address v_operand_tr reads for output block t.
+template <int ROWB>
+__device__ __forceinline__ uint32_t v_tr_addr(const char* sv, int t, int lane) {
+  const int r = lane >> 2;
+  const int k = 2 * t + ((lane & 3) >> 1);
+  return lds_offset(sv + r * ROWB + 16 * (k ^ vswz<ROWB>(r)) + 8 * (lane & 1));
+}
+
+// N transposed LDS reads (the operands of v_operand_tr at the given
+// addresses) in one asm block that waits for them before it ends, so no read
+// is left in flight when the block's outputs are handed back.  The builtin
+// form cannot be used here: the compiler's waits for it do not tell a staged
+// tile from the ring slot that direct-to-LDS loads are still filling, and it
+// waited for every outstanding load (the next tile's too) before each tile's
+// first transposed read.  The caller has already waited for the tile's own
+// loads.
+template <int N>
+__device__ __forceinline__ void lds_read_tr(const uint32_t (&a)[N], u32x2 (&v)[N]);
+template <>
+__device__ __forceinline__ void lds_read_tr<2>(const uint32_t (&a)[2], u32x2 (&v)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1])
+      : "v"(a[0]), "v"(a[1])
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_tr<4>(const uint32_t (&a)[4], u32x2 (&v)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_tr<8>(const uint32_t (&a)[8], u32x2 (&v)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 // Two fp32 values as fp16, rounded to nearest even (values past fp16's range
 // become infinite).
 __device__ __forceinline__ f16x2 to_f16x2(float lo, float hi) {

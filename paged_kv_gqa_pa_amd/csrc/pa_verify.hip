@@ -353,7 +353,14 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         lsum[i] = add_bf16_pair(pa[i][0], add_bf16_pair(pa[i][1], lsum[i]));
     }
     // V of keys 4*grp .. 4*grp+3 at dim 16t + n (the B operand), read once for
-    // all row tiles.
+    // all row tiles.  bf16: the NT transposed reads in one batch.
+    u32x2 vbt[NT];
+    if constexpr (!kInt8) {
+      uint32_t va[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) va[t] = v_tr_addr<ROWB>(sv, t, lane);
+      lds_read_tr<NT>(va, vbt);
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       u32x2 vb;
@@ -363,7 +370,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         const f32x4 tv = M::mm16(u32x2{f16pair_lo(u), f16pair_hi(u)}, ident, vinit);
         vb = u32x2{pack_bf16_exact(tv[0], tv[1]), pack_bf16_exact(tv[2], tv[3])};
       } else {
-        vb = v_operand_tr<ROWB>(sv, t, lane);   // four keys of one dim
+        vb = vbt[t];   // four keys of one dim
       }
 #pragma unroll
       for (int i = 0; i < RT; ++i)
