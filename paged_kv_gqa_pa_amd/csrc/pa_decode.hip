@@ -310,19 +310,21 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
           for (int w = 0; w < 4; ++w) vt[k * PPL + p][w] = valid ? vt[k * PPL + p][w] : 0u;
       }
     }
+    // One comparison per head: the lane's largest score against its reference.
+    float smax[G];
     bool grow = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      smax[h] = s[h][0];
 #pragma unroll
-      for (int k = 0; k < KR; ++k) grow |= s[h][k] > m[h] + kSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+      for (int k = 1; k < KR; ++k) smax[h] = fmaxf(smax[h], s[h][k]);
+      grow |= smax[h] > m[h] + kSlack;
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {  // wave-uniform, rare
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float smax = s[h][0];
-#pragma unroll
-        for (int k = 1; k < KR; ++k) smax = fmaxf(smax, s[h][k]);
-        smax = stride_max<LPK>(smax);   // over the wave's key rows: one reference per wave
-        const float mnew = fmaxf(m[h], smax);
+        // over the wave's key rows: one reference per wave
+        const float mnew = fmaxf(m[h], stride_max<LPK>(smax[h]));
         const float alpha = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mnew);
         m[h] = mnew;
         l[h] *= alpha;

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
                            fmaxf(fmaxf(r[4], r[5]), fmaxf(r[6], r[7])));
         rmax = max_xor32(max_xor16(rmax));
         const float tmax = rmax * sc_pos;   // -inf stays -inf: sc_pos > 0
-        if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
           const float mnew = fmaxf(m[i], tmax);
           const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
           m[i] = mnew;
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
         float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         tmax = max_xor32(max_xor16(tmax));
-        if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
           const float mnew = fmaxf(m[i], tmax);
           const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
           m[i] = mnew;

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         tmax = fmaxf(tmax, s[i][j]);
       }
       tmax = max_xor32(max_xor16(tmax));   // row n over the 16 keys of the tile
-      if (__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
         const float mnew = fmaxf(m[i], tmax);
         const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
         m[i] = mnew;
