@@ -206,23 +206,6 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   const int L = it.L;
   const int n_pieces = min(L > 0 ? cdiv(L, a.split_tokens) : 1, a.max_pieces);
   if (piece < 0 || piece >= n_pieces) return;
-  if constexpr (APPEND) {
-    // The last piece writes the new row into the cache (one key row: the
-    // first LPK lanes of wave 0, PPL pieces each).  Only this workgroup uses
-    // position L - 1, and it takes that row from registers, not the cache.
-    if (piece == n_pieces - 1 && threadIdx.x == 0)
-      check(slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
-    if (piece == n_pieces - 1 && wave == 0 && r == 0 && slot >= 0 &&
-        slot < int64_t(a.num_blocks) * kBlockSize) {
-      const size_t dst = (size_t(g) * a.num_blocks * kBlockSize + size_t(slot)) * GE::ROWB;
-#pragma unroll
-      for (int p = 0; p < PPL; ++p) {
-        const size_t off = dst + size_t(p) * (GE::ROWB / PPL) + size_t(c) * GE::PB;
-        *reinterpret_cast<P*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + off) = nk[p];
-        *reinterpret_cast<P*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + off) = nv[p];
-      }
-    }
-  }
 
   const int blk_end = min(cdiv(L, kBlockSize), blk_begin + split_blocks);
   const size_t head_blocks = size_t(g) * a.num_blocks;
@@ -449,6 +432,26 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
           process(Plain{}, tile(j + v), kb[v], vb[v]);
         else
           process(Masked{}, tile(j + v), kb[v], vb[v]);
+      }
+    }
+  }
+
+  if constexpr (APPEND) {
+    // The last piece writes the new row into the cache (one key row: the
+    // first LPK lanes of wave 0, PPL pieces each).  Only this workgroup uses
+    // position L - 1, and it took that row from registers, not the cache, so
+    // the store waits until the tile loop is done: issued before the loop it
+    // held wave 0's first tile loads back until the new row had arrived.
+    if (piece == n_pieces - 1 && threadIdx.x == 0)
+      check(slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
+    if (piece == n_pieces - 1 && wave == 0 && r == 0 && slot >= 0 &&
+        slot < int64_t(a.num_blocks) * kBlockSize) {
+      const size_t dst = (size_t(g) * a.num_blocks * kBlockSize + size_t(slot)) * GE::ROWB;
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        const size_t off = dst + size_t(p) * (GE::ROWB / PPL) + size_t(c) * GE::PB;
+        *reinterpret_cast<P*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + off) = nk[p];
+        *reinterpret_cast<P*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + off) = nv[p];
       }
     }
   }

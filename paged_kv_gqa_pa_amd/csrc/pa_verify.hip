@@ -142,23 +142,10 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   if (piece < 0 || piece >= n_pieces) return;
   const int blk_end = min(cdiv(L, kBlockSize), blk_begin + split_blocks);
   // The tile holding position L - 1 takes that row from the input (below); the
-  // last piece's wave 0 also writes it into the cache slot (slots < 0 are
-  // skipped, slots past the pool ignored).  Only this workgroup uses the
-  // position, so no other reader waits on the write.
+  // last piece's wave 0 also writes it into the cache slot after its tile
+  // loop (slots < 0 are skipped, slots past the pool ignored).  Only this
+  // workgroup uses the position, so no other reader waits on the write.
   const int blk_new = append && L > 0 ? (L - 1) / kBlockSize : -1;
-  if constexpr (append) {
-    if (piece == n_pieces - 1) {
-      if (threadIdx.x == 0)
-        check(new_slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
-      if (wave == 0 && lane < CPR && new_slot >= 0 &&
-          new_slot < int64_t(a.num_blocks) * kBlockSize) {
-        const size_t dst =
-            (size_t(g) * a.num_blocks * kBlockSize + size_t(new_slot)) * ROWB + 16 * lane;
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + dst) = nk;
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + dst) = nv;
-      }
-    }
-  }
 
   const size_t head_blocks = size_t(g) * a.num_blocks;
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
@@ -407,6 +394,22 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   // wait for it before the slots are reused below.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
   __asm__ __volatile__("" ::: "memory");
+
+  if constexpr (append) {
+    // (after the loop: issued before it, the store held wave 0's first tile
+    // loads back until the new row had arrived)
+    if (piece == n_pieces - 1) {
+      if (threadIdx.x == 0)
+        check(new_slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
+      if (wave == 0 && lane < CPR && new_slot >= 0 &&
+          new_slot < int64_t(a.num_blocks) * kBlockSize) {
+        const size_t dst =
+            (size_t(g) * a.num_blocks * kBlockSize + size_t(new_slot)) * ROWB + 16 * lane;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + dst) = nk;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + dst) = nv;
+      }
+    }
+  }
 
   // Per row tile: row totals (the four key quads of each row), the wave's O
   // rows to its own LDS region (its staging buffers are no longer read); then
