@@ -187,19 +187,23 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
   qr.load(qrow, c);
 
   // Append mode: this lane's pieces of the new token's K and V (position
-  // L - 1), and its slot.
+  // L - 1), and its slot.  Requested after the first tiles' loads (below):
+  // requested before them, every wait for a tile also waited for these rows
+  // (20.47 -> 20.21 us per batch-64 launch, same process).
   P nk[PPL], nv[PPL];
   int64_t slot = -1;
-  if constexpr (APPEND) {
-    const size_t row = (size_t(b) * a.kv_heads + g) * GE::ROWB;
+  auto load_new = [&]() {
+    if constexpr (APPEND) {
+      const size_t row = (size_t(b) * a.kv_heads + g) * GE::ROWB;
 #pragma unroll
-    for (int p = 0; p < PPL; ++p) {
-      const size_t off = row + size_t(p) * (GE::ROWB / PPL) + size_t(c) * GE::PB;
-      nk[p] = *reinterpret_cast<const P*>(reinterpret_cast<const char*>(a.new_k) + off);
-      nv[p] = *reinterpret_cast<const P*>(reinterpret_cast<const char*>(a.new_v) + off);
+      for (int p = 0; p < PPL; ++p) {
+        const size_t off = row + size_t(p) * (GE::ROWB / PPL) + size_t(c) * GE::PB;
+        nk[p] = *reinterpret_cast<const P*>(reinterpret_cast<const char*>(a.new_k) + off);
+        nv[p] = *reinterpret_cast<const P*>(reinterpret_cast<const char*>(a.new_v) + off);
+      }
+      slot = a.slot_mapping[b];
     }
-    slot = a.slot_mapping[b];
-  }
+  };
 
   // Lengths beyond the table are clamped so that no access leaves the
   // buffers (the result of such a call is unspecified).
@@ -413,6 +417,7 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     P kb[RING][LPB], vb[RING][LPB];
 #pragma unroll
     for (int v = 0; v < RING - 1; ++v) fetch(tile(v), v <= last, kb[v], vb[v]);
+    load_new();
     int j = 0;
     for (; j + RING - 1 < n_plain; j += RING) {
 #pragma unroll
@@ -434,6 +439,8 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
           process(Masked{}, tile(j + v), kb[v], vb[v]);
       }
     }
+  } else {
+    load_new();   // no tiles here; wave 0 may still write the new row
   }
 
   if constexpr (APPEND) {
@@ -442,6 +449,9 @@ __global__ __launch_bounds__(NW * kWave, NW >= 8 ? (NW * 2) / 4 : 1) void decode
     // position L - 1, and it took that row from registers, not the cache, so
     // the store waits until the tile loop is done: issued before the loop it
     // held wave 0's first tile loads back until the new row had arrived.
+    // (Issued inside the loop, or as a streaming or write-through store, it
+    // measured no faster, or slower: the ~0.7 us this store adds to a
+    // batch-64 launch is the memory side's cost of 2048 scattered lines.)
     if (piece == n_pieces - 1 && threadIdx.x == 0)
       check(slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
     if (piece == n_pieces - 1 && wave == 0 && r == 0 && slot >= 0 &&
