@@ -94,10 +94,11 @@ def attention_bytes(lens, T, q_heads, kv_heads, head_dim, kv_elem, q_elem=2):
 
 def bucket_timing(torch, pa, kc, vc, qs, nks, nvs, bt, cl, sm, table, scale, reps, sizes=(1, 8, 64),
                   fused=True):
-    """The batch-64 step (pa_plan + 28 x write + decode: one pa_decode_append launch per
-    layer, or with fused=False pa_reshape_and_cache + pa_decode) captured per batch-size
-    bucket by StepGraphs, for batches of the first n sequences; µs per step from graph
-    replays (inputs copied in once; each replay rewrites the same new-token slots)."""
+    """The batch-64 step (28 x write + decode: one pa_decode_append launch per layer, or
+    with fused=False pa_reshape_and_cache + pa_decode; a pa_plan first in the buckets
+    whose units outnumber the CUs, StepGraphs' default) captured per batch-size bucket by
+    StepGraphs, for batches of the first n sequences; µs per step from graph replays
+    (inputs copied in once; each replay rewrites the same new-token slots)."""
     from paged_kv_gqa_pa_amd.graphs import StepGraphs
     NB = kc[0].shape[1]
     used = np.zeros(NB, bool)
