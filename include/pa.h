@@ -420,7 +420,8 @@ int pa_verify_planned(void* out, const void* q, const void* k_cache, const void*
  *               not checked by the host; out-of-range offsets are clamped so
  *               that nothing outside q / out is touched).  Rows of out that
  *               belong to no sequence are not written.
- * total_query_tokens  <= num_seqs * max_query_tokens, else PA_ERR_INVALID_ARG.
+ * total_query_tokens  <= num_seqs * max_query_tokens, else PA_ERR_INVALID_ARG;
+ *               0: nothing is read or written (out and q may be NULL).
  * max_query_tokens    the largest T_b (beyond 48 rows per (sequence, KV
  *               head) the call runs on the prefill kernel, as pa_verify).
  * split_tokens  0 = the matrix-core default (pa_default_split_tokens with
@@ -446,7 +447,7 @@ int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* 
  * query_start[b] new tokens are its last T_b positions (their K/V already in
  * the cache, e.g. by pa_reshape_and_cache), query token t attends to positions
  * 0 .. context_lens[b] - T_b + t -- without its limit on rows: any
- * max_query_tokens, any group size.  Each workgroup covers 64 query rows
+ * max_query_tokens, any group size.  Each workgroup covers 128 query rows
  * (token, head) of one (sequence, KV head) over their whole visible context,
  * so there are no pieces and no workspace.
  *
@@ -455,6 +456,8 @@ int pa_verify_varlen(void* out, const void* q, const void* k_cache, const void* 
  *               sequence are not written).
  * query_start   [num_seqs + 1] int32 device offsets (clamped on the device to
  *               [0, total_query_tokens] and to max_query_tokens per sequence).
+ * total_query_tokens  <= num_seqs * max_query_tokens, else PA_ERR_INVALID_ARG;
+ *               0: nothing is read or written (out and q may be NULL).
  * max_query_tokens  the largest T_b (sets the grid).
  * Supported: PA_BF16 q with a PA_BF16 or PA_INT8 cache (k_scale / v_scale
  * for int8); head_dim 64 or 128; block_size 16.  Other arguments as

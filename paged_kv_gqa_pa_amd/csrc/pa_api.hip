@@ -124,7 +124,7 @@ int check_attention_args(void* out, const void* q, const void* k_cache, const vo
                          const int32_t* block_tables, const int32_t* context_lens,
                          int num_seqs, int kv_heads, int block_size, int num_blocks,
                          int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
-                         int kv_dtype) {
+                         int kv_dtype, bool no_rows = false) {
   if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", block_size);
   if (num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARG, "num_blocks (%d) and max_blocks_per_seq (%d) must be > 0",
@@ -141,7 +141,8 @@ int check_attention_args(void* out, const void* q, const void* k_cache, const vo
     return fail(PA_ERR_UNSUPPORTED, "dtype pair q=%d kv=%d not built", q_dtype, kv_dtype);
   }
   if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (num_seqs == 0) return PA_OK;
+  // nothing to read or write: the (empty) arrays may be NULL
+  if (num_seqs == 0 || no_rows) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (kv_dtype == PA_INT8 && (!k_scale || !v_scale))
@@ -182,9 +183,14 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   if (st != PA_OK) return st;
   if (app.on && kv_dtype == PA_INT8)
     return fail(PA_ERR_UNSUPPORTED, "append into an int8 cache is not built");
+  if (vl.on && (vl.total < 0 || long(vl.total) > long(num_seqs) * T))
+    return fail(PA_ERR_INVALID_ARG,
+                "total_query_tokens %d must be in [0, num_seqs * max_query_tokens = %ld]",
+                vl.total, long(num_seqs) * T);
   st = check_attention_args(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                             context_lens, num_seqs, kv_heads, block_size, num_blocks,
-                            max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype);
+                            max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
+                            vl.on && vl.total == 0);
   if (st != PA_OK) return st;
   const int G = q_heads / kv_heads;
   // Verify calls with more query rows per (sequence, KV head) than the
@@ -211,15 +217,9 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
     if (!aligned(app.key, 16) || !aligned(app.value, 16) || !aligned(app.slot_mapping, 8))
       return fail(PA_ERR_INVALID_ARG, "misaligned key, value or slot_mapping");
   }
-  if (vl.on) {
-    if (vl.total < 0 || long(vl.total) > long(num_seqs) * T)
-      return fail(PA_ERR_INVALID_ARG,
-                  "total_query_tokens %d must be in [0, num_seqs * max_query_tokens = %ld]",
-                  vl.total, long(num_seqs) * T);
-    if (num_seqs > 0 && (!vl.query_start || !aligned(vl.query_start, 4)))
-      return fail(PA_ERR_INVALID_ARG, "query_start must be a 4-byte aligned pointer");
-    if (vl.total == 0) return PA_OK;
-  }
+  if (vl.on && num_seqs > 0 && (!vl.query_start || !aligned(vl.query_start, 4)))
+    return fail(PA_ERR_INVALID_ARG, "query_start must be a 4-byte aligned pointer");
+  if (vl.on && vl.total == 0) return PA_OK;
   if (work_plan) {
     const size_t pb = plan_bytes_for(num_seqs, plan);
     if (pb == 0)
@@ -681,14 +681,15 @@ int run_prefill(void* out, const void* q, const void* k_cache, const void* v_cac
   if (!pa::prefill_supported(q_dtype, kv_dtype, head_dim))
     return fail(PA_ERR_UNSUPPORTED, "prefill not built for q=%d kv=%d head_dim=%d", q_dtype,
                 kv_dtype, head_dim);
-  int st = check_attention_args(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
-                                context_lens, num_seqs, kv_heads, block_size, num_blocks,
-                                max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype);
-  if (st != PA_OK) return st;
   if (total_query_tokens < 0 || long(total_query_tokens) > long(num_seqs) * max_query_tokens)
     return fail(PA_ERR_INVALID_ARG,
                 "total_query_tokens %d must be in [0, num_seqs * max_query_tokens = %ld]",
                 total_query_tokens, long(num_seqs) * max_query_tokens);
+  int st = check_attention_args(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                context_lens, num_seqs, kv_heads, block_size, num_blocks,
+                                max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
+                                total_query_tokens == 0);
+  if (st != PA_OK) return st;
   const int G = q_heads / kv_heads;
   const long rows = long(max_query_tokens) * G;
   const long per_wg = pa::prefill_rows_per_workgroup();

@@ -115,6 +115,27 @@ def test_decode_group_size_and_workspace_checked_before_launch():
     assert st == pa.PA_OK, msg
 
 
+def test_empty_packed_calls_need_no_arrays():
+    """Variable-length verify and prefill with no query rows read and write nothing:
+    NULL q and out are accepted (an empty tensor has no storage); a negative or too
+    large total is still rejected first."""
+    lib = pa.lib()
+    for name in ("pa_verify_varlen", "pa_prefill"):
+        fn = getattr(lib, name)
+
+        def call(total, out=None, q=None):
+            args = [out, q, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 3, total, 5, 4, 2, 128,
+                    16, 64, 8, 128, ctypes.c_float(0.1), pa.PA_BF16, pa.PA_BF16]
+            if name == "pa_verify_varlen":
+                args += [0, None, 0]
+            return fn(*args, None)
+
+        assert call(0) == pa.PA_OK, lib.pa_last_error().decode()
+        assert call(-1) == pa.PA_ERR_INVALID_ARG
+        assert call(16) == pa.PA_ERR_INVALID_ARG            # > num_seqs * max_query_tokens
+        assert call(4) == pa.PA_ERR_INVALID_ARG             # rows to compute, NULL arrays
+
+
 def test_cache_write_rejects_invalid_arguments():
     lib = pa.lib()
 
