@@ -237,11 +237,48 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
             del out[name]["frac"]
         print(f"[bench] {name}: {us:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}%), "
               f"{R} replicas x {alg / 1e6:.1f} MB per rotation", flush=True)
+        if name != "tiny_fp32":
+            out[name]["read_pattern"] = read_pattern_timing(torch, kc, vc, bt, cl, spec.max_len,
+                                                            split, R, cycles, reps, us)
         del kc, vc, g
         torch.cuda.empty_cache()
     out["int8_requant_write"] = requant_write_timing(torch, pa, dev, reps)
     out["chunked_prefill_bf16"] = prefill_timing(torch, pa, dev, reps)
     return out
+
+
+def read_pattern_timing(torch, kc, vc, bt, cl, max_len, split, R, cycles, reps, us_call):
+    """The call's own K/V tile reads without arithmetic (libpa_probe's tile_read: the same
+    units, pieces and tiles in the natural order, nothing computed or written) over the
+    same replicas, with four and with eight waves per workgroup: the read pattern's own
+    time, against which the attention call (pass 1 and, with pieces, the merge) is set."""
+    from paged_kv_gqa_pa_amd import _probe as probe
+    sink = torch.zeros(1, dtype=torch.int32, device=bt.device)
+    res = {}
+    for waves in (4, 8):
+        def reads():
+            for r in [r for _ in range(cycles) for r in range(R)]:
+                probe.tile_read(kc[r], vc[r], bt, cl, max_len, split, sink, waves=waves)
+        reads()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            reads()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{waves}_waves_us"] = round(e0.elapsed_time(e1) * 1e3 / (reps * R * cycles), 2)
+        del g
+    best = min(res.values())
+    res["call_over_best_pattern_us"] = round(us_call - best, 2)
+    print(f"[bench]   its tile reads alone: {res['4_waves_us']:.2f} us (4 waves), "
+          f"{res['8_waves_us']:.2f} us (8 waves)", flush=True)
+    return res
 
 
 def prefill_timing(torch, pa, dev, reps=10, calls=8):
