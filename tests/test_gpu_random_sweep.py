@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 ENTRIES = ("decode", "decode_plan", "append", "verify", "verify_plan", "varlen", "prefill")
 CASES = 210
+WIDE = 70
 KDT = {"f32": torch.float32, "bf16": torch.bfloat16, "int8": torch.int8}
 
 
@@ -40,27 +41,31 @@ def _lengths(rng, n, lo, hi):
 
 
 def _draw(i):
-    rng = np.random.default_rng(50_000 + i)
+    """Case i: cases CASES .. CASES + WIDE - 1 draw wider shapes (more KV heads and
+    sequences, up to 16 query tokens, contexts past several pieces)."""
+    wide = i >= CASES
+    rng = np.random.default_rng((60_000 if wide else 50_000) + i)
     entry = ENTRIES[i % len(ENTRIES)]
     D = int(rng.choice([64, 128]))
-    Hkv = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 9 if wide else 4))
     if entry in ("decode", "decode_plan", "append"):
         G = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 16]))
         T = 1
     else:
         G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
-        T = int(rng.integers(1, 9 if entry != "prefill" else 41))
+        T = int(rng.integers(1, (17 if wide else 9) if entry != "prefill" else 41))
     kv = {"append": ["f32", "bf16", "bf16"], "decode": ["f32", "bf16", "int8"],
           "decode_plan": ["f32", "bf16", "int8"]}.get(entry, ["bf16", "int8"])
     kv = str(rng.choice(kv))
-    N = int(rng.integers(1, 10))
+    N = int(rng.integers(1, 21 if wide else 10))
     lo = 1 if entry == "append" else (T if entry == "prefill" else 0)
-    lens = _lengths(rng, N, lo, int(rng.choice([64, 300, 1100])))
-    split = int(rng.choice([0, 16, 48, 128, 512]))
+    hi = int(rng.choice([700, 2100, 4500] if wide else [64, 300, 1100]))
+    lens = _lengths(rng, N, lo, hi)
+    split = int(rng.choice([0, 16, 48, 128, 512] + ([1024, 4096] if wide else [])))
     return rng, entry, kv, D, Hkv, G, T, lens, split
 
 
-@pytest.mark.parametrize("i", range(CASES))
+@pytest.mark.parametrize("i", range(CASES + WIDE))
 def test_random_sweep(i):
     rng, entry, kv, D, Hkv, G, T, lens, split = _draw(i)
     _say("sweep", i, entry, kv, "D", D, "Hkv", Hkv, "G", G, "T", T, "split", split, "lens", lens)
