@@ -280,7 +280,7 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
  * Decode-Step Stall", "Full Source", engine.py).  For a padding row (negative
  * slot) nothing is written and the row's output is unspecified.
  * Other arguments as pa_decode.  Caches: PA_F32 or PA_BF16 (an int8 cache
- * returns PA_ERR_UNSUPPORTED).
+ * returns PA_ERR_UNSUPPORTED: pa_decode_append_quant writes int8 caches).
  */
 int pa_decode_append(void* out, const void* q, const void* key, const void* value,
                      void* k_cache, void* v_cache, const int64_t* slot_mapping,
@@ -289,6 +289,38 @@ int pa_decode_append(void* out, const void* q, const void* key, const void* valu
                      int max_blocks_per_seq, int max_context_len, float scale, int q_dtype,
                      int kv_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * pa_decode_append_quant -- pa_reshape_and_cache_quant of one new token per
+ * sequence followed by pa_decode over the int8 cache, in one launch of the
+ * matrix-core kernel, with the two calls' results bit for bit: the same codes
+ * and scales in the cache, the same output.  The workgroup that reads the
+ * block holding position context_lens[b] - 1 requantizes it as the write does
+ * ("A Rust inference server for Qwen2 on Apple Silicon", "Day 4 measurements
+ * -- int8 KV", "Partial blocks": the 16 rows dequantized with the old scale,
+ * the new row put in, the scale recomputed as max|x| / 127, every value
+ * requantized), attends over the new codes and scale, and stores them.
+ *
+ * key, value     [num_seqs, kv_heads, head_dim], in_dtype (PA_BF16 or PA_F32).
+ * k_cache, v_cache  int8 [kv_heads, num_blocks, block_size, head_dim];
+ * k_scale, v_scale  fp32 [kv_heads, num_blocks], read and written.
+ * slot_mapping   [num_seqs] int64: the slot of position context_lens[b] - 1
+ *                (negative: nothing is written and the row's output is
+ *                unspecified; slots past the pool are ignored).
+ * q, out         bf16 [num_seqs, q_heads, head_dim].
+ * Other arguments as pa_decode; groups of at most 16 query heads per KV head.
+ * The results equal pa_reshape_and_cache_quant followed by pa_decode whenever
+ * each slot is the slot of its sequence's position context_lens[b] - 1 and no
+ * two sequences share a block (what a decode step passes).
+ */
+int pa_decode_append_quant(void* out, const void* q, const void* key, const void* value,
+                           int in_dtype, int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                           float* v_scale, const int64_t* slot_mapping,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int num_seqs, int q_heads, int kv_heads, int head_dim, int block_size,
+                           int num_blocks, int max_blocks_per_seq, int max_context_len,
+                           float scale, int split_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * pa_verify -- T = num_query_tokens new tokens per sequence (a speculative
@@ -359,8 +391,9 @@ int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache
  *   pa_plan_size(...) bytes, 16-byte aligned, written entirely by this call.
  *   The other arguments must be those of the attention calls that use it.
  *
- * pa_decode_planned, pa_decode_append_planned, pa_verify_planned -- pa_decode,
- *   pa_decode_append and pa_verify, started in the plan's order, with results
+ * pa_decode_planned, pa_decode_append_planned, pa_decode_append_quant_planned,
+ * pa_verify_planned -- pa_decode, pa_decode_append, pa_decode_append_quant
+ *   and pa_verify, started in the plan's order, with results
  *   identical bit for bit to the unplanned calls.  plan / plan_bytes: a plan
  *   from pa_plan (plan_bytes >= pa_plan_size(...) for the call's sizes, else
  *   PA_ERR_INVALID_ARG).  The call takes each unit's length and block-table
@@ -396,6 +429,15 @@ int pa_decode_append_planned(void* out, const void* q, const void* key, const vo
                              int max_context_len, float scale, int q_dtype, int kv_dtype,
                              int split_tokens, void* workspace, size_t workspace_bytes,
                              const void* plan, size_t plan_bytes, void* stream);
+int pa_decode_append_quant_planned(void* out, const void* q, const void* key,
+                                   const void* value, int in_dtype, int8_t* k_cache,
+                                   int8_t* v_cache, float* k_scale, float* v_scale,
+                                   const int64_t* slot_mapping, const int32_t* block_tables,
+                                   const int32_t* context_lens, int num_seqs, int q_heads,
+                                   int kv_heads, int head_dim, int block_size, int num_blocks,
+                                   int max_blocks_per_seq, int max_context_len, float scale,
+                                   int split_tokens, void* workspace, size_t workspace_bytes,
+                                   const void* plan, size_t plan_bytes, void* stream);
 
 int pa_verify_planned(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const float* k_scale, const float* v_scale, const int32_t* block_tables,

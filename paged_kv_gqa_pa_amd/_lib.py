@@ -30,7 +30,8 @@ EXPORTED = ["pa_version", "pa_last_error", "pa_device_check_status", "pa_reshape
             "pa_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_decode_append", "pa_verify", "pa_verify_varlen",
             "pa_prefill", "pa_plan_size", "pa_plan", "pa_decode_planned",
             "pa_decode_append_planned", "pa_verify_planned", "pa_prefill_plan_size",
-            "pa_prefill_plan", "pa_prefill_planned"]
+            "pa_prefill_plan", "pa_prefill_planned", "pa_decode_append_quant",
+            "pa_decode_append_quant_planned"]
 
 _DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_INT8}
 
@@ -76,6 +77,13 @@ def _load():
     lib.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i, i, i, i, i, i, i, i,
                                      f, i, i, i, vp, sz, vp]
+    lib.pa_decode_append_quant.restype = i
+    lib.pa_decode_append_quant.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp,
+                                           i, i, i, i, i, i, i, i,
+                                           f, i, vp, sz, vp]
+    lib.pa_decode_append_quant_planned.restype = i
+    lib.pa_decode_append_quant_planned.argtypes = (lib.pa_decode_append_quant.argtypes[:-1] +
+                                                   [vp, sz, vp])
     lib.pa_verify_varlen.restype = i
     lib.pa_verify_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i, i, i, i, i, i, i, i, i, i,
@@ -502,4 +510,51 @@ def decode_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tabl
         _check(_load().pa_decode_append(*args, _stream(stream)))
     else:
         _check(_load().pa_decode_append_planned(*args, *_plan_args(plan), _stream(stream)))
+    return out
+
+
+def decode_append_quant(out, q, key, value, k_cache, v_cache, k_scale, v_scale, slot_mapping,
+                        block_tables, context_lens, scale, max_context_len, split_tokens=0,
+                        workspace=None, stream=None, plan=None):
+    """Requantizing cache write of one new token per sequence into an int8 cache plus the
+    decode over it, in one launch (pa_decode_append_quant): the same cache bytes, scales and
+    output as reshape_and_cache_quant followed by decode.
+
+    key/value [num_seqs, kv_heads, head_dim] bfloat16 or float32; k_cache/v_cache int8 and
+    k_scale/v_scale float32 [kv_heads, num_blocks] are updated in place; q/out bfloat16.
+    """
+    _need(q, "q", dtype=torch.bfloat16, ndim=3)
+    _need(out, "out", dtype=torch.bfloat16, ndim=3)
+    _need(k_cache, "k_cache", dtype=torch.int8, ndim=4)
+    _need(v_cache, "v_cache", dtype=torch.int8, ndim=4)
+    _need(k_scale, "k_scale", dtype=torch.float32, ndim=2)
+    _need(v_scale, "v_scale", dtype=torch.float32, ndim=2)
+    _need(key, "key", ndim=3)
+    _need(value, "value", dtype=key.dtype, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    if key.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("key/value must be bfloat16 or float32")
+    Hkv, NB, BS, D = k_cache.shape
+    N, Hq, Dq = q.shape
+    if (out.shape != q.shape or Dq != D or key.shape != (N, Hkv, D) or value.shape != key.shape
+            or slot_mapping.shape[0] != N or block_tables.shape[0] != N
+            or context_lens.shape[0] != N or v_cache.shape != k_cache.shape):
+        raise ValueError("decode_append_quant: inconsistent shapes")
+    if k_scale.shape != (Hkv, NB) or v_scale.shape != (Hkv, NB):
+        raise ValueError("scales must be [kv_heads, num_blocks]")
+    need = _load().pa_workspace_size(N, 1, Hq, Hkv, D, int(max_context_len), PA_INT8,
+                                     int(split_tokens))
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(out), _ptr(q), _ptr(key), _ptr(value), _DTYPE[key.dtype], _ptr(k_cache),
+            _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables),
+            _ptr(context_lens), N, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_context_len),
+            float(scale), int(split_tokens), _ptr(workspace), ws_bytes]
+    if plan is None:
+        _check(_load().pa_decode_append_quant(*args, _stream(stream)))
+    else:
+        _check(_load().pa_decode_append_quant_planned(*args, *_plan_args(plan), _stream(stream)))
     return out

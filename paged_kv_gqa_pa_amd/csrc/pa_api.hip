@@ -159,6 +159,7 @@ struct Append {
   const void* key = nullptr;
   const void* value = nullptr;
   const int64_t* slot_mapping = nullptr;
+  int in_dtype = -1;   // requantizing write into an int8 cache: PA_F32 / PA_BF16 rows
   bool on = false;
 };
 
@@ -181,8 +182,17 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   int st = plan_pieces(num_seqs, T, q_heads, kv_heads, head_dim, max_context_len, kv_dtype,
                        split_tokens, &plan, vl.on);
   if (st != PA_OK) return st;
-  if (app.on && kv_dtype == PA_INT8)
-    return fail(PA_ERR_UNSUPPORTED, "append into an int8 cache is not built");
+  if (app.on && kv_dtype == PA_INT8 && app.in_dtype < 0)
+    return fail(PA_ERR_UNSUPPORTED,
+                "append into an int8 cache takes bf16/fp32 rows (pa_decode_append_quant)");
+  if (app.on && app.in_dtype >= 0) {
+    if (kv_dtype != PA_INT8)
+      return fail(PA_ERR_INVALID_ARG, "the requantizing append needs an int8 cache");
+    if (app.in_dtype != PA_F32 && app.in_dtype != PA_BF16)
+      return fail(PA_ERR_INVALID_ARG, "key/value dtype %d: PA_F32 or PA_BF16", app.in_dtype);
+    if (q_heads % kv_heads == 0 && q_heads / kv_heads > 16)
+      return fail(PA_ERR_UNSUPPORTED, "the requantizing append takes groups of at most 16 heads");
+  }
   if (vl.on && (vl.total < 0 || long(vl.total) > long(num_seqs) * T))
     return fail(PA_ERR_INVALID_ARG,
                 "total_query_tokens %d must be in [0, num_seqs * max_query_tokens = %ld]",
@@ -264,6 +274,7 @@ int run_attention(bool is_verify, void* out, const void* q, const void* k_cache,
   a.new_k = app.key;
   a.new_v = app.value;
   a.slot_mapping = app.slot_mapping;
+  a.new_dtype = app.in_dtype == PA_F32 ? pa::kF32 : pa::kBF16;
   a.query_start = vl.on ? vl.query_start : nullptr;
   a.plan = static_cast<const int32_t*>(work_plan);
   a.check_status = status_ptr();
@@ -525,6 +536,26 @@ int pa_decode_append(void* out, const void* q, const void* key, const void* valu
                        split_tokens, workspace, workspace_bytes, stream, app);
 }
 
+int pa_decode_append_quant(void* out, const void* q, const void* key, const void* value,
+                           int in_dtype, int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                           float* v_scale, const int64_t* slot_mapping,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int num_seqs, int q_heads, int kv_heads, int head_dim, int block_size,
+                           int num_blocks, int max_blocks_per_seq, int max_context_len,
+                           float scale, int split_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Append app;
+  app.key = key;
+  app.value = value;
+  app.slot_mapping = slot_mapping;
+  app.in_dtype = in_dtype;
+  app.on = true;
+  return run_attention(false, out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, PA_BF16, PA_INT8,
+                       split_tokens, workspace, workspace_bytes, stream, app);
+}
+
 int pa_verify(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
               const int32_t* context_lens, int num_seqs, int num_query_tokens, int q_heads,
@@ -627,6 +658,29 @@ int pa_decode_append_planned(void* out, const void* q, const void* key, const vo
   return run_attention(false, out, q, k_cache, v_cache, nullptr, nullptr, block_tables,
                        context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
                        num_blocks, max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype,
+                       split_tokens, workspace, workspace_bytes, stream, app, Varlen(), plan,
+                       plan_bytes);
+}
+
+int pa_decode_append_quant_planned(void* out, const void* q, const void* key,
+                                   const void* value, int in_dtype, int8_t* k_cache,
+                                   int8_t* v_cache, float* k_scale, float* v_scale,
+                                   const int64_t* slot_mapping, const int32_t* block_tables,
+                                   const int32_t* context_lens, int num_seqs, int q_heads,
+                                   int kv_heads, int head_dim, int block_size, int num_blocks,
+                                   int max_blocks_per_seq, int max_context_len, float scale,
+                                   int split_tokens, void* workspace, size_t workspace_bytes,
+                                   const void* plan, size_t plan_bytes, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID_ARG, "null work plan");
+  Append app;
+  app.key = key;
+  app.value = value;
+  app.slot_mapping = slot_mapping;
+  app.in_dtype = in_dtype;
+  app.on = true;
+  return run_attention(false, out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, num_seqs, 1, q_heads, kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, PA_BF16, PA_INT8,
                        split_tokens, workspace, workspace_bytes, stream, app, Varlen(), plan,
                        plan_bytes);
 }

@@ -68,10 +68,13 @@ struct DecodeArgs {
   float* part_o;    // [rows, max_pieces, head_dim]  (rows = num_seqs * T * q_heads)
   float* part_lse;  // [rows, max_pieces], log2 domain
   // Append mode only: the new token's K/V per sequence [num_seqs, kv_heads,
-  // head_dim] and its cache slot [num_seqs].
+  // head_dim] and its cache slot [num_seqs].  With an int8 cache the rows are
+  // new_dtype values (kF32 or kBF16), the slot's block is requantized and
+  // k_scale / v_scale are written.
   const void* new_k;
   const void* new_v;
   const int64_t* slot_mapping;
+  int new_dtype;
   // Variable-length verify only: sequence b's query tokens are packed rows
   // query_start[b] .. query_start[b+1]-1 of q and out ([total, q_heads,
   // head_dim]); nullptr for a fixed T per sequence.

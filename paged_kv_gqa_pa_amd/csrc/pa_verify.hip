@@ -85,19 +85,38 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   }
   const int R = T * G;   // at most 16 * RT (the launch picks RT)
   const int L = it.L;
-  // Decode with append (AP, bf16 caches): lane k < CPR of every wave holds
-  // 16-byte chunk k of the new token's K and V rows (position L - 1) and its slot.
-  constexpr bool append = AP && !kInt8;
+  // Decode with append (AP).  bf16 cache: lane k < CPR of every wave holds
+  // 16-byte chunk k of the new token's K and V rows (position L - 1).  int8
+  // cache: the new rows are bf16 or fp32 values (new_dtype); the lane that
+  // owns chunk k of row (L - 1) % 16 in the requantization below (chunk
+  // index 16-row-major, lane = index % 64) holds dims 16k .. 16k + 15 of
+  // both, as raw words.  Every wave also reads the token's slot.
+  constexpr bool append = AP;
   u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+  u32x4 nq[2][4] = {};   // int8 append: [K, V][16-byte words] (bf16: 2 words, fp32: 4)
   int64_t new_slot = -1;
-  if constexpr (append) {
+  if constexpr (append && !kInt8) {
     if (lane < CPR) {
       const size_t off = (size_t(b) * a.kv_heads + g) * ROWB + 16 * size_t(lane);
       nk = load16(reinterpret_cast<const char*>(a.new_k) + off);
       nv = load16(reinterpret_cast<const char*>(a.new_v) + off);
     }
-    new_slot = a.slot_mapping[b];
   }
+  if constexpr (append && kInt8) {
+    const int ch = lane - (L > 0 ? ((L - 1) % kBlockSize) * CPR % kWave : 0);
+    if (L > 0 && ch >= 0 && ch < CPR) {
+      const int words = a.new_dtype == kF32 ? 4 : 2;
+      const size_t off = ((size_t(b) * a.kv_heads + g) * D + 16 * size_t(ch)) * words;   // bytes per value = words
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (w < words) {
+          nq[0][w] = load16(reinterpret_cast<const char*>(a.new_k) + off + 16 * w);
+          nq[1][w] = load16(reinterpret_cast<const char*>(a.new_v) + off + 16 * w);
+        }
+      }
+    }
+  }
+  if constexpr (append) new_slot = a.slot_mapping[b];
 
   const int wave = readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;     // key row of an operand read / query row of S, P
@@ -239,6 +258,57 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   // Loads a fetch issues (tile chunks, then the two int8 scales).
   constexpr int kFetchLoads = 2 * NL + (kInt8 ? 2 : 0);
 
+  // int8 append: the staged block holding position L - 1 is requantized in
+  // place, as pa_reshape_and_cache_quant does it ("A Rust inference server
+  // for Qwen2 on Apple Silicon", "Day 4 measurements -- int8 KV", "Partial
+  // blocks"): its 16 rows dequantized (code * old scale), row (L - 1) % 16
+  // replaced by the new values, the new scale max|x| / 127 (1 for an all-zero
+  // block), every value turned back into rint(x / scale) clipped to +-127 --
+  // the same fp32 operations, so the same codes and scale.  Lane l owns the
+  // 16-byte chunks l, l + 64, .. of the block (16-row-major); it keeps its
+  // new codes for the store after the tile loop.  Returns the new scale.
+  constexpr int NCH = kBlockSize * CPR / kWave;   // chunks per lane
+  u32x4 rq[2][NCH > 0 ? NCH : 1] = {};
+  auto requant = [&](char* t, const u32x4 (&nrow)[4], float s_old, u32x4 (&codes)[NCH > 0 ? NCH : 1]) {
+    const int rn = (L - 1) % kBlockSize;
+    const bool f32_in = a.new_dtype == kF32;
+    float x[NCH][16];
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int idx = lane + kWave * k, row = idx / CPR, ch = idx % CPR;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(t + sw(row, ch));
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        x[k][e] = float(int8_t((w[e / 4] >> (8 * (e % 4))) & 0xFFu)) * s_old;
+      if (row == rn) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float nb = (e & 1) ? bf16_hi(nrow[e / 8][(e / 2) % 4]) : bf16_lo(nrow[e / 8][(e / 2) % 4]);
+          x[k][e] = f32_in ? __uint_as_float(nrow[e / 4][e % 4]) : nb;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(x[k][e]));
+    }
+    m = stride_max<1>(m);
+    const float s_new = m > 0.0f ? m / 127.0f : 1.0f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int idx = lane + kWave * k, row = idx / CPR, ch = idx % CPR;
+      uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float c = fminf(fmaxf(__builtin_rintf(x[k][e] / s_new), -127.0f), 127.0f);
+        wd[e / 4] |= uint32_t(uint8_t(int8_t(c))) << (8 * (e % 4));
+      }
+      codes[k] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      *reinterpret_cast<u32x4*>(t + sw(row, ch)) = codes[k];
+    }
+    return s_new;
+  };
+  float rq_scale[2] = {1.0f, 1.0f};
+
   // Delayed rescaling: m is a reference maximum; weights are exp2(s - m), and
   // O and the sum are rescaled only when a row's tile maximum exceeds its
   // reference by more than kSlack (log2 units), so weights stay below 2^kSlack
@@ -271,6 +341,12 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         const int r = (L - 1) % kBlockSize;
         *reinterpret_cast<u32x4*>(sk + r * ROWB + 16 * (lane ^ ((r / RPB) & (CPR - 1)))) = nk;
         *reinterpret_cast<u32x4*>(sv + r * ROWB + 16 * (lane ^ vswz<ROWB>(r))) = nv;
+      }
+    }
+    if constexpr (kInt8 && append) {
+      if (blk == blk_new) {
+        ks = rq_scale[0] = requant(sk, nq[0], ks, rq[0]);
+        vs = rq_scale[1] = requant(sv, nq[1], vs, rq[1]);
       }
     }
     // Scores of keys 4*grp .. 4*grp+3 for row n of each row tile: product c
@@ -395,7 +471,31 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
   __asm__ __volatile__("" ::: "memory");
 
-  if constexpr (append) {
+  if constexpr (append && kInt8) {
+    // The wave that requantized the block stores its codes and the two
+    // scales at the slot's block (slots < 0 skipped, slots past the pool
+    // ignored).
+    if (piece == n_pieces - 1 && blk_new >= 0 && wave == (blk_new - blk_begin) % NW) {
+      if (threadIdx.x % kWave == 0)
+        check(new_slot < int64_t(a.num_blocks) * kBlockSize, kCheckSlot, a.check_status);
+      if (new_slot >= 0 && new_slot < int64_t(a.num_blocks) * kBlockSize) {
+        const size_t blk_off = (size_t(g) * a.num_blocks + size_t(new_slot / kBlockSize)) * TILE_BYTES;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+          const int idx = lane + kWave * k, row = idx / CPR, ch = idx % CPR;
+          const size_t off = blk_off + size_t(row) * ROWB + 16 * size_t(ch);
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + off) = rq[0][k];
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + off) = rq[1][k];
+        }
+        if (lane == 0) {
+          const size_t sidx = size_t(g) * a.num_blocks + size_t(new_slot / kBlockSize);
+          const_cast<float*>(a.k_scale)[sidx] = rq_scale[0];
+          const_cast<float*>(a.v_scale)[sidx] = rq_scale[1];
+        }
+      }
+    }
+  }
+  if constexpr (append && !kInt8) {
     // (after the loop: issued before it, the store held wave 0's first tile
     // loads back until the new row had arrived)
     if (piece == n_pieces - 1) {
@@ -529,9 +629,9 @@ hipError_t launch_rows_rt(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = PA_ROWS_WAVES;
   const long wgs = long(a.max_pieces) * a.num_seqs * a.kv_heads;
   if (a.new_k) {
-    // Decode with append: one query token per sequence, bf16 cache, groups of
-    // at most 16 heads (one row tile); the host refuses other shapes.
-    if constexpr (RT == 1 && !__is_same(KV, i8_t)) {
+    // Decode with append: one query token per sequence, groups of at most 16
+    // heads (one row tile); the host refuses other shapes.
+    if constexpr (RT == 1) {
       if (a.head_dim == 128)
         rows_pass1<KV, 128, NW, RowsSlots<KV>::value, 1, true><<<dim3(unsigned(wgs)), NW * kWave, 0, stream>>>(a);
       else
