@@ -240,11 +240,66 @@ def other_workloads(torch, pa, wl, dev, reps=10, use_plan=True):
         if name != "tiny_fp32":
             out[name]["read_pattern"] = read_pattern_timing(torch, kc, vc, bt, cl, spec.max_len,
                                                             split, R, cycles, reps, us)
+        if name == "long_ctx_int8":
+            out[name]["append_step"] = int8_append_timing(torch, pa, dev, kc, vc, ks, vs, q, o, bt,
+                                                          cl, lens, table, spec, split, ws, R,
+                                                          cycles, reps)
         del kc, vc, g
         torch.cuda.empty_cache()
     out["int8_requant_write"] = requant_write_timing(torch, pa, dev, reps)
     out["chunked_prefill_bf16"] = prefill_timing(torch, pa, dev, reps)
     return out
+
+
+def int8_append_timing(torch, pa, dev, kc, vc, ks, vs, q, o, bt, cl, lens, table, spec, split,
+                       ws, R, cycles, reps):
+    """A decode step over the long-context int8 caches with its cache write: one new
+    bf16 token per sequence written with requantization of its block and attended
+    over, as one pa_decode_append_quant launch and as pa_reshape_and_cache_quant +
+    pa_decode, over the same replicas (events on the launch stream)."""
+    N, Hkv, D = spec.num_seqs, spec.kv_heads, spec.head_dim
+    g_ = torch.Generator(device=dev)
+    g_.manual_seed(spec.seed + 200)
+    nk = torch.randn((N, Hkv, D), device=dev, dtype=torch.bfloat16, generator=g_)
+    nv = torch.randn((N, Hkv, D), device=dev, dtype=torch.bfloat16, generator=g_)
+    from paged_kv_gqa_pa_amd import workloads as wl
+    sm = torch.from_numpy(wl.slots_for_positions(table, np.arange(N),
+                                                 lens.astype(np.int64) - 1)).to(dev)
+    scale = 1.0 / float(np.sqrt(D))
+    order = [r for _ in range(cycles) for r in range(R)]
+
+    def fused():
+        for r in order:
+            pa.decode_append_quant(o, q, nk, nv, kc[r], vc[r], ks, vs, sm, bt, cl, scale,
+                                   spec.max_len, split_tokens=split, workspace=ws)
+
+    def two_calls():
+        for r in order:
+            pa.reshape_and_cache_quant(nk, nv, kc[r], vc[r], ks, vs, sm)
+            pa.decode(o, q, kc[r], vc[r], bt, cl, scale, spec.max_len, ks, vs,
+                      split_tokens=split, workspace=ws)
+    res = {"entry_points": "pa_decode_append_quant vs pa_reshape_and_cache_quant + pa_decode",
+           "new_rows": "bf16"}
+    for key, fn in (("fused_us_per_call", fused), ("write_then_decode_us_per_call", two_calls)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[key] = round(e0.elapsed_time(e1) * 1e3 / (reps * len(order)), 2)
+        del g
+    print(f"[bench]   with the requantizing write of the new tokens: "
+          f"{res['fused_us_per_call']:.2f} us in one launch, "
+          f"{res['write_then_decode_us_per_call']:.2f} us as write + decode", flush=True)
+    return res
 
 
 def read_pattern_timing(torch, kc, vc, bt, cl, max_len, split, R, cycles, reps, us_call):
