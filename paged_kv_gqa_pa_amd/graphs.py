@@ -33,10 +33,13 @@ from . import _lib as pa
 class StepGraphs:
     """Captured attention steps for batch sizes up to max(buckets).
 
-    k_caches / v_caches: one [kv_heads, num_blocks, 16, head_dim] tensor per layer (bf16
-    or fp32).  spare_block: a block index no sequence uses, in every layer's cache.
-    num_query_tokens: 1 for decode, T = k + 1 (<= 16) for speculative verify.  fused: use
-    pa_decode_append (decode only).  use_plan: one work plan per step (pa_plan) in every
+    k_caches / v_caches: one [kv_heads, num_blocks, 16, head_dim] tensor per layer (bf16,
+    fp32 or int8; an int8 cache takes k_scales / v_scales, one float32 [kv_heads,
+    num_blocks] tensor per layer, bf16 queries and bf16 new rows, written with
+    requantization of their blocks).  spare_block: a block index no sequence uses, in
+    every layer's cache.  num_query_tokens: 1 for decode, T = k + 1 (<= 16) for
+    speculative verify.  fused: use pa_decode_append (pa_decode_append_quant for int8;
+    decode only).  use_plan: one work plan per step (pa_plan) in every
     bucket (True), in none (False), or (None, the default) in the buckets whose
     (sequence, KV head, piece) units outnumber the GPU's compute units.  With no more
     units than compute units every unit starts on a CU of its own, so the order changes
@@ -49,7 +52,9 @@ class StepGraphs:
                  q_heads: int, max_blocks_per_seq: int, spare_block: int, scale: float,
                  buckets=(1, 2, 4, 8, 16, 32, 64), num_query_tokens: int = 1,
                  fused: bool = False, split_tokens: int = 0,
-                 use_plan: Optional[bool] = None):
+                 use_plan: Optional[bool] = None,
+                 k_scales: Optional[Sequence[torch.Tensor]] = None,
+                 v_scales: Optional[Sequence[torch.Tensor]] = None):
         if len(k_caches) == 0 or len(k_caches) != len(v_caches):
             raise ValueError("one K and one V cache per layer")
         kv_heads, num_blocks, bs, head_dim = k_caches[0].shape
@@ -65,6 +70,17 @@ class StepGraphs:
             raise ValueError("num_query_tokens must be in [1, 16]")
         if fused and T != 1:
             raise ValueError("the fused write + decode call takes one token per sequence")
+        self.int8 = k_caches[0].dtype == torch.int8
+        if self.int8:
+            if (k_scales is None or v_scales is None or len(k_scales) != len(k_caches) or
+                    len(v_scales) != len(k_caches)):
+                raise ValueError("an int8 cache needs k_scales / v_scales, one per layer")
+            for ks, vs in zip(k_scales, v_scales):
+                if (ks.dtype != torch.float32 or vs.dtype != torch.float32 or
+                        tuple(ks.shape) != (kv_heads, num_blocks) or ks.shape != vs.shape):
+                    raise ValueError("scales must be float32 [kv_heads, num_blocks]")
+        self.k_scales = list(k_scales) if self.int8 else [None] * len(k_caches)
+        self.v_scales = list(v_scales) if self.int8 else [None] * len(k_caches)
         self.k_caches, self.v_caches = list(k_caches), list(v_caches)
         self.layers = len(k_caches)
         self.q_heads, self.kv_heads, self.head_dim = q_heads, kv_heads, head_dim
@@ -73,6 +89,8 @@ class StepGraphs:
         self.spare, self.scale, self.T = int(spare_block), float(scale), T
         self.fused, self.split, self.use_plan = fused, int(split_tokens), use_plan
         self.dtype = k_caches[0].dtype
+        # queries and new rows: the cache's dtype, bf16 for an int8 cache
+        self.row_dtype = torch.bfloat16 if self.int8 else self.dtype
         self.device = k_caches[0].device
         self.buckets = sorted(set(int(b) for b in buckets))
         self._graphs = {}
@@ -99,10 +117,10 @@ class StepGraphs:
     def _alloc(self, B: int):
         T, dev = self.T, self.device
         qshape = (B, self.q_heads, self.head_dim) if T == 1 else (B, T, self.q_heads, self.head_dim)
-        z = lambda *s: torch.zeros(s, dtype=self.dtype, device=dev)
+        z = lambda *s: torch.zeros(s, dtype=self.row_dtype, device=dev)
         b = {
-            "q": [torch.zeros(qshape, dtype=self.dtype, device=dev) for _ in range(self.layers)],
-            "out": [torch.zeros(qshape, dtype=self.dtype, device=dev) for _ in range(self.layers)],
+            "q": [torch.zeros(qshape, dtype=self.row_dtype, device=dev) for _ in range(self.layers)],
+            "out": [torch.zeros(qshape, dtype=self.row_dtype, device=dev) for _ in range(self.layers)],
             "k_new": [z(B * T, self.kv_heads, self.head_dim) for _ in range(self.layers)],
             "v_new": [z(B * T, self.kv_heads, self.head_dim) for _ in range(self.layers)],
             "tables": torch.full((B, self.max_blocks), -1, dtype=torch.int32, device=dev),
@@ -139,18 +157,31 @@ class StepGraphs:
                          plan=b["plan"])
         for l in range(self.layers):
             kc, vc = self.k_caches[l], self.v_caches[l]
+            ks, vs = self.k_scales[l], self.v_scales[l]
+            if self.fused and self.int8:
+                pa.decode_append_quant(b["out"][l], b["q"][l], b["k_new"][l], b["v_new"][l], kc,
+                                       vc, ks, vs, b["slots"], b["tables"], b["lens"], self.scale,
+                                       self.max_len, split_tokens=self.split, workspace=b["ws"],
+                                       plan=b["plan"])
+                continue
             if self.fused:
                 pa.decode_append(b["out"][l], b["q"][l], b["k_new"][l], b["v_new"][l], kc, vc,
                                  b["slots"], b["tables"], b["lens"], self.scale, self.max_len,
                                  split_tokens=self.split, workspace=b["ws"], plan=b["plan"])
                 continue
-            pa.reshape_and_cache(b["k_new"][l], b["v_new"][l], kc, vc, b["slots"])
+            if self.int8:
+                pa.reshape_and_cache_quant(b["k_new"][l], b["v_new"][l], kc, vc, ks, vs,
+                                           b["slots"])
+            else:
+                pa.reshape_and_cache(b["k_new"][l], b["v_new"][l], kc, vc, b["slots"])
             if T == 1:
                 pa.decode(b["out"][l], b["q"][l], kc, vc, b["tables"], b["lens"], self.scale,
-                          self.max_len, split_tokens=self.split, workspace=b["ws"], plan=b["plan"])
+                          self.max_len, ks, vs, split_tokens=self.split, workspace=b["ws"],
+                          plan=b["plan"])
             else:
                 pa.verify(b["out"][l], b["q"][l], kc, vc, b["tables"], b["lens"], self.scale,
-                          self.max_len, split_tokens=self.split, workspace=b["ws"], plan=b["plan"])
+                          self.max_len, ks, vs, split_tokens=self.split, workspace=b["ws"],
+                          plan=b["plan"])
 
     def _capture(self, B: int):
         b = self._alloc(B)
@@ -189,11 +220,11 @@ class StepGraphs:
         qshape = (n, self.q_heads, self.head_dim) if T == 1 else (n, T, self.q_heads, self.head_dim)
         kvshape = (n * T, self.kv_heads, self.head_dim)
         for l in range(self.layers):
-            if tuple(q[l].shape) != qshape or q[l].dtype != self.dtype:
-                raise ValueError(f"layer {l}: q must be {self.dtype} {qshape}")
+            if tuple(q[l].shape) != qshape or q[l].dtype != self.row_dtype:
+                raise ValueError(f"layer {l}: q must be {self.row_dtype} {qshape}")
             if (tuple(k_new[l].shape) != kvshape or tuple(v_new[l].shape) != kvshape or
-                    k_new[l].dtype != self.dtype or v_new[l].dtype != self.dtype):
-                raise ValueError(f"layer {l}: k_new / v_new must be {self.dtype} {kvshape}")
+                    k_new[l].dtype != self.row_dtype or v_new[l].dtype != self.row_dtype):
+                raise ValueError(f"layer {l}: k_new / v_new must be {self.row_dtype} {kvshape}")
         if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or
                 slot_mapping.dtype != torch.int64):
             raise ValueError("block_tables / context_lens int32, slot_mapping int64")

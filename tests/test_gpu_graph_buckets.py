@@ -110,6 +110,58 @@ def test_bucketed_steps_match_eager(T, fused, hq, hkv):
                 assert max_abs_err(want[0], ref) < TOL["bf16"]
 
 
+@pytest.mark.parametrize("T,fused", [(1, False), (1, True), (5, False)])
+def test_bucketed_steps_int8_match_eager(T, fused):
+    """int8 caches: the requantizing write (fused with the decode, or before it), bf16
+    queries and new rows; real rows and the caches and scales outside the spare block
+    bit-identical to eager calls on the unpadded batch."""
+    _say("bucketed step graphs, int8 cache, T", T, "fused", fused)
+    hq, hkv = 12, 2
+    spare = NB - 1
+    scale = 1.0 / float(np.sqrt(D))
+    rng0 = np.random.default_rng(70 + T + int(fused))
+    kc, vc, ks, vs = [], [], [], []
+    for _ in range(LAYERS):
+        kcode, kscale = wl.quantize_int8_blocks(rng0.standard_normal((hkv, NB, 16, D), dtype=np.float32))
+        vcode, vscale = wl.quantize_int8_blocks(rng0.standard_normal((hkv, NB, 16, D), dtype=np.float32))
+        kc.append(dev(kcode))
+        ks.append(dev(kscale))
+        vc.append(dev(vcode))
+        vs.append(dev(vscale))
+    kc_e, vc_e = [k.clone() for k in kc], [v.clone() for v in vc]
+    ks_e, vs_e = [k.clone() for k in ks], [v.clone() for v in vs]
+    graphs = StepGraphs(kc, vc, hq, MAXB, spare, scale, buckets=(1, 4, 16, 64),
+                        num_query_tokens=T, fused=fused, k_scales=ks, v_scales=vs)
+    rng = np.random.default_rng(80 + T + int(fused))
+    for n in (1, 3, 16, 37):
+        lens, table, slots = _batch(rng, n, T, spare)
+        _say("  batch", n, "bucket", graphs.bucket_for(n))
+        qshape = (n, hq, D) if T == 1 else (n, T, hq, D)
+        q = [torch.randn(qshape, device="cuda").bfloat16() for _ in range(LAYERS)]
+        kn = [torch.randn((n * T, hkv, D), device="cuda").bfloat16() for _ in range(LAYERS)]
+        vn = [torch.randn((n * T, hkv, D), device="cuda").bfloat16() for _ in range(LAYERS)]
+        bt, cl, sm = dev(table), dev(lens), dev(slots)
+        want = []
+        for l in range(LAYERS):
+            o = torch.empty_like(q[l])
+            if fused:
+                pa.decode_append_quant(o, q[l], kn[l], vn[l], kc_e[l], vc_e[l], ks_e[l], vs_e[l],
+                                       sm, bt, cl, scale, MAXB * 16)
+            else:
+                pa.reshape_and_cache_quant(kn[l], vn[l], kc_e[l], vc_e[l], ks_e[l], vs_e[l], sm)
+                fn = pa.decode if T == 1 else pa.verify
+                fn(o, q[l], kc_e[l], vc_e[l], bt, cl, scale, MAXB * 16, ks_e[l], vs_e[l])
+            want.append(o)
+        got = graphs.step(q, kn, vn, bt, cl, sm)
+        torch.cuda.synchronize()
+        for l in range(LAYERS):
+            assert host_bits(got[l]).tobytes() == host_bits(want[l]).tobytes(), (n, l)
+            for a, e in ((kc[l], kc_e[l]), (vc[l], vc_e[l])):
+                assert torch.equal(a[:, :spare], e[:, :spare])
+            for a, e in ((ks[l], ks_e[l]), (vs[l], vs_e[l])):
+                assert torch.equal(a[:, :spare], e[:, :spare])
+
+
 def test_bucket_limits():
     _say("bucket limits")
     kc, vc = _caches(9)
