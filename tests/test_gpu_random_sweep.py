@@ -1,8 +1,8 @@
 """A seeded sweep over random shapes and entry points, each against the oracle.
 
 Every case draws an entry point (decode, decode with a work plan, the fused
-cache write + decode, verify, verify with a work plan, variable-length
-verify, chunked prefill), a cache type, head_dim, group size, KV-head count,
+cache write + decode, the fused requantizing int8 write + decode, verify,
+verify with a work plan, variable-length verify, chunked prefill), a cache type, head_dim, group size, KV-head count,
 a batch whose lengths mix block edges with random ones, a piece length, and
 a pool with poisoned spare blocks and partial-block tails; the GPU result is
 compared with the oracle on the same inputs at the cache type's tolerance
@@ -22,7 +22,8 @@ from tests.test_gpu_verify import _random_verify_case
 
 pytestmark = pytest.mark.gpu
 
-ENTRIES = ("decode", "decode_plan", "append", "verify", "verify_plan", "varlen", "prefill")
+ENTRIES = ("decode", "decode_plan", "append", "append_quant", "verify", "verify_plan", "varlen",
+           "prefill")
 CASES = 210
 WIDE = 70
 KDT = {"f32": torch.float32, "bf16": torch.bfloat16, "int8": torch.int8}
@@ -48,17 +49,18 @@ def _draw(i):
     entry = ENTRIES[i % len(ENTRIES)]
     D = int(rng.choice([64, 128]))
     Hkv = int(rng.integers(1, 9 if wide else 4))
-    if entry in ("decode", "decode_plan", "append"):
+    if entry in ("decode", "decode_plan", "append", "append_quant"):
         G = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 16]))
         T = 1
     else:
         G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
         T = int(rng.integers(1, (17 if wide else 9) if entry != "prefill" else 41))
-    kv = {"append": ["f32", "bf16", "bf16"], "decode": ["f32", "bf16", "int8"],
+    kv = {"append": ["f32", "bf16", "bf16"], "append_quant": ["int8"],
+          "decode": ["f32", "bf16", "int8"],
           "decode_plan": ["f32", "bf16", "int8"]}.get(entry, ["bf16", "int8"])
     kv = str(rng.choice(kv))
     N = int(rng.integers(1, 21 if wide else 10))
-    lo = 1 if entry == "append" else (T if entry == "prefill" else 0)
+    lo = 1 if entry.startswith("append") else (T if entry == "prefill" else 0)
     hi = int(rng.choice([700, 2100, 4500] if wide else [64, 300, 1100]))
     lens = _lengths(rng, N, lo, hi)
     split = int(rng.choice([0, 16, 48, 128, 512] + ([1024, 4096] if wide else [])))
@@ -71,6 +73,32 @@ def test_random_sweep(i):
     _say("sweep", i, entry, kv, "D", D, "Hkv", Hkv, "G", G, "T", T, "split", split, "lens", lens)
     Hq = Hkv * G
     tol = TOL[kv]
+    if entry == "append_quant":
+        # the requantizing int8 write + decode in one launch: the cache, scales and output
+        # against the oracle's requantizing write and decode
+        in_tag = str(rng.choice(["bf16", "f32"]))
+        case = _random_case(rng, lens, Hkv=Hkv, G=G, D=D, tag="int8", poison=True)
+        dc = DevCase(case)
+        slots = wl.slots_for_positions(case.block_tables, np.arange(len(lens)),
+                                       np.asarray(lens, np.int64) - 1)
+        nk = wl.encode(rng.standard_normal((len(lens), Hkv, D), dtype=np.float32), in_tag)
+        nv = wl.encode(rng.standard_normal((len(lens), Hkv, D), dtype=np.float32), in_tag)
+        out = torch.empty_like(dc.q)
+        pa.decode_append_quant(out, dc.q, dev(nk), dev(nv), dc.k_cache, dc.v_cache, dc.k_scale,
+                               dc.v_scale, dev(slots), dc.block_tables, dc.context_lens,
+                               case.scale, case.max_context_len, split_tokens=split)
+        torch.cuda.synchronize()
+        wk, wv, wks, wvs = oracle.reshape_and_cache_int8(nk, nv, in_tag, case.k_cache,
+                                                         case.v_cache, case.k_scale,
+                                                         case.v_scale, slots)
+        assert host_bits(dc.k_cache).tobytes() == wk.tobytes()
+        assert host_bits(dc.v_cache).tobytes() == wv.tobytes()
+        assert host_bits(dc.k_scale).tobytes() == wks.tobytes()
+        assert host_bits(dc.v_scale).tobytes() == wvs.tobytes()
+        want = oracle.decode(case.q, wk, wv, case.block_tables, case.context_lens, case.scale,
+                             "bf16", "int8", wks, wvs)
+        assert max_abs_err(out, want, tol) < tol
+        return
     if entry in ("decode", "decode_plan", "append"):
         case = _random_case(rng, lens, Hkv=Hkv, G=G, D=D, tag=kv, poison=True)
         dc = DevCase(case)
