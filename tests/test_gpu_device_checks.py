@@ -167,3 +167,25 @@ def test_query_offsets_are_reported():
         pa.prefill(out, qp, dv.k_cache, dv.v_cache, dv.block_tables, dv.context_lens, qs,
                    vcase.scale, 4)
         assert _status() & pa.PA_CHECK_QUERY_START
+
+
+def test_append_quant_slot_out_of_range_is_reported():
+    _say("debug library: requantizing append, slot out of range")
+    rng = np.random.default_rng(66)
+    case = _random_case(rng, [20, 40], Hkv=2, G=6, D=128, tag="int8")
+    dc = DevCase(case)
+    nb = case.spec.num_blocks
+    new = torch.randn((2, 2, 128), device="cuda").bfloat16()
+    good = int(case.block_tables[0, 1]) * 16 + 3          # position 19 of sequence 0
+    slots = dev(np.array([good, nb * 16 + 5], np.int64))
+    with _library(DEBUG_LIB):
+        _status()
+        before = dc.k_scale.clone()
+        out = torch.empty_like(dc.q)
+        pa.decode_append_quant(out, dc.q, new, new, dc.k_cache, dc.v_cache, dc.k_scale, dc.v_scale,
+                               slots, dc.block_tables, dc.context_lens, case.scale,
+                               case.max_context_len)
+        assert _status() & pa.PA_CHECK_SLOT
+        # only sequence 0's block has a new scale
+        changed = (dc.k_scale != before).nonzero().tolist()
+        assert all(blk == good // 16 for _, blk in changed), changed
