@@ -61,6 +61,29 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Maximum that carries NaN through (IEEE 754-2019 maximum).  gfx950 has it as
+// one three-operand instruction that takes its operands as they are, whereas
+// fmaxf first quiets every operand the compiler cannot prove canonical (a
+// matrix-product result, a lane exchange) with a move of its own: the row
+// maximum of eight scores and its two lane exchanges take 9 instructions here,
+// 19 with fmaxf.  For row maxima over scores only: a NaN score gives a NaN
+// weight and a NaN row with either maximum, and the maximum of non-NaN
+// numbers is the same number (the sign of a zero aside, which no exponent
+// below depends on).
+__device__ __forceinline__ float nmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float nmax3(float a, float b, float c) { return nmax(nmax(a, b), c); }
+__device__ __forceinline__ float nmax8(const float (&r)[8]) {
+  return nmax(nmax3(r[0], r[1], r[2]), nmax3(r[3], r[4], nmax3(r[5], r[6], r[7])));
+}
+__device__ __forceinline__ float nmax_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return nmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float nmax_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return nmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Sum over groups of N consecutive lanes (N a power of two, N <= 64); every
 // lane of a group receives the group's sum.  Inside a 16-lane DPP row the
 // butterflies are quad_perm (lane ^ 1, lane ^ 2), then row_half_mirror and

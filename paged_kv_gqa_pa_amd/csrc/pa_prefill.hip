@@ -249,7 +249,11 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
       const bool need = blk * kBlockSize < kend;
       const int entry = need ? bt[readfirstlane(blk)] : 0;
       if (threadIdx.x == 0) check(entry >= 0 && entry < a.num_blocks, kCheckTableEntry, a.check_status);
-      phys[kb] = min(max(entry, 0), a.num_blocks - 1);
+      // bf16: the raw entry, clamped where the fetch uses it, so that no wait
+      // for the scalar load comes before then (clamped here, it was waited
+      // for at once, twice per stage); int8: clamped here, it addresses the
+      // block's scales
+      phys[kb] = kInt8 ? min(max(entry, 0), a.num_blocks - 1) : entry;
       if constexpr (kInt8) {
         // a block past the needed range is fully masked: any finite, nonzero
         // scale keeps its zero weights zero (the row sum divides by the V scale)
@@ -271,7 +275,8 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
       const int blk = st * KB + kb;
       // (uniform; kept scalar so the buffer resource needs no per-lane loop)
       const int valid = readfirstlane(min(max(kend - blk * kBlockSize, 0), kBlockSize));
-      const size_t tile_off = (head_blocks + size_t(valid > 0 ? phys[kb] : 0)) * TILE_BYTES;
+      const int pk = kInt8 ? phys[kb] : min(max(phys[kb], 0), a.num_blocks - 1);
+      const size_t tile_off = (head_blocks + size_t(valid > 0 ? pk : 0)) * TILE_BYTES;
       const __amdgpu_buffer_rsrc_t r = make_rsrc((isv ? vbase : kbase) + tile_off, valid * ROWB);
       const int off = isv ? src_off_v[c] : src_off[c];
       buffer_load16_to_lds(r, buf + (isv ? KB + kb : kb) * TILE_BYTES + 1024 * c, off);
@@ -307,8 +312,13 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
   // Scores of a pair (the products only; issued for every pair of a stage
   // before any softmax, so the matrix cores work on the next pair's scores
   // while the vector ALUs take the softmax of this one).
+  // Both runs of matrix products (scores, then P.V) are issued at raised wave
+  // priority: of the waves that share a SIMD, the one issuing products goes
+  // first, and the others' softmax work fills the cycles between its
+  // products.
   auto scores2 = [&](const char* buf, int kb, f32x4 (&s)[RT][2]) {
     const char* const sk0 = buf + kb * TILE_BYTES;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < RT; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -328,6 +338,7 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
         for (int i = 0; i < RT; ++i) s[i][h] = M::qk(kop, qb[i][c], s[i][h]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   auto softmax_pv2 = [&](const char* buf, int kb, int blk, f32x4 (&s)[RT][2], float ks0,
                          float vs0, float ks1, float vs1) {
@@ -353,9 +364,7 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
             r[e] = pos <= last_vis[i] ? r[e] : kNegInf;
           }
         }
-        float rmax = fmaxf(fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])),
-                           fmaxf(fmaxf(r[4], r[5]), fmaxf(r[6], r[7])));
-        rmax = max_xor32(max_xor16(rmax));
+        const float rmax = nmax_xor32(nmax_xor16(nmax8(r)));
         const float tmax = rmax * sc_pos;   // -inf stays -inf: sc_pos > 0
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
           const float mnew = fmaxf(m[i], tmax);
@@ -398,9 +407,7 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
             x[e] = pos <= last_vis[i] ? x[e] : kNegInf;
           }
         }
-        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        tmax = max_xor32(max_xor16(tmax));
+        const float tmax = nmax_xor32(nmax_xor16(nmax8(x)));
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
           const float mnew = fmaxf(m[i], tmax);
           const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
@@ -426,6 +433,7 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
         lsum[i] = __builtin_fmaf(t1, ivsc[1], __builtin_fmaf(t0, ivsc[0], lsum[i]));
       }
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       u32x2 vb[2];
@@ -444,6 +452,7 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
 #pragma unroll
       for (int i = 0; i < RT; ++i) o[i][t] = pv32(pa[i], v8, o[i][t]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Stage st lives in ring buffer st % NBUF; stages up to st + NBUF - 1 are

@@ -377,15 +377,14 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         pa[i] = u32x2{0u, 0u};
         continue;
       }
-      float tmax = kNegInf;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int pos = blk * kBlockSize + 4 * grp + j;
         const float x = (kInt8 ? s[i][j] - kI8Bias * qsum[i] : s[i][j]) * ssc;
         s[i][j] = pos <= last_vis[i] ? x : kNegInf;
-        tmax = fmaxf(tmax, s[i][j]);
       }
-      tmax = max_xor32(max_xor16(tmax));   // row n over the 16 keys of the tile
+      // row n over the 16 keys of the tile
+      const float tmax = nmax_xor32(nmax_xor16(nmax(nmax3(s[i][0], s[i][1], s[i][2]), s[i][3])));
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
         const float mnew = fmaxf(m[i], tmax);
         const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
