@@ -271,14 +271,23 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
       const int li = wave * LPW + i;
       const bool isv = li >= KB * NL;
       const int kb = (li / NL) % KB;
-      const int c = li % NL;
+      // c: the load's 1 KiB part of its tile (known at compile time when a
+      // wave's share is whole tiles)
+      const int c = LPW % NL == 0 ? i % NL : li % NL;
       const int blk = st * KB + kb;
       // (uniform; kept scalar so the buffer resource needs no per-lane loop)
       const int valid = readfirstlane(min(max(kend - blk * kBlockSize, 0), kBlockSize));
       const int pk = kInt8 ? phys[kb] : min(max(phys[kb], 0), a.num_blocks - 1);
       const size_t tile_off = (head_blocks + size_t(valid > 0 ? pk : 0)) * TILE_BYTES;
       const __amdgpu_buffer_rsrc_t r = make_rsrc((isv ? vbase : kbase) + tile_off, valid * ROWB);
-      const int off = isv ? src_off_v[c] : src_off[c];
+      int off = 0;
+      if constexpr (LPW % NL == 0) {
+        off = isv ? src_off_v[c] : src_off[c];
+      } else {
+        // a run-time part: picked by selects, so the arrays stay in registers
+#pragma unroll
+        for (int k = 0; k < NL; ++k) off = c == k ? (isv ? src_off_v[k] : src_off[k]) : off;
+      }
       buffer_load16_to_lds(r, buf + (isv ? KB + kb : kb) * TILE_BYTES + 1024 * c, off);
     }
   };
@@ -293,11 +302,15 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
   const f32x4 vinit = {M::kVInit, M::kVInit, M::kVInit, M::kVInit};
 
   constexpr float kSlack = 8.0f;
-  float m[RT], lsum[RT];
+  // Per row: the reference maximum m (log2 units); for bf16 caches also the
+  // rescale threshold m + kSlack and the reference the exponents subtract
+  // (m, or 0 while m is -inf), both changed only where m changes.
+  float m[RT], thr[RT], mref[RT], lsum[RT];
   f32x4 o[RT][NT];
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
-    m[i] = kNegInf;
+    m[i] = thr[i] = kNegInf;
+    mref[i] = 0.0f;
     lsum[i] = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) o[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -340,14 +353,14 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  auto softmax_pv2 = [&](const char* buf, int kb, int blk, f32x4 (&s)[RT][2], float ks0,
-                         float vs0, float ks1, float vs1) {
-    const char* const sv0 = buf + (KB + kb) * TILE_BYTES;
+  // The softmax of a pair: the packed weights of each row tile (the A
+  // operands of its P.V products), the running maxima and sums updated.
+  auto softmax2 = [&](int blk, f32x4 (&s)[RT][2], float ks0, float vs0, float ks1, float vs1,
+                      u32x4 (&pa)[RT]) {
     const bool edge = (blk + 2) * kBlockSize - 1 > w_minvis;   // uniform per wave
     const float ssc[2] = {sc * ks0, sc * ks1};
     const float vsc[2] = {vs0, vs1};
     const float ivsc[2] = {kInt8 ? __builtin_amdgcn_rcpf(vs0) : 1.0f, kInt8 ? __builtin_amdgcn_rcpf(vs1) : 1.0f};
-    u32x4 pa[RT];
     if constexpr (!kInt8) {
       // bf16 cache: one factor for both blocks, so the row maximum is taken
       // over the raw scores and each weight is exp2 of one fused multiply-add;
@@ -364,12 +377,18 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
             r[e] = pos <= last_vis[i] ? r[e] : kNegInf;
           }
         }
-        const float rmax = nmax_xor32(nmax_xor16(nmax8(r)));
-        const float tmax = rmax * sc_pos;   // -inf stays -inf: sc_pos > 0
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
+        // The rescale test on this lane's own eight scores: rounding the
+        // product by sc_pos > 0 is monotone, so some lane's maximum times
+        // sc_pos passes the threshold exactly when the row's does, and the
+        // row maximum (two lane exchanges) is taken on the rare path only.
+        const float lmax = nmax8(r) * sc_pos;   // -inf stays -inf: sc_pos > 0
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(lmax > thr[i]) != 0, 0)) {   // rare
+          const float tmax = nmax_xor32(nmax_xor16(lmax));
           const float mnew = fmaxf(m[i], tmax);
           const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
           m[i] = mnew;
+          thr[i] = mnew + kSlack;
+          mref[i] = mnew == kNegInf ? 0.0f : mnew;
           lsum[i] *= alpha;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -378,10 +397,9 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
             for (int t = 0; t < NT; ++t) o[i][t][j] *= ar;
           }
         }
-        const float nref = m[i] == kNegInf ? 0.0f : -m[i];
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(r[e], sc_pos, nref));
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(r[e], sc_pos, -mref[i]));
         pa[i] = u32x4{pack_bf16_round(p[0], p[1]), pack_bf16_round(p[2], p[3]),
                       pack_bf16_round(p[4], p[5]), pack_bf16_round(p[6], p[7])};
         float ls = lsum[i];
@@ -420,10 +438,10 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
             for (int t = 0; t < NT; ++t) o[i][t][j] *= ar;
           }
         }
-        const float mref = m[i] == kNegInf ? 0.0f : m[i];
+        const float mr = m[i] == kNegInf ? 0.0f : m[i];
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] - mref);
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] - mr);
         pa[i] = u32x4{pack_bf16_round(p[0] * vsc[0], p[1] * vsc[0]), pack_bf16_round(p[2] * vsc[0], p[3] * vsc[0]),
                       pack_bf16_round(p[4] * vsc[1], p[5] * vsc[1]), pack_bf16_round(p[6] * vsc[1], p[7] * vsc[1])};
         // the row sum adds the weights as rounded for the product, each block's
@@ -433,6 +451,10 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
         lsum[i] = __builtin_fmaf(t1, ivsc[1], __builtin_fmaf(t0, ivsc[0], lsum[i]));
       }
     }
+  };
+  // The P.V products of a pair (V tiles of blocks kb, kb + 1 of buf).
+  auto pv2 = [&](const char* buf, int kb, const u32x4 (&pa)[RT]) {
+    const char* const sv0 = buf + (KB + kb) * TILE_BYTES;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -453,6 +475,12 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
       for (int i = 0; i < RT; ++i) o[i][t] = pv32(pa[i], v8, o[i][t]);
     }
     __builtin_amdgcn_s_setprio(0);
+  };
+  auto softmax_pv2 = [&](const char* buf, int kb, int blk, f32x4 (&s)[RT][2], float ks0,
+                         float vs0, float ks1, float vs1) {
+    u32x4 pa[RT];
+    softmax2(blk, s, ks0, vs0, ks1, vs1, pa);
+    pv2(buf, kb, pa);
   };
 
   // Stage st lives in ring buffer st % NBUF; stages up to st + NBUF - 1 are
