@@ -383,9 +383,12 @@ __global__ __launch_bounds__(NW * kWave) void rows_pass1(DecodeArgs a) {
         const float x = (kInt8 ? s[i][j] - kI8Bias * qsum[i] : s[i][j]) * ssc;
         s[i][j] = pos <= last_vis[i] ? x : kNegInf;
       }
-      // row n over the 16 keys of the tile
-      const float tmax = nmax_xor32(nmax_xor16(nmax(nmax3(s[i][0], s[i][1], s[i][2]), s[i][3])));
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
+      // The rescale test on this lane's own four scores: some lane passes
+      // m + kSlack exactly when the row (16 keys of the tile) does, so the
+      // row maximum (two lane exchanges) is taken on the rare path only.
+      const float lmax = nmax(nmax3(s[i][0], s[i][1], s[i][2]), s[i][3]);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(lmax > m[i] + kSlack) != 0, 0)) {   // rare
+        const float tmax = nmax_xor32(nmax_xor16(lmax));
         const float mnew = fmaxf(m[i], tmax);
         const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
         m[i] = mnew;
