@@ -48,9 +48,11 @@
 #define PA_PREFILL_STAGES 2
 #endif
 // Register budget: at least two waves per SIMD asked of the compiler (the
-// second launch bound is waves per SIMD), which then fits the bf16 kernel in
-// 164 VGPRs, i.e. three four-wave workgroups per CU; with no bound it spends
-// 88 accumulation registers and gets two.  Asking for three spills.
+// second launch bound is waves per SIMD), which then fits the bf16 and int8
+// kernels (head_dim 128) in 168 VGPRs, i.e. three four-wave workgroups per
+// CU; with no bound it spends 88 accumulation registers and gets two.  Asking
+// for three spills.  At 168 the budget is full: any further per-row state
+// costs the third workgroup.
 #ifndef PA_PREFILL_MIN_WAVES_PER_SIMD
 #define PA_PREFILL_MIN_WAVES_PER_SIMD 2
 #endif
