@@ -427,8 +427,11 @@ __global__ __launch_bounds__(NW * kWave, PA_PREFILL_MIN_WAVES_PER_SIMD) void pre
             x[e] = pos <= last_vis[i] ? x[e] : kNegInf;
           }
         }
-        const float tmax = nmax_xor32(nmax_xor16(nmax8(x)));
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > m[i] + kSlack) != 0, 0)) {   // rare
+        // (the rescale test on this lane's own maximum, exact: the scores
+        // are already scaled)
+        const float lmax = nmax8(x);
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(lmax > m[i] + kSlack) != 0, 0)) {   // rare
+          const float tmax = nmax_xor32(nmax_xor16(lmax));
           const float mnew = fmaxf(m[i], tmax);
           const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[i] - mnew);
           m[i] = mnew;
