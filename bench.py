@@ -803,21 +803,29 @@ def main():
         print("[bench] calibration copy: 256 MiB read + 256 MiB written", flush=True)
         del src, dst
 
-    # Whole step: W untimed steps, then K steps between events (one before each
-    # step and one after the last), synchronised on both sides; the total gives
-    # the mean, the gaps the per-step median, min and max.
+    # Whole step: W untimed steps, then K steps back to back between two events,
+    # synchronised on both sides: the mean.  A second pass of K steps with an
+    # event after every step gives the per-step median, min and max (each of
+    # those events costs the stream a few µs between steps, so these run a
+    # little above the mean).
     def timed_steps(run):
         for _ in range(max(1, args.warmup)):
             run()
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        mean = e0.elapsed_time(e1) / args.steps
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         ev[0].record()
         for i in range(args.steps):
             run()
             ev[i + 1].record()
         torch.cuda.synchronize()
-        return (ev[0].elapsed_time(ev[-1]) / args.steps,
-                sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)))
+        return mean, sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
 
     # The step: per layer, pa_decode_append writes the new token's K and V into
     # the layer's cache and attends over the context that includes it (one launch).
@@ -832,13 +840,21 @@ def main():
     # Decode kernel alone: back-to-back launches over the 28 layers (distinct caches,
     # 2.8 GB per pass, far beyond the 256 MB last-level cache), events on the launch stream.
     torch.cuda.synchronize()
+    # the mean from the passes back to back between two events; the per-pass
+    # spread from a second run with an event after every pass
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(args.decode_reps):
+        run_decode()
+    d1.record()
+    torch.cuda.synchronize()
+    us_decode = d0.elapsed_time(d1) * 1e3 / (args.decode_reps * Lyr)
     dv = [torch.cuda.Event(enable_timing=True) for _ in range(args.decode_reps + 1)]
     dv[0].record()
     for i in range(args.decode_reps):
         run_decode()
         dv[i + 1].record()
     torch.cuda.synchronize()
-    us_decode = dv[0].elapsed_time(dv[-1]) * 1e3 / (args.decode_reps * Lyr)
     per_pass = sorted(dv[i].elapsed_time(dv[i + 1]) * 1e3 / Lyr for i in range(args.decode_reps))
     bytes_launch = algorithmic_bytes(lens, Hq, Hkv, D)
     gbps = bytes_launch / (us_decode * 1e-6) / 1e9
@@ -928,8 +944,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
-                    "max": round(per_step[-1], 4)},
+        "step_ms_with_events": {"median": round(per_step[len(per_step) // 2], 4),
+                                "min": round(per_step[0], 4), "max": round(per_step[-1], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -945,8 +961,8 @@ def main():
                    "split_tokens": args.split or pa.default_split_tokens(Hq, Hkv, D, torch.bfloat16)},
         "write_then_decode_step": {
             "ms_per_step": round(ms_split, 4), "tokens_per_s": round(N / (ms_split / 1e3), 1),
-            "step_ms": {"median": round(per_split[len(per_split) // 2], 4),
-                        "min": round(per_split[0], 4), "max": round(per_split[-1], 4)},
+            "step_ms_with_events": {"median": round(per_split[len(per_split) // 2], 4),
+                                    "min": round(per_split[0], 4), "max": round(per_split[-1], 4)},
             "entry_points": "28 x (pa_reshape_and_cache + pa_decode)" +
                             ("" if plan is None else ", after one pa_plan per step")},
         "hbm_gbps": round(gbps, 1),
